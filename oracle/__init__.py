@@ -1,0 +1,225 @@
+"""ctypes binding of the plain CPU oracle of the float VIF feature.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the GPU library and
+its Python binding never do.  The C source (vif_oracle.c) cites the passage
+each step follows.
+
+The shared library is built next to its source with gcc, on demand if it is
+missing (``build()`` rebuilds it unconditionally).  ``Oracle(path)`` wraps
+any build of the same source, which the mutation tests use to load
+deliberately broken copies.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vif_oracle.c")
+_LIB = os.path.join(_HERE, "libvif_oracle.so")
+
+CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-builtin", "-msse2", "-mfpmath=sse", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+
+NSCALES = 4
+WIDTHS = (17, 9, 5, 3)
+
+_default = None
+
+
+def build(src=_SRC, out=_LIB):
+    """Compile the oracle C source into a shared library (default: in place)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc"] + CFLAGS + ["-I", _HERE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _fp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+class Oracle:
+    """numpy-facing wrapper of one build of the oracle library."""
+
+    def __init__(self, path):
+        lib = ctypes.CDLL(path)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.vifo_taps.argtypes = [ctypes.c_int, f32p]
+        lib.vifo_taps.restype = ctypes.c_int
+        lib.vifo_log2.argtypes = [ctypes.c_float]
+        lib.vifo_log2.restype = ctypes.c_float
+        lib.vifo_log2_array.argtypes = [f32p, f32p, ctypes.c_long]
+        lib.vifo_log2_array.restype = None
+        lib.vifo_ratio_arrays.argtypes = [f32p, f32p, f32p, f32p,
+                                          ctypes.c_long]
+        lib.vifo_ratio_arrays.restype = None
+        lib.vifo_statistic.argtypes = [ctypes.c_float] * 5 + [f32p, f32p]
+        lib.vifo_statistic.restype = None
+        lib.vifo_normalise.argtypes = [ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, f32p]
+        lib.vifo_normalise.restype = ctypes.c_int
+        for name in ("vifo_filter", "vifo_decimate"):
+            fn = getattr(lib, name)
+            fn.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p,
+                           ctypes.c_int, f32p]
+            fn.restype = ctypes.c_int
+        lib.vifo_total_rows.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.vifo_total_rows.restype = ctypes.c_int
+        lib.vifo_score.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   f64p, f32p, f32p]
+        lib.vifo_score.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def taps(self, scale):
+        buf = np.zeros(17, dtype=np.float32)
+        n = self.lib.vifo_taps(int(scale), _fp(buf))
+        if n < 0:
+            raise ValueError("bad scale %r" % (scale,))
+        return buf[:n].copy()
+
+    def log2(self, x):
+        return np.float32(self.lib.vifo_log2(float(np.float32(x))))
+
+    def log2_array(self, xs):
+        """Element-wise oracle log2f_approx over a float32 array."""
+        xs = np.ascontiguousarray(xs, dtype=np.float32)
+        out = np.empty_like(xs)
+        self.lib.vifo_log2_array(_fp(xs), _fp(out), xs.size)
+        return out
+
+    def ratios(self, a, sv):
+        """(fl32(1 + a/(sv + nsq)), fl32(1 + a/nsq)) element-wise."""
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        sv = np.ascontiguousarray(sv, dtype=np.float32)
+        num = np.empty_like(a)
+        den = np.empty_like(a)
+        self.lib.vifo_ratio_arrays(_fp(a), _fp(sv), _fp(num), _fp(den), a.size)
+        return num, den
+
+    def statistic(self, mu1, mu2, xx, yy, xy):
+        n = ctypes.c_float()
+        d = ctypes.c_float()
+        self.lib.vifo_statistic(float(np.float32(mu1)), float(np.float32(mu2)),
+                                float(np.float32(xx)), float(np.float32(yy)),
+                                float(np.float32(xy)), ctypes.byref(n),
+                                ctypes.byref(d))
+        return np.float32(n.value), np.float32(d.value)
+
+    def normalise(self, plane, bpc):
+        plane = np.ascontiguousarray(plane)
+        h, w = plane.shape
+        out = np.empty((h, w), dtype=np.float32)
+        rc = self.lib.vifo_normalise(plane.ctypes.data, w, h, int(bpc),
+                                     _fp(out))
+        if rc != 0:
+            raise ValueError("normalise rejected its arguments")
+        return out
+
+    def filter2d(self, plane, tap):
+        plane = np.ascontiguousarray(plane, dtype=np.float32)
+        tap = np.ascontiguousarray(tap, dtype=np.float32)
+        h, w = plane.shape
+        out = np.empty((h, w), dtype=np.float32)
+        rc = self.lib.vifo_filter(_fp(plane), w, h, _fp(tap), len(tap),
+                                  _fp(out))
+        if rc != 0:
+            raise ValueError("filter rejected its arguments")
+        return out
+
+    def decimate(self, plane, tap):
+        plane = np.ascontiguousarray(plane, dtype=np.float32)
+        tap = np.ascontiguousarray(tap, dtype=np.float32)
+        h, w = plane.shape
+        out = np.empty((h // 2, w // 2), dtype=np.float32)
+        rc = self.lib.vifo_decimate(_fp(plane), w, h, _fp(tap), len(tap),
+                                    _fp(out))
+        if rc != 0:
+            raise ValueError("decimate rejected its arguments")
+        return out
+
+    def total_rows(self, w, h):
+        return int(self.lib.vifo_total_rows(int(w), int(h)))
+
+    def score(self, ref, dist, bpc, want_rows=False):
+        """Return (out[8] float64, sums[8] float32[, rowsums (rows, 2)])."""
+        ref = np.ascontiguousarray(ref)
+        dist = np.ascontiguousarray(dist)
+        if ref.shape != dist.shape or ref.ndim != 2:
+            raise ValueError("ref and dist must be equal 2-D planes")
+        want = np.uint8 if bpc == 8 else np.uint16
+        if ref.dtype != want or dist.dtype != want:
+            raise ValueError("bpc %d needs %s samples"
+                             % (bpc, np.dtype(want).name))
+        h, w = ref.shape
+        out = np.zeros(8, dtype=np.float64)
+        sums = np.zeros(8, dtype=np.float32)
+        rows = None
+        rp = None
+        if want_rows:
+            rows = np.zeros((self.total_rows(w, h), 2), dtype=np.float32)
+            rp = _fp(rows)
+        rc = self.lib.vifo_score(
+            ref.ctypes.data, dist.ctypes.data, w, h, int(bpc),
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _fp(sums), rp)
+        if rc != 0:
+            raise ValueError("vifo_score rejected its arguments (rc=%d)" % rc)
+        if want_rows:
+            return out, sums, rows
+        return out, sums
+
+
+def _load():
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def taps(scale):
+    return _load().taps(scale)
+
+
+def log2(x):
+    return _load().log2(x)
+
+
+def log2_array(xs):
+    return _load().log2_array(xs)
+
+
+def ratios(a, sv):
+    return _load().ratios(a, sv)
+
+
+def statistic(mu1, mu2, xx, yy, xy):
+    return _load().statistic(mu1, mu2, xx, yy, xy)
+
+
+def normalise(plane, bpc):
+    return _load().normalise(plane, bpc)
+
+
+def filter2d(plane, tap):
+    return _load().filter2d(plane, tap)
+
+
+def decimate(plane, tap):
+    return _load().decimate(plane, tap)
+
+
+def total_rows(w, h):
+    return _load().total_rows(w, h)
+
+
+def score(ref, dist, bpc, want_rows=False):
+    return _load().score(ref, dist, bpc, want_rows)

@@ -1,0 +1,79 @@
+"""Runs the oracle pin battery against one build of the oracle library.
+
+Usage: python tests/mutant_battery.py <path-to-libvif_oracle.so>
+
+Prints one line per pin that fails and exits 1 if any failed, 0 if all
+passed.  Used by test_oracle_mutations.py on deliberately broken copies of
+the oracle (built in a temporary directory, never in place).
+"""
+import os
+import sys
+import traceback
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+sys.path.insert(0, HERE)
+
+import oracle  # noqa: E402
+import test_oracle_pins as P  # noqa: E402
+
+
+def battery(orc):
+    cases = []
+    for s in range(4):
+        cases.append(("taps%d" % s, lambda s=s: P.test_taps_closed_form(orc, s)))
+        cases.append(("impulse%d" % s,
+                      lambda s=s: P.test_filter_interior_impulse(orc, s, 3.0)))
+        cases.append(("mirror%d" % s,
+                      lambda s=s: P.test_filter_whole_sample_mirror(orc, s)))
+        cases.append(("brute%d" % s, lambda s=s: P.test_filter_vs_fp64_bruteforce(
+            orc, (23, 17), s)))
+    for s in (1, 2, 3):
+        cases.append(("decim%d" % s,
+                      lambda s=s: P.test_decimate_vs_fp64_bruteforce(orc, s)))
+    for bpc in (8, 10, 12, 16):
+        cases.append(("norm%d" % bpc,
+                      lambda b=bpc: P.test_normalise_exact_for_every_code(orc, b)))
+    cases += [
+        ("mirror_rb", lambda: P.test_filter_right_bottom_mirror(orc)),
+        ("order", lambda: P.test_filter_order_is_vertical_then_horizontal(orc)),
+        ("decim_phase", lambda: P.test_decimate_even_phase_impulse(orc)),
+        ("bitdepth", lambda: P.test_cross_bit_depth_invariance(orc)),
+        ("flat_sums", lambda: P.test_flat_frame_sums_are_pixel_counts(
+            orc, (40, 40))),
+        ("flat_one", lambda: P.test_flat_frame_scores_exactly_one(orc, 8, 128)),
+        ("self", lambda: P.test_reference_against_itself(orc, 1)),
+        ("stat_low", lambda: P.test_statistic_low_variance_branch(orc)),
+        ("stat_thr", lambda: P.test_statistic_threshold_is_inclusive_high(orc)),
+        ("stat_s2", lambda: P.test_statistic_zero_distorted_variance(orc)),
+        ("stat_neg", lambda: P.test_statistic_negative_gain(orc)),
+        ("stat_fp64", lambda: P.test_statistic_vs_fp64_formula(orc)),
+        ("num_ratio", lambda: P.test_num_ratio_vs_extended_precision(orc)),
+        ("den_ratio", lambda: P.test_den_ratio_closed_form(orc)),
+        ("checker", lambda: P.test_checkerboard_translation_symmetry(orc)),
+        ("reflect", lambda: P.test_intensity_reflection_symmetry_random(orc)),
+        ("log2_pow", lambda: P.test_log2_powers_of_two_exact(orc)),
+        ("log2_all", lambda: P.test_log2_exhaustive_first_binade(orc)),
+        ("log2_e5", lambda: P.test_log2_other_binades(orc, 5)),
+        ("pipe1", lambda: P.test_pipeline_vs_fp64_definition(orc, (32, 32), 1)),
+        ("pipe3", lambda: P.test_pipeline_vs_fp64_definition(orc, (41, 73), 3)),
+    ]
+    return cases
+
+
+def main(path):
+    orc = oracle.Oracle(path)
+    failed = []
+    for name, fn in battery(orc):
+        try:
+            fn()
+        except Exception:  # an assertion or any error counts as caught
+            failed.append(name)
+            tb = traceback.format_exc().strip().splitlines()[-1]
+            print("FAIL %s: %s" % (name, tb[:160]))
+    sys.stdout.flush()
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1]))

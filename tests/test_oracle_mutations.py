@@ -1,0 +1,115 @@
+"""The pins are sharp: plausible mistakes planted in a copy of the oracle
+are each caught by at least one pin.
+
+Each mutant is the oracle's C source with one textual change, compiled into
+a temporary directory and run through tests/mutant_battery.py in its own
+process (so a mutant that crashes cannot take the test run down; a crash
+also counts as caught).  The real oracle must pass the same battery.
+CPU only.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "vif_oracle.c")
+
+# (name, text in vif_oracle.c, replacement).  Not listed: removing the
+# clamp of sigma1_sq at zero, an equivalent mutant (a negative sigma1_sq
+# takes the low-variance branch either way, so no output can change), and
+# evaluating the denominator ratio in fp32 as 1.0f + sigma1_sq * 0.5f, which
+# is provably the same value (see test_den_ratio_closed_form).
+MUTANTS = [
+    ("sigma_n_over_6", "(double)n / 5.0", "(double)n / 6.0"),
+    ("taps_unnormalised", "taps[k] = (float)(g[k] / sum);",
+     "taps[k] = (float)(g[k]);"),
+    ("mirror_half_sample_low", "        m = -m;\n", "        m = -m - 1;\n"),
+    ("mirror_half_sample_high", "m = 2 * (n - 1) - m;", "m = 2 * n - 1 - m;"),
+    ("vertical_tap_offset", "const int yy = mirror(y + k - r, h);",
+     "const int yy = mirror(y + k - r + (k == 0), h);"),
+    ("horizontal_reads_src", "taps[k] * v[(size_t)y * w + xx]",
+     "taps[k] * src[(size_t)y * w + xx]"),
+    ("decimate_odd_phase", "full[(size_t)(2 * y) * w + 2 * x]",
+     "full[(size_t)(2 * y + 1) * w + 2 * x + 1]"),
+    ("decimate_prev_scale_taps",
+     "            if (vifo_decimate(X, ws, hs, taps, nt, Xn) != 0 ||\n"
+     "                vifo_decimate(Y, ws, hs, taps, nt, Yn) != 0)\n",
+     "            float pt[VIFO_MAX_TAPS];\n"
+     "            const int np = vifo_taps(s - 1, pt);\n"
+     "            if (vifo_decimate(X, ws, hs, pt, np, Xn) != 0 ||\n"
+     "                vifo_decimate(Y, ws, hs, pt, np, Yn) != 0)\n"),
+    ("xy_is_xx", "XY[i] = X[i] * Y[i];", "XY[i] = X[i] * X[i];"),
+    ("ref_dist_swapped", "vifo_normalise(ref, w, h, bpc, X);\n"
+     "    vifo_normalise(dist, w, h, bpc, Y);",
+     "vifo_normalise(dist, w, h, bpc, X);\n"
+     "    vifo_normalise(ref, w, h, bpc, Y);"),
+    ("norm10_wrong", "scale = 0.25f;", "scale = 0.125f;"),
+    ("sigma12_sign", "const float sigma12 = xy - mu1_mu2;",
+     "const float sigma12 = mu1_mu2 - xy;"),
+    ("sigma2_no_mean", "float sigma2_sq = yy - mu2_sq;",
+     "float sigma2_sq = yy;"),
+    ("threshold_1", "if ((double)sigma1_sq < kNsq) {",
+     "if ((double)sigma1_sq < 1.0) {"),
+    ("threshold_le", "if ((double)sigma1_sq < kNsq) {",
+     "if ((double)sigma1_sq <= kNsq) {"),
+    ("low_branch_num_0", "        *num_t = 1.0f;\n", "        *num_t = 0.0f;\n"),
+    ("no_nsq_in_num", "(double)sv_sq + kNsq;", "(double)sv_sq + 1.0;"),
+    ("nsq_fp32_num", "const double num_q = (double)num_arg / num_den;",
+     "const double num_q = (double)(num_arg / (float)num_den);"),
+    ("num_single_rounding_fp32", "return (float)(1.0 + num_q);",
+     "return 1.0f + (float)num_q;"),
+    ("den_ratio_inverted", "const double den_q = (double)sigma1_sq / kNsq;",
+     "const double den_q = kNsq / (double)sigma1_sq;"),
+    ("no_negative_gain_rule", "if (g < 0.0f) {", "if (g < -1e30f) {"),
+    ("sv_floor_1", "if (sv_sq < eps)\n        sv_sq = eps;",
+     "if (sv_sq < 1.0f)\n        sv_sq = 1.0f;"),
+    ("gain_not_squared", "const float g_sq = g * g;", "const float g_sq = g;"),
+    ("log2_bias", "- 127;", "- 126;"),
+    ("log2_coef_sign", "0xbe6194f1u", "0x3e6194f1u"),
+    ("log2_drop_last_coef", "0xbb96254au", "0x00000000u"),
+    ("log2_t_not_minus_one", "const float t = m - 1.0f;",
+     "const float t = m - 0.5f;"),
+    ("row_sum_swapped", "n_s = n_s + n_y;", "n_s = n_s + d_y;"),
+    ("totals_skip_scale1", "num = (double)N[0] + (double)N[1];",
+     "num = (double)N[0] + (double)N[0];"),
+    ("score_inverted", "out[s] = (double)N[s] / (double)D[s];",
+     "out[s] = (double)D[s] / (double)N[s];"),
+]
+
+
+def _run(path):
+    return subprocess.run([sys.executable, os.path.join(HERE,
+                                                        "mutant_battery.py"),
+                           path], capture_output=True, text=True, timeout=600)
+
+
+def _build_mutant(tmp, name, old, new):
+    import oracle
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation %s does not apply" % name
+    mutated = src.replace(old, new, 1)
+    cpath = os.path.join(tmp, name + ".c")
+    with open(cpath, "w") as f:
+        f.write(mutated)
+    return oracle.build(src=cpath, out=os.path.join(tmp, name + ".so"))
+
+
+def test_real_oracle_passes_battery():
+    import oracle
+    oracle._load()
+    r = _run(oracle._LIB)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_every_mutant_is_caught(tmp_path):
+    tmp = str(tmp_path)
+    libs = [(name, _build_mutant(tmp, name, old, new))
+            for (name, old, new) in MUTANTS]
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda nl: (nl[0], _run(nl[1])), libs))
+    survivors = [name for name, r in results if r.returncode == 0]
+    assert not survivors, "mutants not caught by any pin: %s" % survivors
