@@ -1,0 +1,224 @@
+"""Throughput of the float VIF feature on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step scores one 3840x2160 8-bit luma frame pair (the whole path: four
+scales of filtering, statistic, decimation and row sums, one read-back and
+the host sums).  The 20 synthetic 1/f-noise frame pairs are resident in HBM
+before the timed region; steps cycle through them.  Prints one JSON line.
+
+The line carries, besides the contract fields:
+  roofline      the dominant kernel (the scale-0 filter/statistic kernel):
+                algorithmic fp32 operations per launch / its average duration,
+                timed with HIP events on the context's stream during the timed
+                region, against the VALU peak; `traffic` is the kernel's HBM
+                bytes per launch from committed rocprofv3 counters when the
+                kernel source has not changed since they were taken, else null.
+  cpu_baseline  the CPU oracle on this host, one core, on a bounded sample of
+                the same workload.
+  extra         1920x1080 frames/s, HBM GB/s of the whole frame from counters
+                when available, and the per-kernel split.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("VIF frames/sec at 1080p and 4K on 1 MI355X; achieved HBM GB/s vs "
+          "peak")
+
+# Plain fp32 VALU operations per launch of the scale-0 kernel, counted from
+# the definition (no fused multiply-add, no packed math): per scale-0 pixel
+# 3 products + 5 quantities x 2 passes x (17 mul + 16 add) + 8 for the
+# variances = 341, plus the next scale's 9-tap low-pass of both planes at
+# even rows (two columns per decimated pixel) and even columns: 2 planes x 3
+# x (9 mul + 8 add) = 102 per scale-1 pixel = 25.5 per scale-0 pixel.  The
+# statistic's own operations are left out (they depend on the content), so
+# the figure is a lower bound of the work done.
+OPS_PER_PIXEL_SCALE0 = 341.0 + 102.0 / 4.0
+
+# VALU peak for plain (unfused, unpacked) fp32 operations: 256 CUs x 4 SIMDs
+# x 16 lanes x 2.4 GHz = 39.3e12 operations/s.
+VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+
+HBM_PEAK_GBS = 8000.0
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in ("vif_image_fidelity_amd/csrc/vif_kernels.hip",
+                "vif_image_fidelity_amd/csrc/vif_device_math.h",
+                "vif_image_fidelity_amd/csrc/vif_internal.h",
+                "vif_image_fidelity_amd/build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """Counter-derived HBM bytes per launch of the scale-0 kernel, if taken
+    on the current kernel source."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None, None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None, None
+    return rec.get("scale0_bytes_per_launch"), rec.get("frame_bytes")
+
+
+def ensure_lib():
+    from vif_image_fidelity_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    _lib.load()
+
+
+def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
+    import torch
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    pairs = [(td(r), td(d)) for (r, d, _) in frames]
+    ctx = V.Vif(w, h, bpc)
+    for i in range(warmup):
+        r, d = pairs[i % len(pairs)]
+        ctx.score(r, d)
+    ctx.set_profiling(prof_kinds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r, d = pairs[i % len(pairs)]
+        ctx.score(r, d)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = ctx.kernel_times()
+    ctx.close()
+    return (t1 - t0), kt
+
+
+def cpu_baseline(frames, budget_s=12.0):
+    import oracle
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r, d, b = frames[n % len(frames)]
+        oracle.score(r, d, b)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return n / dt, n, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--frames", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps-1080p", type=int, default=500)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the feature on "
+              "a single MI355X (frames shard across GPUs with no exchange; "
+              "see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ensure_lib()
+    import vif_image_fidelity_amd as V
+    from vif_image_fidelity_amd import synth
+
+    print("generating %d synthetic 3840x2160 frame pairs" % args.frames,
+          file=sys.stderr, flush=True)
+    frames4k = synth.pink_4k_8bit(frames=args.frames)
+    w, h, bpc = 3840, 2160, 8
+
+    dt, kt = time_frames(V, frames4k, w, h, bpc, args.steps, args.warmup,
+                         prof_kinds=["scale0"])
+    fps = args.steps / dt
+    ms_step = 1000.0 * dt / args.steps
+    s0_ms, s0_n = kt["scale0"]
+    s0_avg_ms = s0_ms / max(s0_n, 1)
+    print("4K: %.1f frames/s, %.3f ms/step; scale-0 kernel %.1f us avg"
+          % (fps, ms_step, 1000 * s0_avg_ms), file=sys.stderr, flush=True)
+
+    # per-kernel split (all kinds timed; separate run, not the headline)
+    _, kt_all = time_frames(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
+                            prof_kinds=0xFF)
+    split = {k: round(1000.0 * ms / max(n, 1), 2) for k, (ms, n) in
+             kt_all.items()}
+
+    # 1080p (10-bit checkerboard workload) for the metric's second size
+    f1080 = synth.checker_1080p_10bit()
+    dt1080, _ = time_frames(V, f1080, 1920, 1080, 10, args.steps_1080p, 10)
+    fps1080 = args.steps_1080p / dt1080
+
+    ops = OPS_PER_PIXEL_SCALE0 * w * h
+    achieved = ops / (s0_avg_ms / 1000.0) / 1e12
+    peak = VALU_PEAK_OPS / 1e12
+    traffic, frame_bytes = load_traffic()
+    roofline = {"bound": "alu", "achieved": round(achieved, 3),
+                "peak": round(peak, 2), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    extra = {"fps_1080p_10bit": round(fps1080, 1),
+             "kernel_avg_us_4k": split,
+             "scale0_kernel_avg_us": round(1000 * s0_avg_ms, 2)}
+    if frame_bytes:
+        gbs = frame_bytes * fps / 1e9
+        extra["hbm_gbs_per_frame_counters"] = round(gbs, 1)
+        extra["hbm_frac_of_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cfps, cn, cdt = cpu_baseline(frames4k)
+        cpu = {"value": round(cfps, 4), "unit": "frames/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "%d of the 3840x2160 8-bit frame pairs, single "
+                         "thread, %.1f s" % (cn, cdt)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(fps, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "pink_4k_8bit: 3840x2160 8-bit luma pairs, "
+                               "1/f-noise ref, 2x down/up-scaled dist, %d "
+                               "frames resident in HBM" % args.frames,
+                   "w": w, "h": h, "bpc": bpc, "scales": 4},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * vif.h -- C ABI of the MI355X (gfx950) float VIF feature extractor.
+ *
+ * One call scores one reference/distorted luma frame pair with the float
+ * VIF feature: four scales, a separable Gaussian low-pass (17/9/5/3 taps)
+ * with mirrored borders, 2x decimation between scales, per-pixel local
+ * statistics, the two one-plus-ratio values evaluated in fp64 and rounded
+ * to fp32 once, a log2 polynomial, and fp32 sums per row and then over the
+ * rows.  The results are bit-identical to the CPU definition.
+ *
+ * Sources (page title, section):
+ *   ADR-1422 "float_vif_sycl computes the CPU's arithmetic without an fp64
+ *     type ...", Context and Decision: taps generated at run time and passed
+ *     to each launch by value; the fp64 expressions; one fp32 accumulator
+ *     per row, rows added top to bottom; two floats per row per scale read
+ *     back in one copy and added on the host.
+ *   ADR-1444 "float_vif_hip runs the arithmetic of the CUDA twin ...",
+ *     Decision and Consequences: reflected-then-clamped tile indices, frames
+ *     from 16x16 up, the frame ratio and the per-scale sums as outputs.
+ *   Research-2130 "float_ssim decimation on the SYCL device", Sources
+ *     (sample normalisation) and Open questions (a submit fails cleanly
+ *     instead of dereferencing NULL).
+ *
+ * No C++ or torch types cross this boundary.  Every function is safe to call
+ * from C.  Functions that return int return VIF_OK (0) on success or a
+ * negative VIF_E* code; the code of the last failure on the calling thread
+ * is also kept for vif_errno().
+ */
+#ifndef VIF_H
+#define VIF_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VIF_OK 0
+#define VIF_EINVAL (-1) /* bad geometry, bit depth, NULL pointer, state   */
+#define VIF_ENOMEM (-2) /* device or pinned host allocation failed        */
+#define VIF_EHIP (-3)   /* any other HIP runtime error (see vif_strerror)  */
+
+#define VIF_NSCALES 4
+#define VIF_MAX_TAPS 17
+#define VIF_MIN_SIDE 16          /* smallest width or height accepted     */
+#define VIF_MAX_PIXELS (1L << 27) /* largest w * h accepted               */
+
+typedef struct vif_ctx vif_ctx;
+
+/*
+ * vif_create -- a scoring context for frames of w x h samples at bpc bits.
+ *   w, h   >= VIF_MIN_SIDE and w * h <= VIF_MAX_PIXELS.  The pages' smallest
+ *          scored frame is 16x16 (ADR-1444, Consequences).
+ *   bpc    8, 10, 12 or 16 (Research-2130, Sources: 8-bit samples used as
+ *          they are, wider samples divided by 4, 16 or 256).
+ * Allocates every device buffer the context needs (pyramid planes, term
+ * planes, row sums) and a pinned host buffer, on the device current at the
+ * call, and computes the taps on the host.  Work goes to the default stream
+ * unless vif_set_stream() is called.  Returns NULL on failure; vif_errno()
+ * then gives VIF_EINVAL, VIF_ENOMEM or VIF_EHIP.  Geometry is refused here,
+ * never in the middle of a frame.
+ */
+vif_ctx *vif_create(int w, int h, int bpc);
+
+/*
+ * vif_score -- score one frame pair.
+ *   ref, dist  DEVICE pointers to tightly packed row-major planes (pitch =
+ *              w samples): uint8_t when bpc is 8, else uint16_t holding the
+ *              sample in its low bits (2-byte aligned).  Sample values are
+ *              used as given (no range check).  Owned by the caller, who
+ *              keeps them valid until the call returns.
+ *   out        HOST memory for 8 doubles, owned by the caller:
+ *                out[0..3] vif_scale0..3 = N_s / D_s in fp64
+ *                out[4]    num = ((N_0 + N_1) + N_2) + N_3 in fp64
+ *                out[5]    den, the same way
+ *                out[6]    num / den (the frame's vif ratio)
+ *                out[7]    0.0 (reserved)
+ *              where N_s, D_s are the fp32 sums of scale s.
+ * Synchronous: returns after the results are on the host.  Allocates
+ * nothing.  One call in flight per context; a context is not thread-safe,
+ * separate contexts are independent.  On error out is left untouched.
+ */
+int vif_score(vif_ctx *ctx, const void *ref, const void *dist, double out[8]);
+
+/* vif_destroy -- frees everything the context owns.  NULL is a no-op. */
+void vif_destroy(vif_ctx *ctx);
+
+/*
+ * vif_set_stream -- run the context's work on a HIP stream (a hipStream_t
+ * passed as void*, e.g. torch's current stream; NULL = default stream).
+ * The caller keeps the stream alive while the context uses it.
+ */
+int vif_set_stream(vif_ctx *ctx, void *hip_stream);
+
+/*
+ * vif_get_sums -- the fp32 per-scale sums of the last successful
+ * vif_score: N_0, D_0, N_1, D_1, N_2, D_2, N_3, D_3 (the eight per-scale
+ * sums of the pages' debug output, ADR-1422, Consequences).
+ * VIF_EINVAL if no frame has been scored yet.
+ */
+int vif_get_sums(const vif_ctx *ctx, float sums[8]);
+
+/*
+ * vif_get_row_sums -- the per-row fp32 sums of the last successful
+ * vif_score, as they came back from the device: for scale 0..3, for row
+ * y = 0..h_s-1, the pair (n_y, d_y).  rows must hold 2 * capacity floats.
+ * Returns the total number of rows (h_0 + h_1 + h_2 + h_3) when capacity
+ * is large enough, else VIF_EINVAL.  Plane heights halve with floor.
+ */
+int vif_get_row_sums(const vif_ctx *ctx, float *rows, int capacity);
+
+/*
+ * vif_taps -- the fp32 Gaussian taps of scale 0..3 that the context passes
+ * to its kernels (ADR-1422, Decision: taps computed on the host at run time
+ * and passed by value).  Writes N floats to taps (room for VIF_MAX_TAPS)
+ * and returns N (17, 9, 5 or 3), or VIF_EINVAL.  Host only; needs no GPU.
+ */
+int vif_taps(int scale, float *taps);
+
+/*
+ * vif_set_profiling -- kinds is a bit mask of kernel kinds (bit k = kind k
+ * of vif_get_kernel_times; 0xff = all, 0 = off).  vif_score then records a
+ * pair of HIP events around each launch of those kinds on the context's
+ * stream and accumulates their durations (a small cost per event).  Every
+ * call resets the totals.
+ */
+int vif_set_profiling(vif_ctx *ctx, int kinds);
+
+/*
+ * vif_get_kernel_times -- accumulated kernel durations in milliseconds and
+ * launch counts since profiling was enabled, one entry per kernel kind:
+ *   0..3  the per-scale filter/statistic kernel of scale 0..3
+ *   4..7  the row-sum kernel of scale 0..3
+ * ms and launches hold at least `capacity` entries (either may be NULL).
+ * Returns the number of kinds (8) or VIF_EINVAL.
+ */
+int vif_get_kernel_times(const vif_ctx *ctx, double *ms, long *launches,
+                         int capacity);
+
+/* vif_errno -- the last error code set on the calling thread (0 if none). */
+int vif_errno(void);
+
+/* vif_strerror -- a static description of an error code.  For VIF_EHIP it
+ * names the HIP error of the calling thread's last failure. */
+const char *vif_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIF_H */

@@ -1,0 +1,61 @@
+/*
+ * vif_selftest.h -- device-math gates of the float VIF library.
+ *
+ * These entry points run the device functions of the scoring kernels (the
+ * same inline code, not copies) over caller-provided arrays, so a test can
+ * compare the device's arithmetic with the host's bit for bit before
+ * trusting the pipeline.  The pattern follows ADR-1444 "float_vif_hip runs
+ * the arithmetic of the CUDA twin ...", Decision: the device's fp64 add and
+ * divide were compared with the host's over 33.5 million operand pairs from
+ * 2^-40 to 2^40 and six noise variances, checking the sum, the quotient and
+ * both fp32 roundings of one plus the quotient; and Consequences: a
+ * device-math test compares the shared arithmetic with the CPU's.
+ *
+ * Every pointer is a DEVICE pointer owned by the caller; n >= 0 elements;
+ * stream is a hipStream_t as void* (NULL = default stream).  Each call is
+ * synchronous (it waits for its kernel).  Returns VIF_OK or VIF_EINVAL (NULL
+ * pointer, n < 0) or VIF_EHIP.
+ */
+#ifndef VIF_SELFTEST_H
+#define VIF_SELFTEST_H
+
+#include "vif.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* For each i, with a, b fp32 and nsq fp64:
+ *   sum[i]   = (double)b[i] + nsq                       (fp64 add)
+ *   quot[i]  = (double)a[i] / sum[i]                    (fp64 divide)
+ *   rnum[i]  = (float)(1.0 + quot[i])                   (fp64 add, cvt)
+ *   rden[i]  = (float)(1.0 + (double)a[i] / nsq)        (fp64 div, add, cvt)
+ */
+int vif_selftest_fp64(const float *a, const float *b, double nsq, long n,
+                      double *sum, double *quot, float *rnum, float *rden,
+                      void *stream);
+
+/* q[i] = a[i] / b[i] in fp32 with the kernels' (correctly rounded)
+ * division. */
+int vif_selftest_div32(const float *a, const float *b, long n, float *q,
+                       void *stream);
+
+/* y[i] = the kernels' log2 polynomial of x[i] (x[i] finite, >= 1). */
+int vif_selftest_log2(const float *x, long n, float *y, void *stream);
+
+/* The kernels' one-plus-ratio values with the built-in noise variance 2.0:
+ *   num[i] = fl32(1 + a[i] / (sv[i] + 2)),  den[i] = fl32(1 + a[i] / 2). */
+int vif_selftest_ratios(const float *a, const float *sv, long n, float *num,
+                        float *den, void *stream);
+
+/* The kernels' per-pixel statistic: from the five filtered values
+ * (mu1, mu2, xx, yy, xy, each an array of n floats) to the two terms. */
+int vif_selftest_statistic(const float *mu1, const float *mu2,
+                           const float *xx, const float *yy, const float *xy,
+                           long n, float *num, float *den, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIF_SELFTEST_H */

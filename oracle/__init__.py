@@ -60,6 +60,8 @@ class Oracle:
                                           ctypes.c_long]
         lib.vifo_ratio_arrays.restype = None
         lib.vifo_statistic.argtypes = [ctypes.c_float] * 5 + [f32p, f32p]
+        lib.vifo_statistic_array.argtypes = [f32p] * 7 + [ctypes.c_long]
+        lib.vifo_statistic_array.restype = None
         lib.vifo_statistic.restype = None
         lib.vifo_normalise.argtypes = [ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, f32p]
@@ -112,6 +114,16 @@ class Oracle:
                                 float(np.float32(xy)), ctypes.byref(n),
                                 ctypes.byref(d))
         return np.float32(n.value), np.float32(d.value)
+
+    def statistic_array(self, mu1, mu2, xx, yy, xy):
+        """vifo_statistic element-wise over five float32 arrays."""
+        ins = [np.ascontiguousarray(a, dtype=np.float32)
+               for a in (mu1, mu2, xx, yy, xy)]
+        num = np.empty_like(ins[0])
+        den = np.empty_like(ins[0])
+        self.lib.vifo_statistic_array(*[_fp(a) for a in ins], _fp(num),
+                                      _fp(den), ins[0].size)
+        return num, den
 
     def normalise(self, plane, bpc):
         plane = np.ascontiguousarray(plane)
@@ -203,6 +215,10 @@ def ratios(a, sv):
 
 def statistic(mu1, mu2, xx, yy, xy):
     return _load().statistic(mu1, mu2, xx, yy, xy)
+
+
+def statistic_array(mu1, mu2, xx, yy, xy):
+    return _load().statistic_array(mu1, mu2, xx, yy, xy)
 
 
 def normalise(plane, bpc):

@@ -192,6 +192,15 @@ void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
     *den_t = vifo_log2(vifo_den_ratio(sigma1_sq));
 }
 
+void vifo_statistic_array(const float *mu1, const float *mu2, const float *xx,
+                          const float *yy, const float *xy, float *num_t,
+                          float *den_t, long n)
+{
+    for (long i = 0; i < n; i++)
+        vifo_statistic(mu1[i], mu2[i], xx[i], yy[i], xy[i], &num_t[i],
+                       &den_t[i]);
+}
+
 /* ---------------------------------------------------------------------- */
 /* O2  normalisation [Research-2130 Sources, picture_copy]: 8-bit samples
  * as they are, 10/12/16-bit samples divided by 4/16/256.  Reading: no

@@ -50,6 +50,11 @@ void vifo_ratio_arrays(const float *a, const float *sv, float *num_out,
 void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
                     float *num_t, float *den_t);
 
+/* vifo_statistic over n pixels given as five arrays. */
+void vifo_statistic_array(const float *mu1, const float *mu2, const float *xx,
+                          const float *yy, const float *xy, float *num_t,
+                          float *den_t, long n);
+
 /* Sample normalisation of a w*h plane to fp32. */
 int vifo_normalise(const void *src, int w, int h, int bpc, float *dst);
 

@@ -1,0 +1,39 @@
+"""Helpers shared by the tests: load the built HIP library (building it only
+if nothing is built), parse the public headers, move frames to the GPU."""
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def ensure_built():
+    from vif_image_fidelity_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return _lib.load()
+
+
+def header_functions():
+    """Every function name declared in include/*.h."""
+    names = []
+    for fn in sorted(os.listdir(INCLUDE)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b(vif_[a-z0-9_]+)\s*\(", text):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def to_device(plane):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(plane)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16))
+    else:
+        t = torch.from_numpy(a)
+    return t.to("cuda:0")

@@ -1,0 +1,184 @@
+"""Device-math gates (GPU): the kernels' own device functions against the
+host, bit for bit, before the pipeline is trusted.
+
+ADR-1444 "float_vif_hip runs the arithmetic of the CUDA twin ...",
+Decision: the device's fp64 add and divide were compared with the host's
+over 33.5 million operand pairs spanning 2^-40 to 2^40 and six noise
+variances (the sum, the quotient and both fp32 roundings of one plus the
+quotient).  Here: 2^25 pairs over the same span, six variances, plus
+targeted near-ties; the fp32 division; the log2 polynomial exhaustively
+(every mantissa of exponents 0..31); the ratios and the whole statistic
+against the oracle.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from libutil import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FACTS = json.load(open(os.path.join(HERE, "golden", "page_facts.json")))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    lib = ensure_built()
+    assert torch.cuda.is_available()
+    return lib
+
+
+def _d(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _h(t):
+    return t.cpu().numpy()
+
+
+def _check(rc):
+    assert rc == 0, rc
+
+
+def _span_operands(g, n, lo=-40, hi=40):
+    e = g.uniform(lo, hi, size=n)
+    return np.exp2(e).astype(np.float32)
+
+
+def _near_ties(g, n, nsq):
+    """Pairs (a, b) whose 1 + a/(b + nsq) lies within ~2^-24 (relative) of a
+    midpoint between two fp32 values: the double-rounding zone."""
+    lo = np.exp2(g.uniform(0, 20, size=n)).astype(np.float32)
+    up = np.nextafter(lo, np.float32(np.inf))
+    mid = (lo.astype(np.float64) + up.astype(np.float64)) / 2
+    b = _span_operands(g, n, -20, 20)
+    a = ((mid - 1.0) * (b.astype(np.float64) + nsq)).astype(np.float32)
+    return a, b
+
+
+@pytest.mark.parametrize("nsq", FACTS["fp64_gate_nsq_values"]["value"])
+def test_fp64_add_div_cvt_bitwise(dev, nsq):
+    import torch
+    from vif_image_fidelity_amd import _lib
+    total = FACTS["fp64_gate_pairs"]["value"]
+    lo, hi = FACTS["fp64_gate_exponent_span"]["value"]
+    n = total // 6 + 1
+    g = np.random.Generator(np.random.PCG64(int(nsq * 1000)))
+    a = _span_operands(g, n, lo, hi)
+    b = _span_operands(g, n, lo, hi)
+    ta, tb = _near_ties(g, 1 << 18, nsq)
+    a = np.concatenate([a, ta])
+    b = np.concatenate([b, tb])
+    m = a.size
+    da, db = _d(a), _d(b)
+    s = torch.empty(m, dtype=torch.float64, device="cuda:0")
+    q = torch.empty_like(s)
+    rn = torch.empty(m, dtype=torch.float32, device="cuda:0")
+    rd = torch.empty_like(rn)
+    _check(_lib.load().vif_selftest_fp64(da.data_ptr(), db.data_ptr(), nsq, m,
+                                         s.data_ptr(), q.data_ptr(),
+                                         rn.data_ptr(), rd.data_ptr(), None))
+    hs = b.astype(np.float64) + nsq
+    hq = a.astype(np.float64) / hs
+    hrn = (1.0 + hq).astype(np.float32)
+    hrd = (1.0 + a.astype(np.float64) / nsq).astype(np.float32)
+    assert np.array_equal(_h(s).view(np.uint64), hs.view(np.uint64))
+    assert np.array_equal(_h(q).view(np.uint64), hq.view(np.uint64))
+    assert np.array_equal(_h(rn).view(np.uint32), hrn.view(np.uint32))
+    assert np.array_equal(_h(rd).view(np.uint32), hrd.view(np.uint32))
+
+
+def test_fp32_division_bitwise(dev):
+    import torch
+    from vif_image_fidelity_amd import _lib
+    g = np.random.Generator(np.random.PCG64(31))
+    n = 1 << 25
+    a = (_span_operands(g, n, -60, 60) *
+         np.where(g.random(n) < 0.5, -1, 1)).astype(np.float32)
+    b = (_span_operands(g, n, -60, 60) *
+         np.where(g.random(n) < 0.5, -1, 1)).astype(np.float32)
+    q = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    da, db = _d(a), _d(b)  # keep the device copies alive across the call
+    _check(_lib.load().vif_selftest_div32(da.data_ptr(), db.data_ptr(),
+                                          n, q.data_ptr(), None))
+    assert np.array_equal(_h(q).view(np.uint32), (a / b).view(np.uint32))
+
+
+def test_log2_exhaustive_bitwise(dev, orc):
+    """Every fp32 mantissa of every exponent 0..31: device == oracle."""
+    import torch
+    from vif_image_fidelity_amd import _lib
+    m = np.arange(1 << 23, dtype=np.uint32)
+    y = torch.empty(1 << 23, dtype=torch.float32, device="cuda:0")
+    for e in range(32):
+        x = ((np.uint32(127 + e) << np.uint32(23)) | m).view(np.float32)
+        dx = _d(x)
+        _check(_lib.load().vif_selftest_log2(dx.data_ptr(), x.size,
+                                             y.data_ptr(), None))
+        ref = orc.log2_array(x)
+        assert np.array_equal(_h(y).view(np.uint32), ref.view(np.uint32)), e
+
+
+def test_ratios_bitwise(dev, orc):
+    import torch
+    from vif_image_fidelity_amd import _lib
+    g = np.random.Generator(np.random.PCG64(32))
+    n = 1 << 22
+    a = np.exp(g.uniform(np.log(1e-6), np.log(5e8), n)).astype(np.float32)
+    sv = np.exp(g.uniform(np.log(1e-10), np.log(1e5), n)).astype(np.float32)
+    ta, tb = _near_ties(g, 1 << 18, 2.0)
+    a = np.concatenate([a, ta])
+    sv = np.concatenate([sv, tb])
+    num = torch.empty(a.size, dtype=torch.float32, device="cuda:0")
+    den = torch.empty_like(num)
+    da, dsv = _d(a), _d(sv)
+    _check(_lib.load().vif_selftest_ratios(da.data_ptr(), dsv.data_ptr(),
+                                           a.size, num.data_ptr(),
+                                           den.data_ptr(), None))
+    rn, rd = orc.ratios(a, sv)
+    assert np.array_equal(_h(num).view(np.uint32), rn.view(np.uint32))
+    assert np.array_equal(_h(den).view(np.uint32), rd.view(np.uint32))
+
+
+def _statistic_inputs(g, n):
+    """Five filtered values shaped like real data: means in [0, 256),
+    variances from 0 to ~2e4 (many near the noise variance 2), covariance
+    of either sign, with the cancellation of xx - mu^2 in fp32."""
+    mu1 = g.uniform(0, 256, n).astype(np.float32)
+    mu2 = g.uniform(0, 256, n).astype(np.float32)
+    v1 = np.where(g.random(n) < 0.3, g.uniform(0, 4, n),
+                  np.exp(g.uniform(-3, 10, n)))
+    v2 = np.where(g.random(n) < 0.3, g.uniform(0, 4, n),
+                  np.exp(g.uniform(-3, 10, n)))
+    rho = g.uniform(-1, 1, n)
+    c = rho * np.sqrt(v1 * v2)
+    xx = (mu1.astype(np.float64) ** 2 + v1).astype(np.float32)
+    yy = (mu2.astype(np.float64) ** 2 + v2).astype(np.float32)
+    xy = (mu1.astype(np.float64) * mu2 + c).astype(np.float32)
+    return mu1, mu2, xx, yy, xy
+
+
+def test_statistic_bitwise(dev, orc):
+    import torch
+    from vif_image_fidelity_amd import _lib
+    g = np.random.Generator(np.random.PCG64(33))
+    n = 1 << 22
+    ins = _statistic_inputs(g, n)
+    dins = [_d(a) for a in ins]
+    num = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    den = torch.empty_like(num)
+    _check(_lib.load().vif_selftest_statistic(
+        *[t.data_ptr() for t in dins], n, num.data_ptr(), den.data_ptr(),
+        None))
+    rn, rd = orc.statistic_array(*ins)
+    assert np.array_equal(_h(num).view(np.uint32), rn.view(np.uint32))
+    assert np.array_equal(_h(den).view(np.uint32), rd.view(np.uint32))
+    # the sample really exercises both branches and every clamp
+    hi = rd != 1.0
+    assert 0.2 < hi.mean() < 0.95
+    assert (rn[hi] == 0).any()

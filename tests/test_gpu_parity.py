@@ -1,0 +1,171 @@
+"""Full-pipeline parity (GPU): the HIP path through the C ABI against the CPU
+oracle on the same seeded frames, bit for bit: every output of every frame
+(out[0..7]), the eight per-scale fp32 sums and every per-row fp32 sum.  The
+largest absolute difference is always computed and anything above the
+pages' 5e-5 gate fails on its own (Research-2130, Findings; ADR-1444,
+Context), before the 0-ULP assertion.
+
+Workloads: the five synthetic stand-ins of vif_image_fidelity_amd.synth,
+plus edge geometries (16x16, ragged tiles, tall and wide frames, odd sizes)
+and bit-depth invariance.  The 3840x2160 workload runs its first two frames
+in full in the launch configuration the benchmark times.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from libutil import ensure_built, to_device
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FACTS = json.load(open(os.path.join(HERE, "golden", "page_facts.json")))
+GATE = FACTS["parity_gate"]["value"]
+
+
+@pytest.fixture(scope="module")
+def V():
+    import torch
+    ensure_built()
+    assert torch.cuda.is_available()
+    import vif_image_fidelity_amd as V
+    return V
+
+
+_ctx_cache = {}
+
+
+def _ctx(V, w, h, bpc):
+    key = (w, h, bpc)
+    if key not in _ctx_cache:
+        _ctx_cache[key] = V.Vif(w, h, bpc)
+    return _ctx_cache[key]
+
+
+def _compare(V, orc, ref, dist, bpc, label):
+    h, w = ref.shape
+    print("parity case %s %dx%d bpc %d" % (label, w, h, bpc), flush=True)
+    ctx = _ctx(V, w, h, bpc)
+    got = ctx.score(to_device(ref), to_device(dist))
+    gsums = ctx.sums()
+    grows = ctx.row_sums()
+    exp, esums, erows = orc.score(ref, dist, bpc, want_rows=True)
+    maxdiff = float(np.max(np.abs(got - exp)))
+    print("  max|diff| = %.3g" % maxdiff, flush=True)
+    assert maxdiff <= GATE, (label, maxdiff)
+    assert got.view(np.uint64).tolist() == exp.view(np.uint64).tolist(), \
+        (label, got, exp)
+    assert gsums.view(np.uint32).tolist() == esums.view(np.uint32).tolist()
+    bad = np.nonzero(grows.view(np.uint32) != erows.view(np.uint32))
+    assert bad[0].size == 0, (label, bad[0][:10])
+    return got
+
+
+@pytest.mark.parametrize("name", ["netflix_576x324_8bit", "tiny_frames_8bit",
+                                  "checker_1080p_10bit",
+                                  "bright_1080p_16bit"])
+def test_workload_parity(V, orc, name):
+    from vif_image_fidelity_amd import synth
+    for i, (ref, dist, bpc) in enumerate(synth.WORKLOADS[name]()):
+        _compare(V, orc, ref, dist, bpc, "%s[%d]" % (name, i))
+
+
+def test_4k_parity_first_frames(V, orc):
+    from vif_image_fidelity_amd import synth
+    for i in range(2):
+        ref, dist, bpc = synth.pink_4k_frame(i)
+        _compare(V, orc, ref, dist, bpc, "pink_4k_8bit[%d]" % i)
+
+
+EDGE_SHAPES = [(16, 16), (17, 16), (16, 17), (112, 16), (113, 17), (224, 32),
+               (225, 33), (16, 300), (300, 16), (71, 71), (72, 72), (73, 41),
+               (129, 97), (1000, 37), (37, 1000), (3841, 33)]
+
+
+@pytest.mark.parametrize("wh", EDGE_SHAPES)
+def test_edge_geometry_parity(V, orc, wh):
+    w, h = wh
+    g = np.random.Generator(np.random.PCG64(w * 7919 + h))
+    ref = g.integers(0, 256, size=(h, w)).astype(np.uint8)
+    dist = np.clip(ref.astype(np.int64) + g.integers(-25, 26, size=(h, w)),
+                   0, 255).astype(np.uint8)
+    _compare(V, orc, ref, dist, 8, "edge")
+
+
+@pytest.mark.parametrize("bpc", [10, 12, 16])
+def test_wide_samples_parity_and_invariance(V, orc, bpc):
+    """Random wide samples at parity; and a frame whose codes are 4/16/256
+    times an 8-bit frame's scores bit-identically to the 8-bit frame."""
+    g = np.random.Generator(np.random.PCG64(bpc))
+    h, w = 90, 150
+    top = (1 << bpc) - 1
+    ref = g.integers(0, top + 1, size=(h, w)).astype(np.uint16)
+    dist = np.clip(ref.astype(np.int64) + g.integers(-top // 20, top // 20,
+                                                      size=(h, w)),
+                   0, top).astype(np.uint16)
+    _compare(V, orc, ref, dist, bpc, "wide%d" % bpc)
+    r8 = g.integers(0, 256, size=(h, w)).astype(np.uint8)
+    d8 = np.clip(r8.astype(np.int64) + g.integers(-9, 10, size=(h, w)), 0,
+                 255).astype(np.uint8)
+    mul = 1 << (bpc - 8)
+    a = _compare(V, orc, r8, d8, 8, "inv8")
+    b = _compare(V, orc, (r8.astype(np.uint32) * mul).astype(np.uint16),
+                 (d8.astype(np.uint32) * mul).astype(np.uint16), bpc,
+                 "inv%d" % bpc)
+    assert a.tobytes() == b.tobytes()
+
+
+def test_flat_and_identical_frames(V, orc):
+    f = np.full((64, 80), 200, np.uint8)
+    out = _compare(V, orc, f, f, 8, "flat")
+    assert np.all(out[:4] == 1.0) and out[6] == 1.0
+    assert out[4] == out[5] == 80 * 64 + 40 * 32 + 20 * 16 + 10 * 8
+    g = np.random.Generator(np.random.PCG64(9))
+    r = g.integers(0, 256, size=(64, 80)).astype(np.uint8)
+    out = _compare(V, orc, r, r, 8, "self")
+    assert abs(out[4] - out[5]) <= 1e-6 * out[5]
+
+
+def test_repeat_is_deterministic_and_stream_aware(V, orc):
+    import torch
+    from vif_image_fidelity_amd import synth
+    ref, dist, bpc = synth.netflix_576x324_8bit(frames=1)[0]
+    ctx = V.Vif(576, 324, 8)
+    dr, dd = to_device(ref), to_device(dist)
+    a = ctx.score(dr, dd)
+    s = torch.cuda.Stream()
+    ctx.set_stream(s)
+    b = ctx.score(dr, dd)
+    ctx.set_stream(None)
+    c = ctx.score(dr, dd)
+    assert a.tobytes() == b.tobytes() == c.tobytes()
+    ctx.close()
+
+
+def test_profiling_counts_launches(V):
+    from vif_image_fidelity_amd import synth
+    ref, dist, bpc = synth.netflix_576x324_8bit(frames=1)[0]
+    ctx = V.Vif(576, 324, 8)
+    ctx.set_profiling(True)
+    dr, dd = to_device(ref), to_device(dist)
+    for _ in range(3):
+        ctx.score(dr, dd)
+    kt = ctx.kernel_times()
+    for kind in V.KERNEL_KINDS:
+        ms, n = kt[kind]
+        assert n == 3 and ms > 0, kind
+    ctx.close()
+
+
+def test_score_rejects_misaligned_wide_pointer(V):
+    import torch
+    ctx = V.Vif(64, 64, 10)
+    buf = torch.zeros(64 * 64 * 2 + 2, dtype=torch.uint8, device="cuda:0")
+    from vif_image_fidelity_amd import _lib
+    out = np.zeros(8)
+    p = buf.data_ptr() + 1
+    assert _lib.vif_score(ctx._ctx, p, p, out) == _lib.VIF_EINVAL
+    ctx.close()

@@ -1,0 +1,137 @@
+"""MI355X-native float VIF (visual information fidelity) feature.
+
+``Vif(w, h, bpc)`` wraps one scoring context of the C-ABI library
+(include/vif.h).  Frames are device buffers (torch tensors on a ROCm
+device, or raw device pointers); every step of the feature runs in the
+library's HIP kernels for gfx950, and torch only supplies memory and
+streams.  There is no CPU fallback: if the library is not built, using
+``Vif`` raises.
+
+The synthetic workload generators live in ``vif_image_fidelity_amd.synth``
+and need neither the library nor a GPU.
+"""
+import numpy as np
+
+from . import _lib
+from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
+                   KERNEL_KINDS)
+
+__all__ = ["Vif", "VifError", "taps", "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM",
+           "VIF_EHIP", "KERNEL_KINDS"]
+
+
+def taps(scale):
+    """Host Gaussian taps of scale 0..3 as the library computes them."""
+    buf = np.zeros(_lib.MAX_TAPS, dtype=np.float32)
+    n = _lib.vif_taps(scale, buf)
+    if n < 0:
+        raise VifError(n, "vif_taps")
+    return buf[:n].copy()
+
+
+def _ptr(x):
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("frames must be device tensors")
+        if not x.is_contiguous():
+            raise ValueError("frames must be contiguous")
+        return x.data_ptr()
+    raise TypeError("expected a device tensor or a device pointer")
+
+
+class Vif:
+    """One scoring context for w x h frames of bpc bits (8, 10, 12, 16)."""
+
+    def __init__(self, w, h, bpc, stream=None):
+        self.w, self.h, self.bpc = int(w), int(h), int(bpc)
+        ctx = _lib.vif_create(self.w, self.h, self.bpc)
+        if not ctx:
+            raise VifError(_lib.vif_errno(), "vif_create")
+        self._ctx = ctx
+        self.total_rows = sum((self.h >> s) for s in range(4))
+        if stream is not None:
+            self.set_stream(stream)
+
+    def set_stream(self, stream):
+        """stream: a torch.cuda.Stream, a raw hipStream_t (int) or None."""
+        ptr = getattr(stream, "cuda_stream", stream)
+        rc = _lib.vif_set_stream(self._ctx, ptr)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_set_stream")
+
+    def _check_frame(self, t):
+        if hasattr(t, "shape"):
+            if tuple(t.shape) != (self.h, self.w):
+                raise ValueError("frame shape %s, context is (%d, %d)"
+                                 % (tuple(t.shape), self.h, self.w))
+            want = 1 if self.bpc == 8 else 2
+            if t.element_size() != want:
+                raise ValueError("bpc %d needs %d-byte samples"
+                                 % (self.bpc, want))
+
+    def score(self, ref, dist):
+        """Score one pair; returns float64[8]: vif_scale0..3, num, den,
+        num/den, 0."""
+        self._check_frame(ref)
+        self._check_frame(dist)
+        out = np.zeros(8, dtype=np.float64)
+        rc = _lib.vif_score(self._ctx, _ptr(ref), _ptr(dist), out)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_score")
+        return out
+
+    def sums(self):
+        s = np.zeros(8, dtype=np.float32)
+        rc = _lib.vif_get_sums(self._ctx, s)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_get_sums")
+        return s
+
+    def row_sums(self):
+        rows = np.zeros((self.total_rows, 2), dtype=np.float32)
+        rc = _lib.vif_get_row_sums(self._ctx, rows, self.total_rows)
+        if rc < 0:
+            raise VifError(rc, "vif_get_row_sums")
+        return rows
+
+    def set_profiling(self, kinds=0xFF):
+        """Time the kernel kinds in the bit mask (0xFF all, 0 off); a list of
+        kind names is accepted too."""
+        if isinstance(kinds, (list, tuple)):
+            kinds = sum(1 << KERNEL_KINDS.index(k) for k in kinds)
+        elif kinds is True:
+            kinds = 0xFF
+        elif kinds is False or kinds is None:
+            kinds = 0
+        rc = _lib.vif_set_profiling(self._ctx, int(kinds))
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_set_profiling")
+
+    def kernel_times(self):
+        """{kind: (total_ms, launches)} since profiling was enabled."""
+        ms = np.zeros(8, dtype=np.float64)
+        n = np.zeros(8, dtype=np.int64)
+        rc = _lib.vif_get_kernel_times(self._ctx, ms, n, 8)
+        if rc < 0:
+            raise VifError(rc, "vif_get_kernel_times")
+        return {k: (float(ms[i]), int(n[i]))
+                for i, k in enumerate(KERNEL_KINDS)}
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            _lib.vif_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

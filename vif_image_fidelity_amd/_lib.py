@@ -1,0 +1,140 @@
+"""ctypes binding of libvif_amd.so (include/vif.h, include/vif_selftest.h).
+
+Argument marshalling only: every step of the feature runs in the library's
+HIP kernels.  The functions keep the C names.  Loading fails loudly when the
+library has not been built; there is no CPU fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvif_amd.so")
+
+VIF_OK = 0
+VIF_EINVAL = -1
+VIF_ENOMEM = -2
+VIF_EHIP = -3
+NSCALES = 4
+MAX_TAPS = 17
+KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3",
+                "rowsum0", "rowsum1", "rowsum2", "rowsum3")
+
+_lib = None
+
+
+class VifError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (what, vif_strerror(code),
+                                                      code))
+
+
+def load():
+    """Load the built library (once); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libvif_amd.so is not built (%s); run "
+            "`python -m vif_image_fidelity_amd.build` first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ip, fp = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_long)
+    sig = {
+        "vif_create": ([ip, ip, ip], vp),
+        "vif_score": ([vp, vp, vp, dp], ip),
+        "vif_destroy": ([vp], None),
+        "vif_set_stream": ([vp, vp], ip),
+        "vif_get_sums": ([vp, fp], ip),
+        "vif_get_row_sums": ([vp, fp, ip], ip),
+        "vif_taps": ([ip, fp], ip),
+        "vif_set_profiling": ([vp, ip], ip),
+        "vif_get_kernel_times": ([vp, dp, lp, ip], ip),
+        "vif_errno": ([], ip),
+        "vif_strerror": ([ip], ctypes.c_char_p),
+        "vif_selftest_fp64": ([vp, vp, ctypes.c_double, ctypes.c_long, vp, vp,
+                               vp, vp, vp], ip),
+        "vif_selftest_div32": ([vp, vp, ctypes.c_long, vp, vp], ip),
+        "vif_selftest_log2": ([vp, ctypes.c_long, vp, vp], ip),
+        "vif_selftest_ratios": ([vp, vp, ctypes.c_long, vp, vp, vp], ip),
+        "vif_selftest_statistic": ([vp, vp, vp, vp, vp, ctypes.c_long, vp, vp,
+                                    vp], ip),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    """Names of every C function this binding declares."""
+    return ["vif_create", "vif_score", "vif_destroy", "vif_set_stream",
+            "vif_get_sums", "vif_get_row_sums", "vif_taps",
+            "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
+            "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
+            "vif_selftest_log2", "vif_selftest_ratios",
+            "vif_selftest_statistic"]
+
+
+# ------------------------------------------------------- C-named wrappers
+
+def vif_create(w, h, bpc):
+    return load().vif_create(int(w), int(h), int(bpc))
+
+
+def vif_score(ctx, ref_ptr, dist_ptr, out):
+    """out: a ctypes double[8] or a contiguous float64 numpy array."""
+    return load().vif_score(ctx, ref_ptr, dist_ptr, _dptr(out))
+
+
+def vif_destroy(ctx):
+    load().vif_destroy(ctx)
+
+
+def vif_set_stream(ctx, stream_ptr):
+    return load().vif_set_stream(ctx, stream_ptr)
+
+
+def vif_get_sums(ctx, sums):
+    return load().vif_get_sums(ctx, _fptr(sums))
+
+
+def vif_get_row_sums(ctx, rows, capacity):
+    return load().vif_get_row_sums(ctx, _fptr(rows), int(capacity))
+
+
+def vif_taps(scale, taps):
+    return load().vif_taps(int(scale), _fptr(taps))
+
+
+def vif_set_profiling(ctx, enable):
+    return load().vif_set_profiling(ctx, int(enable))
+
+
+def vif_get_kernel_times(ctx, ms, launches, capacity):
+    return load().vif_get_kernel_times(
+        ctx, _dptr(ms), ctypes.cast(launches.ctypes.data,
+                                    ctypes.POINTER(ctypes.c_long)),
+        int(capacity))
+
+
+def vif_errno():
+    return load().vif_errno()
+
+
+def vif_strerror(code):
+    return load().vif_strerror(int(code)).decode()
+
+
+def _fptr(a):
+    return ctypes.cast(a.ctypes.data, ctypes.POINTER(ctypes.c_float))
+
+
+def _dptr(a):
+    if isinstance(a, ctypes.Array):
+        return a
+    return ctypes.cast(a.ctypes.data, ctypes.POINTER(ctypes.c_double))

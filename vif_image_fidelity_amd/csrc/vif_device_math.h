@@ -1,0 +1,121 @@
+// vif_device_math.h -- per-pixel arithmetic of the float VIF kernels (gfx950).
+//
+// Every function here is plain fp32/fp64 code whose roundings are fixed by
+// the build: -ffp-contract=off (no fused multiply-add), correctly rounded
+// fp32 division, IEEE denormals, no fast-math (ADR-1444 "float_vif_hip runs
+// the arithmetic of the CUDA twin ...", Context: HIP spells each rounding
+// step as a plain operator under those flags).  Each operation below is one
+// IEEE rounding, in the order written.  The scoring kernels and the
+// self-test kernels include this header, so the gates test the very code
+// the pipeline runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vifk {
+
+// Noise variance of the statistic, kept in binary64 (ADR-1422
+// "float_vif_sycl computes the CPU's arithmetic ...", Context).
+constexpr double kNoiseVar = 2.0;
+
+// Floor of the variance terms: the fp32 value nearest 1e-10.
+constexpr float kEps = 1e-10f;
+
+// Mirror an index into [0, n): reflect about the edge sample once, then
+// clamp.  Every index an output consumes lies within one reflection of the
+// plane, so the clamp only moves loads that no output uses (ADR-1444,
+// Decision: reflected tile indices pass through a clamp so a frame under
+// 72 px never reads outside its plane).
+__device__ __forceinline__ int mirror_clamp(int i, int n) {
+  int m = i < 0 ? -i : i;
+  m = m > n - 1 ? 2 * (n - 1) - m : m;
+  m = m < 0 ? 0 : m;
+  return m > n - 1 ? n - 1 : m;
+}
+
+// log2 polynomial (ADR-1422, Context: the CPU evaluates log2 with a
+// polynomial in fp32, not a library log2).  This method's coefficients:
+// Chebyshev interpolation of log2(1+t)/t on [0,1], degree 9, rounded to
+// fp32; c1 first.  x = 2^e * (1 + t); returns (float)e + t * P(t), Horner
+// from the highest coefficient.  Valid for finite x >= 1.
+__device__ __forceinline__ float bits_f32(uint32_t u) {
+  return __builtin_bit_cast(float, u);
+}
+
+__device__ __forceinline__ float log2_poly(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const int e = static_cast<int>((u >> 23) & 0xffu) - 127;
+  const float m = bits_f32((u & 0x007fffffu) | 0x3f800000u);
+  const float t = m - 1.0f;
+  float p = bits_f32(0xbb96254au);   // c10
+  p = p * t + bits_f32(0x3ce6f6e9u); // c9
+  p = p * t + bits_f32(0xbda6904fu); // c8
+  p = p * t + bits_f32(0x3e1bc356u); // c7
+  p = p * t + bits_f32(0xbe6194f1u); // c6
+  p = p * t + bits_f32(0x3e913ea6u); // c5
+  p = p * t + bits_f32(0xbeb84ebdu); // c4
+  p = p * t + bits_f32(0x3ef63175u); // c3
+  p = p * t + bits_f32(0xbf38aa21u); // c2
+  p = p * t + bits_f32(0x3fb8aa3bu); // c1
+  const float q = p * t;
+  return static_cast<float>(e) + q;
+}
+
+// fl32(1 + a / (sv + nsq)) with the sum, quotient and sum with one in fp64
+// and a single conversion to fp32 at the end (ADR-1422, Context and
+// Decision).
+__device__ __forceinline__ float num_ratio(float a, float sv) {
+  const double d = static_cast<double>(sv) + kNoiseVar;
+  const double q = static_cast<double>(a) / d;
+  return static_cast<float>(1.0 + q);
+}
+
+// fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.
+__device__ __forceinline__ float den_ratio(float s1) {
+  const double q = static_cast<double>(s1) / kNoiseVar;
+  return static_cast<float>(1.0 + q);
+}
+
+// Per-pixel statistic from the five filtered values.
+//   sigma1_sq = xx - mu1*mu1, sigma2_sq = yy - mu2*mu2 (each clamped at 0),
+//   sigma12 = xy - mu1*mu2.  Below the noise variance (compared in fp64,
+//   ADR-1422, Decision) both terms are 1.  Above it: g = sigma12 /
+//   sigma1_sq, sv_sq = sigma2_sq - g * sigma12; sigma2_sq < eps sets g and
+//   sv_sq to 0; g < 0 sets sv_sq = sigma2_sq and g = 0; sv_sq is floored at
+//   eps; then the two ratios and their log2.
+__device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
+                                            float yy, float xy, float &num,
+                                            float &den) {
+  const float m11 = mu1 * mu1;
+  const float m22 = mu2 * mu2;
+  const float m12 = mu1 * mu2;
+  float s1 = xx - m11;
+  float s2 = yy - m22;
+  const float s12 = xy - m12;
+  s1 = s1 < 0.0f ? 0.0f : s1;
+  s2 = s2 < 0.0f ? 0.0f : s2;
+  if (static_cast<double>(s1) < kNoiseVar) {
+    num = 1.0f;
+    den = 1.0f;
+    return;
+  }
+  float g = s12 / s1;
+  const float gs = g * s12;
+  float sv = s2 - gs;
+  if (s2 < kEps) {
+    g = 0.0f;
+    sv = 0.0f;
+  }
+  if (g < 0.0f) {
+    sv = s2;
+    g = 0.0f;
+  }
+  sv = sv < kEps ? kEps : sv;
+  const float gg = g * g;
+  const float a = gg * s1;
+  num = log2_poly(num_ratio(a, sv));
+  den = log2_poly(den_ratio(s1));
+}
+
+}  // namespace vifk

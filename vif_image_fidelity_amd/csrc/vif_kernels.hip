@@ -1,0 +1,347 @@
+// vif_kernels.hip -- HIP kernels of the float VIF feature for gfx950.
+//
+// Per scale s one kernel does, for a 112 x 16 tile of output pixels:
+//   1. stage the tile's input (+ halo of the filter radius) into LDS as fp32,
+//      normalising native samples on the way (Research-2130 "float_ssim
+//      decimation on the SYCL device", Sources: 8-bit as is, 10/12/16-bit
+//      divided by 4/16/256) and mirroring out-of-plane indices by one
+//      reflection and a clamp (ADR-1444 "float_vif_hip runs the arithmetic
+//      of the CUDA twin ...", Decision);
+//   2. the vertical pass of the separable Gaussian for the five quantities
+//      x, y, x*x, y*y, x*y, one thread per column and 8 rows in registers,
+//      and the vertical pass of the next scale's low-pass at even rows;
+//   3. the horizontal pass (7 outputs per thread), the per-pixel statistic
+//      and the two terms, written to a row-strip-blocked term buffer;
+//   4. the horizontal pass of the next scale's low-pass at even columns,
+//      written as the next scale's fp32 planes (2x decimation).
+// A second kernel adds each row's terms left to right in one fp32
+// accumulator (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...",
+// Context and Decision: one fp32 sum per row, no group or atomic
+// reduction).
+//
+// Every multiply and add is its own IEEE fp32 rounding (the library is
+// built with -ffp-contract=off), taps in ascending order, vertical pass
+// before horizontal.  A filter accumulator starts at its first product
+// instead of 0.0f + product: every filter input is >= +0 (samples, their
+// products and their low-passes), so the product is never -0 and the two
+// are the same value.
+#include <hip/hip_runtime.h>
+
+#include "vif_device_math.h"
+#include "vif_internal.h"
+
+namespace vifk {
+
+constexpr int kThreads = 256;
+
+template <typename InT>
+__device__ __forceinline__ float load_sample(const InT *__restrict__ p,
+                                             size_t i, float scale);
+
+template <>
+__device__ __forceinline__ float load_sample<uint8_t>(
+    const uint8_t *__restrict__ p, size_t i, float) {
+  return static_cast<float>(p[i]);
+}
+
+template <>
+__device__ __forceinline__ float load_sample<uint16_t>(
+    const uint16_t *__restrict__ p, size_t i, float scale) {
+  // scale is an exact power of two (1/4, 1/16, 1/256): the product is exact
+  return static_cast<float>(p[i]) * scale;
+}
+
+template <>
+__device__ __forceinline__ float load_sample<float>(
+    const float *__restrict__ p, size_t i, float) {
+  return p[i];
+}
+
+// R: filter radius of this scale (taps 2R+1).  RD: radius of the next
+// scale's low-pass (0 at the last scale: no decimation).
+template <int R, int RD, typename InT>
+__global__ __launch_bounds__(kThreads) void scale_kernel(
+    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
+    float in_scale, TapArgs taps, TapArgs dtaps, float *__restrict__ terms,
+    float *__restrict__ next_ref, float *__restrict__ next_dist) {
+  constexpr int N = 2 * R + 1;
+  constexpr int ND = 2 * RD + 1;
+  constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
+  constexpr int IR = kTileH + 2 * R; // input rows
+  constexpr int CWP = CW + 1;        // odd pitch: conflict-free row reads
+  constexpr int VB = 8;              // rows per thread in the vertical pass
+  constexpr int HB = 7;              // outputs per thread, horizontal pass
+  constexpr int kIn = 2 * IR * CW;
+  constexpr int kVd = RD > 0 ? 2 * (kTileH / 2) * CWP : 0;
+  constexpr int kV = 5 * kTileH * CWP + kVd;
+  constexpr int kLds = kIn > kV ? kIn : kV;
+  static_assert(CW <= 128, "one thread per vertical column in two halves");
+  static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
+  static_assert(kTileH == 2 * VB, "two row blocks");
+  __shared__ float lds[kLds];
+
+  const int tid = threadIdx.x;
+  const int x0 = blockIdx.x * kTileW;
+  const int y0 = blockIdx.y * kTileH;
+
+  // 1. input tile [IR][CW] for ref then dist
+  {
+    const int c = tid & 127;
+    const int half = tid >> 7;
+    if (c < CW) {
+      const int gx = mirror_clamp(x0 - R + c, w);
+      for (int j = half; j < IR; j += 2) {
+        const int gy = mirror_clamp(y0 - R + j, h);
+        const size_t off = static_cast<size_t>(gy) * w + gx;
+        lds[j * CW + c] = load_sample<InT>(ref, off, in_scale);
+        lds[IR * CW + j * CW + c] = load_sample<InT>(dist, off, in_scale);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. vertical passes: thread (vc, vb) owns column vc, tile rows
+  //    vb*8 .. vb*8+7; the next scale's low-pass at tile rows vb*8 + 2m.
+  const int vc = tid & 127;
+  const int vb = tid >> 7;
+  const bool vact = vc < CW;
+  float acc[5][VB];
+  float dacc[2][VB / 2];
+  if (vact) {
+    const float *sx = lds + (vb * VB) * CW + vc;
+    const float *sy = sx + IR * CW;
+#pragma unroll
+    for (int j = 0; j < VB + 2 * R; ++j) {
+      const float x = sx[j * CW];
+      const float y = sy[j * CW];
+      const float xx = x * x;
+      const float yy = y * y;
+      const float xy = x * y;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        const int k = j - i;
+        if (k >= 0 && k < N) {
+          const float t = taps.t[k];
+          if (k == 0) {
+            acc[0][i] = t * x;
+            acc[1][i] = t * y;
+            acc[2][i] = t * xx;
+            acc[3][i] = t * yy;
+            acc[4][i] = t * xy;
+          } else {
+            acc[0][i] = acc[0][i] + t * x;
+            acc[1][i] = acc[1][i] + t * y;
+            acc[2][i] = acc[2][i] + t * xx;
+            acc[3][i] = acc[3][i] + t * yy;
+            acc[4][i] = acc[4][i] + t * xy;
+          }
+        }
+      }
+      if constexpr (RD > 0) {
+#pragma unroll
+        for (int m = 0; m < VB / 2; ++m) {
+          const int k = j - 2 * m - R + RD;
+          if (k >= 0 && k < ND) {
+            const float t = dtaps.t[k];
+            if (k == 0) {
+              dacc[0][m] = t * x;
+              dacc[1][m] = t * y;
+            } else {
+              dacc[0][m] = dacc[0][m] + t * x;
+              dacc[1][m] = dacc[1][m] + t * y;
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads(); // the input tile is dead from here on
+
+  // 3. vertical results to LDS: V[q][16][CWP], Vd[p][8][CWP]
+  float *sV = lds;
+  float *sVd = lds + 5 * kTileH * CWP;
+  if (vact) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        sV[(q * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
+    if constexpr (RD > 0) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int m = 0; m < VB / 2; ++m)
+          sVd[(p * (kTileH / 2) + vb * (VB / 2) + m) * CWP + vc] = dacc[p][m];
+    }
+  }
+  __syncthreads();
+
+  // 4. horizontal pass, statistic and terms: thread (ty, seg) owns tile row
+  //    ty and columns seg*7 .. seg*7+6.
+  {
+    const int ty = tid & 15;
+    const int seg = tid >> 4;
+    float f[5][HB];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const float *row = sV + (q * kTileH + ty) * CWP + seg * HB;
+      float v[HB + 2 * R];
+#pragma unroll
+      for (int j = 0; j < HB + 2 * R; ++j)
+        v[j] = row[j];
+#pragma unroll
+      for (int i = 0; i < HB; ++i) {
+        float a = taps.t[0] * v[i];
+#pragma unroll
+        for (int k = 1; k < N; ++k)
+          a = a + taps.t[k] * v[i + k];
+        f[q][i] = a;
+      }
+    }
+    const int y = y0 + ty;
+    if (y < h) {
+      // term layout: [strip][x][row in strip][num, den]
+      float *tstrip = terms + static_cast<size_t>(blockIdx.y) * w * 32 + ty * 2;
+#pragma unroll
+      for (int i = 0; i < HB; ++i) {
+        const int x = x0 + seg * HB + i;
+        if (x < w) {
+          float num, den;
+          pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], num, den);
+          *reinterpret_cast<float2 *>(tstrip + static_cast<size_t>(x) * 32) =
+              make_float2(num, den);
+        }
+      }
+    }
+  }
+
+  // 5. next scale's planes: horizontal low-pass at even columns of the even
+  //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1.
+  if constexpr (RD > 0) {
+    const int yd = tid & 7;
+    const int sd = tid >> 3;
+    const int wd = w >> 1;
+    const int hd = h >> 1;
+    const int ydg = (y0 >> 1) + yd;
+    if (sd < kTileW / 4 && ydg < hd) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int xl = sd * 2 + o;
+        const int xdg = (x0 >> 1) + xl;
+        if (xdg < wd) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float *row =
+                sVd + (p * (kTileH / 2) + yd) * CWP + 2 * xl + R - RD;
+            float a = dtaps.t[0] * row[0];
+#pragma unroll
+            for (int k = 1; k < ND; ++k)
+              a = a + dtaps.t[k] * row[k];
+            float *dst = p == 0 ? next_ref : next_dist;
+            dst[static_cast<size_t>(ydg) * wd + xdg] = a;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Ordered row sums of one scale.  One block per 16-row strip.  Waves 1..3
+// stream the strip's terms into LDS, chunk by chunk (double-buffered); lane
+// l < 32 of wave 0 owns row l/2, component l%2 (num or den) and adds the
+// chunk's terms to its single fp32 accumulator in ascending x.
+constexpr int kRowChunk = 128; // columns per chunk (16 KiB)
+
+__global__ __launch_bounds__(kThreads) void rowsum_kernel(
+    const float *__restrict__ terms, int w, int h, float *__restrict__ rows) {
+  __shared__ float4 buf[2][kRowChunk * 8];
+  const int tid = threadIdx.x;
+  const int strip = blockIdx.x;
+  const float4 *src = reinterpret_cast<const float4 *>(
+      terms + static_cast<size_t>(strip) * w * 32);
+  const int nchunks = (w + kRowChunk - 1) / kRowChunk;
+
+  auto load_chunk = [&](int c) {
+    const int ncols = min(kRowChunk, w - c * kRowChunk);
+    const float4 *s = src + static_cast<size_t>(c) * kRowChunk * 8;
+    float4 *d = buf[c & 1];
+    for (int i = tid - 64; i < ncols * 8; i += kThreads - 64)
+      d[i] = s[i];
+  };
+
+  if (tid >= 64)
+    load_chunk(0);
+  __syncthreads();
+  float acc = 0.0f;
+  for (int c = 0; c < nchunks; ++c) {
+    if (tid >= 64) {
+      if (c + 1 < nchunks)
+        load_chunk(c + 1);
+    } else if (tid < 32) {
+      const int ncols = min(kRowChunk, w - c * kRowChunk);
+      const float *b = reinterpret_cast<const float *>(buf[c & 1]) + tid;
+      for (int x = 0; x < ncols; ++x)
+        acc = acc + b[x * 32];
+    }
+    __syncthreads();
+  }
+  if (tid < 32) {
+    const int y = strip * kTileH + (tid >> 1);
+    if (y < h)
+      rows[y * 2 + (tid & 1)] = acc;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+hipError_t launch_scale(int scale, int bpc, const void *in_ref,
+                        const void *in_dist, const ScaleGeom &g,
+                        const TapArgs &taps, const TapArgs &next_taps,
+                        float *terms, float *next_ref, float *next_dist,
+                        hipStream_t stream) {
+  const dim3 grid((g.w + kTileW - 1) / kTileW, g.strips);
+  const dim3 block(kThreads);
+  switch (scale) {
+  case 0:
+    if (bpc == 8) {
+      scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
+          static_cast<const uint8_t *>(in_ref),
+          static_cast<const uint8_t *>(in_dist), g.w, g.h, 1.0f, taps,
+          next_taps, terms, next_ref, next_dist);
+    } else {
+      const float sc = bpc == 10 ? 0.25f : bpc == 12 ? 0.0625f : 0.00390625f;
+      scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
+          static_cast<const uint16_t *>(in_ref),
+          static_cast<const uint16_t *>(in_dist), g.w, g.h, sc, taps,
+          next_taps, terms, next_ref, next_dist);
+    }
+    break;
+  case 1:
+    scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
+        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
+        g.w, g.h, 1.0f, taps, next_taps, terms, next_ref, next_dist);
+    break;
+  case 2:
+    scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
+        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
+        g.w, g.h, 1.0f, taps, next_taps, terms, next_ref, next_dist);
+    break;
+  case 3:
+    scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
+        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
+        g.w, g.h, 1.0f, taps, next_taps, terms, nullptr, nullptr);
+    break;
+  default:
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rowsum(const float *terms, const ScaleGeom &g, float *rows,
+                         hipStream_t stream) {
+  rowsum_kernel<<<dim3(g.strips), dim3(kThreads), 0, stream>>>(terms, g.w, g.h,
+                                                               rows);
+  return hipGetLastError();
+}
+
+} // namespace vifk

@@ -1,0 +1,156 @@
+// vif_selftest.hip -- device-math gates: run the scoring kernels' own device
+// functions (vif_device_math.h) over caller arrays so tests can compare the
+// device's roundings with the host's bit for bit (ADR-1444 "float_vif_hip
+// runs the arithmetic of the CUDA twin ...", Decision and Consequences).
+#include <hip/hip_runtime.h>
+
+#include "../../include/vif_selftest.h"
+#include "vif_device_math.h"
+#include "vif_status.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ void fp64_gate_kernel(const float *__restrict__ a,
+                                 const float *__restrict__ b, double nsq,
+                                 long n, double *__restrict__ sum,
+                                 double *__restrict__ quot,
+                                 float *__restrict__ rnum,
+                                 float *__restrict__ rden) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= n)
+    return;
+  const double s = static_cast<double>(b[i]) + nsq;
+  const double q = static_cast<double>(a[i]) / s;
+  sum[i] = s;
+  quot[i] = q;
+  rnum[i] = static_cast<float>(1.0 + q);
+  rden[i] = static_cast<float>(1.0 + static_cast<double>(a[i]) / nsq);
+}
+
+__global__ void div32_kernel(const float *__restrict__ a,
+                             const float *__restrict__ b, long n,
+                             float *__restrict__ q) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n)
+    q[i] = a[i] / b[i];
+}
+
+__global__ void log2_kernel(const float *__restrict__ x, long n,
+                            float *__restrict__ y) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n)
+    y[i] = vifk::log2_poly(x[i]);
+}
+
+__global__ void ratios_kernel(const float *__restrict__ a,
+                              const float *__restrict__ sv, long n,
+                              float *__restrict__ num,
+                              float *__restrict__ den) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n) {
+    num[i] = vifk::num_ratio(a[i], sv[i]);
+    den[i] = vifk::den_ratio(a[i]);
+  }
+}
+
+__global__ void statistic_kernel(const float *__restrict__ mu1,
+                                 const float *__restrict__ mu2,
+                                 const float *__restrict__ xx,
+                                 const float *__restrict__ yy,
+                                 const float *__restrict__ xy, long n,
+                                 float *__restrict__ num,
+                                 float *__restrict__ den) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n) {
+    float a, b;
+    vifk::pixel_terms(mu1[i], mu2[i], xx[i], yy[i], xy[i], a, b);
+    num[i] = a;
+    den[i] = b;
+  }
+}
+
+dim3 grid_for(long n) {
+  return dim3(static_cast<unsigned>((n + kBlock - 1) / kBlock));
+}
+
+int finish(hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess)
+    e = hipStreamSynchronize(s);
+  return vifk::status_from_hip(e);
+}
+
+// grid.x is limited to 2^31-1 blocks; n up to 2^38 stays well inside.
+bool bad_n(long n) { return n < 0 || n > (1L << 36); }
+
+} // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int
+vif_selftest_fp64(const float *a, const float *b, double nsq, long n,
+                  double *sum, double *quot, float *rnum, float *rden,
+                  void *stream) {
+  if (bad_n(n) || (n > 0 && (!a || !b || !sum || !quot || !rnum || !rden)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fp64_gate_kernel<<<grid_for(n), kBlock, 0, s>>>(a, b, nsq, n, sum, quot,
+                                                  rnum, rden);
+  return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_div32(const float *a, const float *b, long n, float *q,
+                   void *stream) {
+  if (bad_n(n) || (n > 0 && (!a || !b || !q)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  div32_kernel<<<grid_for(n), kBlock, 0, s>>>(a, b, n, q);
+  return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_log2(const float *x, long n, float *y, void *stream) {
+  if (bad_n(n) || (n > 0 && (!x || !y)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  log2_kernel<<<grid_for(n), kBlock, 0, s>>>(x, n, y);
+  return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_ratios(const float *a, const float *sv, long n, float *num,
+                    float *den, void *stream) {
+  if (bad_n(n) || (n > 0 && (!a || !sv || !num || !den)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ratios_kernel<<<grid_for(n), kBlock, 0, s>>>(a, sv, n, num, den);
+  return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_statistic(const float *mu1, const float *mu2, const float *xx,
+                       const float *yy, const float *xy, long n, float *num,
+                       float *den, void *stream) {
+  if (bad_n(n) ||
+      (n > 0 && (!mu1 || !mu2 || !xx || !yy || !xy || !num || !den)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  statistic_kernel<<<grid_for(n), kBlock, 0, s>>>(mu1, mu2, xx, yy, xy, n,
+                                                  num, den);
+  return finish(s);
+}
+
+} // extern "C"

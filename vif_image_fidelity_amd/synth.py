@@ -150,7 +150,8 @@ def pink_4k_frame(index, h=2160, w=3840):
     small = ref.reshape(h // 2, 2, w // 2, 2).mean(axis=(1, 3))
     up = _bilinear_up2(small, h, w)
     dist = np.clip(np.rint(up), 0, 255)
-    return ref.astype(np.uint8), dist.astype(np.uint8), 8
+    return (np.ascontiguousarray(ref, dtype=np.uint8),
+            np.ascontiguousarray(dist, dtype=np.uint8), 8)
 
 
 def pink_4k_8bit(frames=20, first=0, h=2160, w=3840):
