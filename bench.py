@@ -3,9 +3,12 @@
   python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step scores one 3840x2160 8-bit luma frame pair (the whole path: four
-scales of filtering, statistic, decimation and row sums, one read-back and
-the host sums).  The 20 synthetic 1/f-noise frame pairs are resident in HBM
-before the timed region; steps cycle through them.  Prints one JSON line.
+scales of filtering, statistic, decimation and ordered row sums, one
+read-back and the host sums).  The 20 synthetic 1/f-noise frame pairs are
+resident in HBM before the timed region; steps cycle through them and go
+through the context's asynchronous queue (submit / collect, up to three
+frames in flight), so consecutive frames overlap their read-back and host
+work with the next frame's kernels.  Prints one JSON line.
 
 The line carries, besides the contract fields:
   roofline      the dominant kernel (the scale-0 filter/statistic kernel):
@@ -94,20 +97,46 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
 
     pairs = [(td(r), td(d)) for (r, d, _) in frames]
     ctx = V.Vif(w, h, bpc)
-    for i in range(warmup):
-        r, d = pairs[i % len(pairs)]
-        ctx.score(r, d)
+
+    def run(n):
+        # keep the context's queue full: frame i+depth is submitted as soon
+        # as frame i has been collected
+        for i in range(n):
+            if ctx.pending() == V.QUEUE_DEPTH:
+                ctx.collect()
+            r, d = pairs[i % len(pairs)]
+            ctx.submit(r, d)
+        while ctx.pending():
+            ctx.collect()
+
+    run(warmup)
     ctx.set_profiling(prof_kinds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        r, d = pairs[i % len(pairs)]
-        ctx.score(r, d)
+    run(steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = ctx.kernel_times()
     ctx.close()
     return (t1 - t0), kt
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(launches):
+    """A plain device-to-device copy of COPY_BYTES, `launches` times: each
+    launch reads and writes exactly COPY_BYTES, the reference against which
+    the FETCH_SIZE and WRITE_SIZE counters are scaled."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(max(launches, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copied %d x %d bytes" % (max(launches, 1), COPY_BYTES),
+          file=sys.stderr, flush=True)
 
 
 def cpu_baseline(frames, budget_s=12.0):
@@ -132,6 +161,11 @@ def main():
     ap.add_argument("--frames", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-1080p", type=int, default=500)
+    ap.add_argument("--mode", choices=["full", "frames", "copy"],
+                    default="full",
+                    help="full: the JSON line; frames: only the timed 4K "
+                    "loop (for profiler runs); copy: a plain device copy of "
+                    "known size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the feature on "
@@ -143,6 +177,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.mode == "copy":
+        copy_calibration(args.steps)
+        return
     ensure_lib()
     import vif_image_fidelity_amd as V
     from vif_image_fidelity_amd import synth
@@ -160,10 +197,12 @@ def main():
     s0_avg_ms = s0_ms / max(s0_n, 1)
     print("4K: %.1f frames/s, %.3f ms/step; scale-0 kernel %.1f us avg"
           % (fps, ms_step, 1000 * s0_avg_ms), file=sys.stderr, flush=True)
+    if args.mode == "frames":
+        return
 
     # per-kernel split (all kinds timed; separate run, not the headline)
     _, kt_all = time_frames(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
-                            prof_kinds=0xFF)
+                            prof_kinds=0x1F)
     split = {k: round(1000.0 * ms / max(n, 1), 2) for k, (ms, n) in
              kt_all.items()}
 

@@ -74,11 +74,30 @@ vif_ctx *vif_create(int w, int h, int bpc);
  *                out[6]    num / den (the frame's vif ratio)
  *                out[7]    0.0 (reserved)
  *              where N_s, D_s are the fp32 sums of scale s.
- * Synchronous: returns after the results are on the host.  Allocates
- * nothing.  One call in flight per context; a context is not thread-safe,
- * separate contexts are independent.  On error out is left untouched.
+ * Synchronous: returns after the results are on the host (vif_submit then
+ * vif_collect); VIF_EINVAL if frames submitted with vif_submit are still
+ * pending.  Allocates nothing.  A context is not thread-safe; separate
+ * contexts are independent.  On error out is left untouched.
  */
 int vif_score(vif_ctx *ctx, const void *ref, const void *dist, double out[8]);
+
+/*
+ * Asynchronous scoring.  A context keeps up to VIF_QUEUE_DEPTH frames in
+ * flight: vif_submit enqueues one frame pair on the context's stream and
+ * returns at once; vif_collect waits for the oldest submitted frame and
+ * writes its outputs (the same 8 doubles as vif_score), in submission order.
+ * The frames of a submitted pair must stay valid and unchanged until their
+ * vif_collect returns.  vif_submit returns VIF_EINVAL when VIF_QUEUE_DEPTH
+ * frames are already pending (collect first); vif_collect returns VIF_EINVAL
+ * when none is.  Consecutive frames overlap on the device: one frame's
+ * read-back runs while the next frame's kernels compute.
+ */
+#define VIF_QUEUE_DEPTH 3
+int vif_submit(vif_ctx *ctx, const void *ref, const void *dist);
+int vif_collect(vif_ctx *ctx, double out[8]);
+
+/* vif_pending -- frames submitted and not yet collected (or VIF_EINVAL). */
+int vif_pending(const vif_ctx *ctx);
 
 /* vif_destroy -- frees everything the context owns.  NULL is a no-op. */
 void vif_destroy(vif_ctx *ctx);
@@ -91,16 +110,17 @@ void vif_destroy(vif_ctx *ctx);
 int vif_set_stream(vif_ctx *ctx, void *hip_stream);
 
 /*
- * vif_get_sums -- the fp32 per-scale sums of the last successful
- * vif_score: N_0, D_0, N_1, D_1, N_2, D_2, N_3, D_3 (the eight per-scale
- * sums of the pages' debug output, ADR-1422, Consequences).
- * VIF_EINVAL if no frame has been scored yet.
+ * vif_get_sums -- the fp32 per-scale sums of the last frame returned by
+ * vif_score or vif_collect: N_0, D_0, N_1, D_1, N_2, D_2, N_3, D_3 (the
+ * eight per-scale sums of the pages' debug output, ADR-1422, Consequences).
+ * VIF_EINVAL if no frame has been returned yet.
  */
 int vif_get_sums(const vif_ctx *ctx, float sums[8]);
 
 /*
- * vif_get_row_sums -- the per-row fp32 sums of the last successful
- * vif_score, as they came back from the device: for scale 0..3, for row
+ * vif_get_row_sums -- the per-row fp32 sums of the last frame returned by
+ * vif_score or vif_collect, as they came back from the device: for scale
+ * 0..3, for row
  * y = 0..h_s-1, the pair (n_y, d_y).  rows must hold 2 * capacity floats.
  * Returns the total number of rows (h_0 + h_1 + h_2 + h_3) when capacity
  * is large enough, else VIF_EINVAL.  Plane heights halve with floor.
@@ -117,20 +137,22 @@ int vif_taps(int scale, float *taps);
 
 /*
  * vif_set_profiling -- kinds is a bit mask of kernel kinds (bit k = kind k
- * of vif_get_kernel_times; 0xff = all, 0 = off).  vif_score then records a
- * pair of HIP events around each launch of those kinds on the context's
- * stream and accumulates their durations (a small cost per event).  Every
- * call resets the totals.
+ * of vif_get_kernel_times; 0x1f = all, 0 = off).  Frames submitted from
+ * then on record a pair of HIP events around each launch of those kinds on
+ * the stream it runs on, and vif_collect accumulates their durations (a
+ * small cost per event).  Every call resets the totals; VIF_EINVAL while
+ * frames are pending.
  */
 int vif_set_profiling(vif_ctx *ctx, int kinds);
 
 /*
  * vif_get_kernel_times -- accumulated kernel durations in milliseconds and
  * launch counts since profiling was enabled, one entry per kernel kind:
- *   0..3  the per-scale filter/statistic kernel of scale 0..3
- *   4..7  the row-sum kernel of scale 0..3
+ *   0..3  the kernel of scale s (filter, statistic, terms, next scale's
+ *         planes)
+ *   4     the ordered row sums of all four scales (one launch per frame)
  * ms and launches hold at least `capacity` entries (either may be NULL).
- * Returns the number of kinds (8) or VIF_EINVAL.
+ * Returns the number of kinds (5) or VIF_EINVAL.
  */
 int vif_get_kernel_times(const vif_ctx *ctx, double *ms, long *launches,
                          int capacity);

@@ -72,6 +72,9 @@ def test_null_handling(lib):
     assert _lib.vif_set_stream(None, None) == _lib.VIF_EINVAL
     assert _lib.vif_get_sums(None, np.zeros(8, np.float32)) == _lib.VIF_EINVAL
     assert _lib.vif_set_profiling(None, 1) == _lib.VIF_EINVAL
+    assert _lib.vif_submit(None, 1, 1) == _lib.VIF_EINVAL
+    assert _lib.vif_collect(None, out) == _lib.VIF_EINVAL
+    assert _lib.vif_pending(None) == _lib.VIF_EINVAL
     _lib.vif_destroy(None)  # no-op
 
 
@@ -112,7 +115,8 @@ def test_fault_injection_alloc(lib):
 def test_package_import_needs_no_gpu():
     import vif_image_fidelity_amd as V
     assert V.VIF_OK == 0
-    assert len(V.KERNEL_KINDS) == 8
+    assert len(V.KERNEL_KINDS) == 5
+    assert V.QUEUE_DEPTH == 3
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -145,6 +145,33 @@ def test_repeat_is_deterministic_and_stream_aware(V, orc):
     ctx.close()
 
 
+def test_async_queue_matches_oracle(V, orc):
+    """submit/collect with the queue full, frames collected in order."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit(frames=3) * 3
+    exps = [orc.score(r, d, b)[0] for (r, d, b) in frames[:3]]
+    dev = [(to_device(r), to_device(d)) for (r, d, _) in frames]
+    ctx = V.Vif(576, 324, 8)
+    outs = []
+    for i, (r, d) in enumerate(dev):
+        if ctx.pending() == V.QUEUE_DEPTH:
+            outs.append(ctx.collect())
+        ctx.submit(r, d)
+    assert ctx.pending() == V.QUEUE_DEPTH
+    with pytest.raises(V.VifError):
+        ctx.submit(*dev[0])      # the queue is full
+    with pytest.raises(V.VifError):
+        ctx.score(*dev[0])       # frames are pending
+    while ctx.pending():
+        outs.append(ctx.collect())
+    with pytest.raises(V.VifError):
+        ctx.collect()            # nothing pending
+    assert len(outs) == len(frames)
+    for i, o in enumerate(outs):
+        assert o.tobytes() == exps[i % 3].tobytes(), i
+    ctx.close()
+
+
 def test_profiling_counts_launches(V):
     from vif_image_fidelity_amd import synth
     ref, dist, bpc = synth.netflix_576x324_8bit(frames=1)[0]

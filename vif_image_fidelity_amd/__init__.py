@@ -14,10 +14,10 @@ import numpy as np
 
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
-                   KERNEL_KINDS)
+                   KERNEL_KINDS, QUEUE_DEPTH)
 
 __all__ = ["Vif", "VifError", "taps", "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM",
-           "VIF_EHIP", "KERNEL_KINDS"]
+           "VIF_EHIP", "KERNEL_KINDS", "QUEUE_DEPTH"]
 
 
 def taps(scale):
@@ -82,6 +82,26 @@ class Vif:
             raise VifError(rc, "vif_score")
         return out
 
+    def submit(self, ref, dist):
+        """Enqueue one pair (at most QUEUE_DEPTH pending); the frames must
+        stay valid until the matching collect() returns."""
+        self._check_frame(ref)
+        self._check_frame(dist)
+        rc = _lib.vif_submit(self._ctx, _ptr(ref), _ptr(dist))
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_submit")
+
+    def collect(self):
+        """Outputs of the oldest submitted pair (float64[8])."""
+        out = np.zeros(8, dtype=np.float64)
+        rc = _lib.vif_collect(self._ctx, out)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_collect")
+        return out
+
+    def pending(self):
+        return _lib.vif_pending(self._ctx)
+
     def sums(self):
         s = np.zeros(8, dtype=np.float32)
         rc = _lib.vif_get_sums(self._ctx, s)
@@ -96,13 +116,13 @@ class Vif:
             raise VifError(rc, "vif_get_row_sums")
         return rows
 
-    def set_profiling(self, kinds=0xFF):
-        """Time the kernel kinds in the bit mask (0xFF all, 0 off); a list of
-        kind names is accepted too."""
+    def set_profiling(self, kinds=0x1F):
+        """Time the kernel kinds in the bit mask (0x1F all, 0 off); a list
+        of kind names is accepted too."""
         if isinstance(kinds, (list, tuple)):
             kinds = sum(1 << KERNEL_KINDS.index(k) for k in kinds)
         elif kinds is True:
-            kinds = 0xFF
+            kinds = 0x1F
         elif kinds is False or kinds is None:
             kinds = 0
         rc = _lib.vif_set_profiling(self._ctx, int(kinds))
@@ -111,9 +131,10 @@ class Vif:
 
     def kernel_times(self):
         """{kind: (total_ms, launches)} since profiling was enabled."""
-        ms = np.zeros(8, dtype=np.float64)
-        n = np.zeros(8, dtype=np.int64)
-        rc = _lib.vif_get_kernel_times(self._ctx, ms, n, 8)
+        k = len(KERNEL_KINDS)
+        ms = np.zeros(k, dtype=np.float64)
+        n = np.zeros(k, dtype=np.int64)
+        rc = _lib.vif_get_kernel_times(self._ctx, ms, n, k)
         if rc < 0:
             raise VifError(rc, "vif_get_kernel_times")
         return {k: (float(ms[i]), int(n[i]))

@@ -16,8 +16,8 @@ VIF_ENOMEM = -2
 VIF_EHIP = -3
 NSCALES = 4
 MAX_TAPS = 17
-KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3",
-                "rowsum0", "rowsum1", "rowsum2", "rowsum3")
+QUEUE_DEPTH = 3
+KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
 
 _lib = None
 
@@ -45,6 +45,9 @@ def load():
     sig = {
         "vif_create": ([ip, ip, ip], vp),
         "vif_score": ([vp, vp, vp, dp], ip),
+        "vif_submit": ([vp, vp, vp], ip),
+        "vif_collect": ([vp, dp], ip),
+        "vif_pending": ([vp], ip),
         "vif_destroy": ([vp], None),
         "vif_set_stream": ([vp, vp], ip),
         "vif_get_sums": ([vp, fp], ip),
@@ -72,7 +75,9 @@ def load():
 
 def exported_symbols():
     """Names of every C function this binding declares."""
-    return ["vif_create", "vif_score", "vif_destroy", "vif_set_stream",
+    return ["vif_create", "vif_score", "vif_submit", "vif_collect",
+            "vif_pending",
+            "vif_destroy", "vif_set_stream",
             "vif_get_sums", "vif_get_row_sums", "vif_taps",
             "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
@@ -89,6 +94,18 @@ def vif_create(w, h, bpc):
 def vif_score(ctx, ref_ptr, dist_ptr, out):
     """out: a ctypes double[8] or a contiguous float64 numpy array."""
     return load().vif_score(ctx, ref_ptr, dist_ptr, _dptr(out))
+
+
+def vif_submit(ctx, ref_ptr, dist_ptr):
+    return load().vif_submit(ctx, ref_ptr, dist_ptr)
+
+
+def vif_collect(ctx, out):
+    return load().vif_collect(ctx, _dptr(out))
+
+
+def vif_pending(ctx):
+    return load().vif_pending(ctx)
 
 
 def vif_destroy(ctx):

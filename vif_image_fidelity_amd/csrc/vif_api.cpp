@@ -1,13 +1,16 @@
 // vif_api.cpp -- the C ABI of include/vif.h: context, launch sequence, one
-// read-back and the host sums.
+// read-back per frame and the host sums.
 //
-// Per frame, on the context's stream: for s = 0..3 the per-scale kernel
-// (filter, statistic, terms, next scale's planes) and the row-sum kernel of
-// that scale; then one device-to-host copy of every row sum (two floats per
-// row per scale) into pinned memory, and the host adds the rows of each
-// scale top to bottom in fp32 (ADR-1422 "float_vif_sycl computes the CPU's
-// arithmetic ...", Decision).  The scores are fp64 quotients of the fp32
-// sums; num and den add the four scales in order in fp64.
+// Per frame, on the context's stream: the four per-scale kernels (filter,
+// statistic, terms and the next scale's planes), writing the terms into the
+// frame's slot of a small ring.  A second stream then runs the ordered
+// row sums of all scales (one launch) and copies them (two floats per row
+// per scale) to pinned host memory in one copy, while the next frame's
+// kernels already run on the first stream.  vif_collect adds the rows of
+// each scale top to bottom in fp32 on the host (ADR-1422 "float_vif_sycl
+// computes the CPU's arithmetic ...", Decision).  The scores are fp64
+// quotients of the fp32 sums; num and den add the four scales in order in
+// fp64.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdlib>
@@ -20,25 +23,46 @@
 
 using vifk::kScales;
 
+namespace {
+
+constexpr int kDepth = VIF_QUEUE_DEPTH;
+
+constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
+
+struct Slot {
+  float *terms[kScales] = {};        // term buffers of the four scales
+  float *rows_dev = nullptr;         // 2 * total rows
+  float *rows_host = nullptr;        // pinned
+  hipEvent_t kernels_done = nullptr; // on the work stream
+  hipEvent_t copy_done = nullptr;    // on the copy stream
+  hipEvent_t prof[kKinds][2] = {};
+  int prof_mask = 0; // kinds timed for the frame in this slot
+  bool used = false;
+};
+
+} // namespace
+
 struct vif_ctx {
   int w = 0, h = 0, bpc = 0;
   int device = 0;
-  hipStream_t stream = nullptr;
+  hipStream_t stream = nullptr;      // work stream (caller's or default)
+  hipStream_t copy_stream = nullptr; // owned: read-backs
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
-  float *pyr_ref[kScales] = {};  // [0] unused: scale 0 reads the frames
+  float *pyr_ref[kScales] = {}; // [0] unused: scale 0 reads the frames
   float *pyr_dist[kScales] = {};
-  float *terms[kScales] = {};
-  float *rows_dev = nullptr;
-  float *rows_host = nullptr; // pinned
+  Slot slots[kDepth];
   int total_rows = 0;
   int row_base[kScales] = {};
+  int rowsum_waves = 0;
+  vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
+  long head = 0, tail = 0;      // submitted / collected frame counts
   float sums[8] = {};
+  float *last_rows = nullptr; // host copy of the last collected row sums
   bool have_sums = false;
-  int prof_mask = 0; // kernel kinds timed with events
-  hipEvent_t ev[2 * 8] = {};
-  double kernel_ms[8] = {};
-  long kernel_launches[8] = {};
+  int prof_mask = 0;
+  double kernel_ms[kKinds] = {};
+  long kernel_launches[kKinds] = {};
 };
 
 namespace vifk {
@@ -92,28 +116,153 @@ bool fault_injected_alloc() {
   return v != nullptr && std::strcmp(v, "alloc") == 0;
 }
 
+void destroy_event(hipEvent_t &e) {
+  if (e) {
+    (void)hipEventDestroy(e);
+    e = nullptr;
+  }
+}
+
 void free_all(vif_ctx *c) {
   for (int s = 0; s < kScales; ++s) {
     if (c->pyr_ref[s])
       (void)hipFree(c->pyr_ref[s]);
     if (c->pyr_dist[s])
       (void)hipFree(c->pyr_dist[s]);
-    if (c->terms[s])
-      (void)hipFree(c->terms[s]);
   }
-  if (c->rows_dev)
-    (void)hipFree(c->rows_dev);
-  if (c->rows_host)
-    (void)hipHostFree(c->rows_host);
-  for (hipEvent_t &e : c->ev)
-    if (e) {
-      (void)hipEventDestroy(e);
-      e = nullptr;
+  for (Slot &sl : c->slots) {
+    for (float *t : sl.terms)
+      if (t)
+        (void)hipFree(t);
+    if (sl.rows_dev)
+      (void)hipFree(sl.rows_dev);
+    if (sl.rows_host)
+      (void)hipHostFree(sl.rows_host);
+    destroy_event(sl.kernels_done);
+    destroy_event(sl.copy_done);
+    for (auto &p : sl.prof) {
+      destroy_event(p[0]);
+      destroy_event(p[1]);
     }
+  }
+  if (c->copy_stream)
+    (void)hipStreamDestroy(c->copy_stream);
+  std::free(c->last_rows);
 }
 
 template <typename T> hipError_t dev_alloc(T **p, size_t elems) {
   return hipMalloc(reinterpret_cast<void **>(p), elems * sizeof(T));
+}
+
+// Enqueues one frame into the slot at ctx->head.
+int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
+  Slot &sl = ctx->slots[ctx->head % kDepth];
+  hipStream_t st = ctx->stream;
+  hipStream_t cs = ctx->copy_stream;
+  hipError_t e = hipSuccess;
+  // the slot's terms and row sums are free once its last read-back is done
+  if (sl.used)
+    e = hipStreamWaitEvent(st, sl.copy_done, 0);
+  sl.prof_mask = ctx->prof_mask;
+  for (int s = 0; s < kScales && e == hipSuccess; ++s) {
+    const void *in_ref = s == 0 ? ref : ctx->pyr_ref[s];
+    const void *in_dist = s == 0 ? dist : ctx->pyr_dist[s];
+    float *nref = s + 1 < kScales ? ctx->pyr_ref[s + 1] : nullptr;
+    float *ndist = s + 1 < kScales ? ctx->pyr_dist[s + 1] : nullptr;
+    const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
+    const bool timed = (sl.prof_mask >> s) & 1;
+    if (timed)
+      e = hipEventRecord(sl.prof[s][0], st);
+    if (e == hipSuccess)
+      e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
+                             ctx->taps[s], nt, nref, ndist, sl.terms[s], st);
+    if (e == hipSuccess && timed)
+      e = hipEventRecord(sl.prof[s][1], st);
+  }
+  if (e == hipSuccess)
+    e = hipEventRecord(sl.kernels_done, st);
+  if (e == hipSuccess)
+    e = hipStreamWaitEvent(cs, sl.kernels_done, 0);
+  vifk::RowSumArgs ra = ctx->rowsum;
+  for (int s = 0; s < kScales; ++s) {
+    ra.terms[s] = sl.terms[s];
+    ra.rows[s] = sl.rows_dev + 2 * ctx->row_base[s];
+  }
+  const bool timed = (sl.prof_mask >> kScales) & 1;
+  if (e == hipSuccess && timed)
+    e = hipEventRecord(sl.prof[kScales][0], cs);
+  if (e == hipSuccess)
+    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, cs);
+  if (e == hipSuccess && timed)
+    e = hipEventRecord(sl.prof[kScales][1], cs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(sl.rows_host, sl.rows_dev,
+                       sizeof(float) * 2 * ctx->total_rows,
+                       hipMemcpyDeviceToHost, cs);
+  if (e == hipSuccess)
+    e = hipEventRecord(sl.copy_done, cs);
+  if (e != hipSuccess)
+    return vifk::status_from_hip(e);
+  sl.used = true;
+  ctx->head += 1;
+  return vifk::set_status(VIF_OK);
+}
+
+// Waits for the oldest pending frame and writes its outputs.
+int collect_frame(vif_ctx *ctx, double out[8]) {
+  Slot &sl = ctx->slots[ctx->tail % kDepth];
+  hipError_t e = hipEventSynchronize(sl.copy_done);
+  if (e != hipSuccess) {
+    ctx->tail += 1; // the frame is lost; keep the ring consistent
+    return vifk::status_from_hip(e);
+  }
+  for (int k = 0; k < kKinds; ++k) {
+    if (!((sl.prof_mask >> k) & 1))
+      continue;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, sl.prof[k][0], sl.prof[k][1]) ==
+        hipSuccess) {
+      ctx->kernel_ms[k] += ms;
+      ctx->kernel_launches[k] += 1;
+    }
+  }
+  float N[kScales], D[kScales];
+  for (int s = 0; s < kScales; ++s) {
+    const float *r = sl.rows_host + 2 * ctx->row_base[s];
+    float n = 0.0f, d = 0.0f;
+    for (int y = 0; y < ctx->geom[s].h; ++y) {
+      n = n + r[2 * y];
+      d = d + r[2 * y + 1];
+    }
+    N[s] = n;
+    D[s] = d;
+    ctx->sums[2 * s] = n;
+    ctx->sums[2 * s + 1] = d;
+  }
+  std::memcpy(ctx->last_rows, sl.rows_host,
+              sizeof(float) * 2 * ctx->total_rows);
+  ctx->have_sums = true;
+  ctx->tail += 1;
+  for (int s = 0; s < kScales; ++s)
+    out[s] = static_cast<double>(N[s]) / static_cast<double>(D[s]);
+  double num = static_cast<double>(N[0]) + static_cast<double>(N[1]);
+  num = num + static_cast<double>(N[2]);
+  num = num + static_cast<double>(N[3]);
+  double den = static_cast<double>(D[0]) + static_cast<double>(D[1]);
+  den = den + static_cast<double>(D[2]);
+  den = den + static_cast<double>(D[3]);
+  out[4] = num;
+  out[5] = den;
+  out[6] = num / den;
+  out[7] = 0.0;
+  return vifk::set_status(VIF_OK);
+}
+
+bool bad_frame_ptrs(const vif_ctx *ctx, const void *ref, const void *dist) {
+  if (ref == nullptr || dist == nullptr)
+    return true;
+  return ctx->bpc != 8 && ((reinterpret_cast<uintptr_t>(ref) |
+                            reinterpret_cast<uintptr_t>(dist)) & 1u);
 }
 
 } // namespace
@@ -156,28 +305,49 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
     g.w = ws;
     g.h = hs;
     g.strips = (hs + vifk::kTileH - 1) / vifk::kTileH;
-    g.term_elems = static_cast<size_t>(g.strips) * ws * 32;
+    g.ntx = (ws + vifk::kTileW - 1) / vifk::kTileW;
     c->row_base[s] = rows;
     rows += hs;
     vifk::gaussian_taps(s, c->taps[s].t);
+    c->rowsum.w[s] = ws;
+    c->rowsum.h[s] = hs;
+    c->rowsum.strips[s] = g.strips;
+    c->rowsum.pair_base[s + 1] = c->rowsum.pair_base[s] + (g.strips + 1) / 2;
   }
+  c->rowsum_waves = c->rowsum.pair_base[kScales];
   c->total_rows = rows;
+  c->last_rows =
+      static_cast<float *>(std::calloc(static_cast<size_t>(2) * rows, 4));
+  if (c->last_rows == nullptr)
+    e = hipErrorOutOfMemory;
 
-  for (int s = 0; s < kScales && e == hipSuccess; ++s) {
+  for (int s = 1; s < kScales && e == hipSuccess; ++s) {
     const size_t n = static_cast<size_t>(c->geom[s].w) * c->geom[s].h;
-    if (s > 0) {
-      e = dev_alloc(&c->pyr_ref[s], n);
-      if (e == hipSuccess)
-        e = dev_alloc(&c->pyr_dist[s], n);
-    }
+    e = dev_alloc(&c->pyr_ref[s], n);
     if (e == hipSuccess)
-      e = dev_alloc(&c->terms[s], c->geom[s].term_elems);
+      e = dev_alloc(&c->pyr_dist[s], n);
+  }
+  for (Slot &sl : c->slots) {
+    for (int s = 0; s < kScales && e == hipSuccess; ++s)
+      e = dev_alloc(&sl.terms[s], static_cast<size_t>(c->geom[s].strips) *
+                                      vifk::term_groups(c->geom[s].w) *
+                                      vifk::kSeq * 4);
+    if (e == hipSuccess)
+      e = dev_alloc(&sl.rows_dev, static_cast<size_t>(2) * rows);
+    if (e == hipSuccess)
+      e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
+                        sizeof(float) * 2 * rows, hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&sl.kernels_done, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&sl.copy_done, hipEventDisableTiming);
+    for (auto &p : sl.prof)
+      for (hipEvent_t &ev : p)
+        if (e == hipSuccess)
+          e = hipEventCreate(&ev);
   }
   if (e == hipSuccess)
-    e = dev_alloc(&c->rows_dev, static_cast<size_t>(2) * rows);
-  if (e == hipSuccess)
-    e = hipHostMalloc(reinterpret_cast<void **>(&c->rows_host),
-                      sizeof(float) * 2 * rows, hipHostMallocDefault);
+    e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     free_all(c);
     delete c;
@@ -193,6 +363,10 @@ __attribute__((visibility("default"))) void vif_destroy(vif_ctx *ctx) {
     return;
   {
     DeviceScope scope(ctx->device);
+    if (ctx->head != ctx->tail) {
+      (void)hipStreamSynchronize(ctx->stream);
+      (void)hipStreamSynchronize(ctx->copy_stream);
+    }
     free_all(ctx);
   }
   delete ctx;
@@ -200,93 +374,52 @@ __attribute__((visibility("default"))) void vif_destroy(vif_ctx *ctx) {
 
 __attribute__((visibility("default"))) int vif_set_stream(vif_ctx *ctx,
                                                           void *hip_stream) {
-  if (ctx == nullptr)
+  if (ctx == nullptr || ctx->head != ctx->tail)
     return vifk::set_status(VIF_EINVAL);
   ctx->stream = static_cast<hipStream_t>(hip_stream);
   return vifk::set_status(VIF_OK);
 }
 
 __attribute__((visibility("default"))) int
-vif_score(vif_ctx *ctx, const void *ref, const void *dist, double out[8]) {
-  if (ctx == nullptr || ref == nullptr || dist == nullptr || out == nullptr)
-    return vifk::set_status(VIF_EINVAL);
-  if (ctx->bpc != 8 && ((reinterpret_cast<uintptr_t>(ref) |
-                         reinterpret_cast<uintptr_t>(dist)) & 1u))
+vif_submit(vif_ctx *ctx, const void *ref, const void *dist) {
+  if (ctx == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
+      ctx->head - ctx->tail >= kDepth)
     return vifk::set_status(VIF_EINVAL);
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
     return vifk::status_from_hip(scope.error());
-  hipStream_t st = ctx->stream;
-  hipError_t e = hipSuccess;
-  // events ev[2k], ev[2k+1] bracket kernel kind k (0..3 scale kernels,
-  // 4..7 row sums) when bit k of prof_mask is set
-  auto mark = [&](int kind, int edge) {
-    if ((ctx->prof_mask >> kind) & 1 && e == hipSuccess)
-      e = hipEventRecord(ctx->ev[2 * kind + edge], st);
-  };
-  for (int s = 0; s < kScales && e == hipSuccess; ++s) {
-    const void *in_ref = s == 0 ? ref : ctx->pyr_ref[s];
-    const void *in_dist = s == 0 ? dist : ctx->pyr_dist[s];
-    float *nref = s + 1 < kScales ? ctx->pyr_ref[s + 1] : nullptr;
-    float *ndist = s + 1 < kScales ? ctx->pyr_dist[s + 1] : nullptr;
-    const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
-    mark(s, 0);
-    if (e == hipSuccess)
-      e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
-                             ctx->taps[s], nt, ctx->terms[s], nref, ndist, st);
-    mark(s, 1);
-    mark(4 + s, 0);
-    if (e == hipSuccess)
-      e = vifk::launch_rowsum(ctx->terms[s], ctx->geom[s],
-                              ctx->rows_dev + 2 * ctx->row_base[s], st);
-    mark(4 + s, 1);
-  }
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(ctx->rows_host, ctx->rows_dev,
-                       sizeof(float) * 2 * ctx->total_rows,
-                       hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess)
-    e = hipStreamSynchronize(st);
-  if (e != hipSuccess)
-    return vifk::status_from_hip(e);
+  return submit_frame(ctx, ref, dist);
+}
 
-  for (int k = 0; k < 8; ++k) {
-    float ms = 0.0f;
-    if ((ctx->prof_mask >> k) & 1 &&
-        hipEventElapsedTime(&ms, ctx->ev[2 * k], ctx->ev[2 * k + 1]) ==
-            hipSuccess) {
-      ctx->kernel_ms[k] += ms;
-      ctx->kernel_launches[k] += 1;
-    }
-  }
+__attribute__((visibility("default"))) int vif_collect(vif_ctx *ctx,
+                                                       double out[8]) {
+  if (ctx == nullptr || out == nullptr || ctx->head == ctx->tail)
+    return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  return collect_frame(ctx, out);
+}
 
-  float N[kScales], D[kScales];
-  for (int s = 0; s < kScales; ++s) {
-    const float *r = ctx->rows_host + 2 * ctx->row_base[s];
-    float n = 0.0f, d = 0.0f;
-    for (int y = 0; y < ctx->geom[s].h; ++y) {
-      n = n + r[2 * y];
-      d = d + r[2 * y + 1];
-    }
-    N[s] = n;
-    D[s] = d;
-    ctx->sums[2 * s] = n;
-    ctx->sums[2 * s + 1] = d;
-  }
-  ctx->have_sums = true;
-  for (int s = 0; s < kScales; ++s)
-    out[s] = static_cast<double>(N[s]) / static_cast<double>(D[s]);
-  double num = static_cast<double>(N[0]) + static_cast<double>(N[1]);
-  num = num + static_cast<double>(N[2]);
-  num = num + static_cast<double>(N[3]);
-  double den = static_cast<double>(D[0]) + static_cast<double>(D[1]);
-  den = den + static_cast<double>(D[2]);
-  den = den + static_cast<double>(D[3]);
-  out[4] = num;
-  out[5] = den;
-  out[6] = num / den;
-  out[7] = 0.0;
-  return vifk::set_status(VIF_OK);
+__attribute__((visibility("default"))) int vif_pending(const vif_ctx *ctx) {
+  if (ctx == nullptr)
+    return vifk::set_status(VIF_EINVAL);
+  vifk::set_status(VIF_OK);
+  return static_cast<int>(ctx->head - ctx->tail);
+}
+
+__attribute__((visibility("default"))) int
+vif_score(vif_ctx *ctx, const void *ref, const void *dist, double out[8]) {
+  if (ctx == nullptr || out == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
+      ctx->head != ctx->tail)
+    return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  const int rc = submit_frame(ctx, ref, dist);
+  if (rc != VIF_OK)
+    return rc;
+  return collect_frame(ctx, out);
 }
 
 __attribute__((visibility("default"))) int vif_get_sums(const vif_ctx *ctx,
@@ -302,7 +435,7 @@ vif_get_row_sums(const vif_ctx *ctx, float *rows, int capacity) {
   if (ctx == nullptr || rows == nullptr || !ctx->have_sums ||
       capacity < ctx->total_rows)
     return vifk::set_status(VIF_EINVAL);
-  std::memcpy(rows, ctx->rows_host, sizeof(float) * 2 * ctx->total_rows);
+  std::memcpy(rows, ctx->last_rows, sizeof(float) * 2 * ctx->total_rows);
   vifk::set_status(VIF_OK);
   return ctx->total_rows;
 }
@@ -319,21 +452,12 @@ __attribute__((visibility("default"))) int vif_taps(int scale, float *taps) {
 
 __attribute__((visibility("default"))) int vif_set_profiling(vif_ctx *ctx,
                                                              int kinds) {
-  if (ctx == nullptr || kinds < 0 || kinds > 0xff)
+  if (ctx == nullptr || kinds < 0 || kinds > (1 << kKinds) - 1 ||
+      ctx->head != ctx->tail)
     return vifk::set_status(VIF_EINVAL);
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kKinds; ++k) {
     ctx->kernel_ms[k] = 0.0;
     ctx->kernel_launches[k] = 0;
-  }
-  if (kinds != 0) {
-    DeviceScope scope(ctx->device);
-    for (hipEvent_t &ev : ctx->ev) {
-      if (ev == nullptr) {
-        hipError_t e = hipEventCreate(&ev);
-        if (e != hipSuccess)
-          return vifk::status_from_hip(e);
-      }
-    }
   }
   ctx->prof_mask = kinds;
   return vifk::set_status(VIF_OK);
@@ -342,16 +466,16 @@ __attribute__((visibility("default"))) int vif_set_profiling(vif_ctx *ctx,
 __attribute__((visibility("default"))) int
 vif_get_kernel_times(const vif_ctx *ctx, double *ms, long *launches,
                      int capacity) {
-  if (ctx == nullptr || capacity < 8)
+  if (ctx == nullptr || capacity < kKinds)
     return vifk::set_status(VIF_EINVAL);
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kKinds; ++k) {
     if (ms)
       ms[k] = ctx->kernel_ms[k];
     if (launches)
       launches[k] = ctx->kernel_launches[k];
   }
   vifk::set_status(VIF_OK);
-  return 8;
+  return kKinds;
 }
 
 __attribute__((visibility("default"))) int vif_errno(void) {

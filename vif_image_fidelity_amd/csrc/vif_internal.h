@@ -21,27 +21,48 @@ struct TapArgs {
   float t[kMaxTaps];
 };
 
+// Terms of a 16-row strip: 32 sequences (16 rows x {num, den}).  In the
+// term buffer of a scale, strip p holds term_groups(w) groups of 4 columns,
+// each group the 32 sequences' 4 values: floats
+// [(p * term_groups(w) + g) * 128 + seq * 4 + (x % 4)] for column x = 4g + ...
+// In LDS a tile keeps them as [seq][x] with pitch kTermPitch.
+constexpr int kSeq = 32;
+constexpr int kTermPitch = kTileW + 4;
+
+__host__ __device__ inline int term_groups(int w) { return (w + 3) / 4; }
+
+// Arguments of the row-sum kernel (all four scales in one launch): scale s
+// owns the waves [pair_base[s], pair_base[s+1]), one wave per two strips.
+struct RowSumArgs {
+  const float *terms[kScales];
+  float *rows[kScales]; // rows[s][2*y + c]
+  int w[kScales], h[kScales], strips[kScales];
+  int pair_base[kScales + 1];
+};
+
 // Host tap generator (vif_taps.cpp).
 int gaussian_taps(int scale, float *taps);
 
 // Geometry of one scale.
 struct ScaleGeom {
   int w, h;
-  int strips;        // ceil(h / kTileH)
-  size_t term_elems; // floats in the term buffer: strips * w * 32
+  int strips; // ceil(h / kTileH)
+  int ntx;    // ceil(w / kTileW)
+  size_t tiles() const { return static_cast<size_t>(strips) * ntx; }
 };
 
-// Per-scale filter + statistic + decimation kernel.  in_* are the scale's
-// planes (native samples at scale 0, fp32 planes above); next_* receive the
-// next scale's planes (unused at scale 3).
+// Per-scale kernel: filter, statistic, terms and the next scale's planes.
+// in_* are the scale's planes (native samples at scale 0, fp32 planes
+// above); next_* receive the next scale's planes (unused at scale 3); terms
+// is the scale's term buffer (strips * term_groups(w) * 128 floats).
 hipError_t launch_scale(int scale, int bpc, const void *in_ref,
                         const void *in_dist, const ScaleGeom &g,
                         const TapArgs &taps, const TapArgs &next_taps,
-                        float *terms, float *next_ref, float *next_dist,
+                        float *next_ref, float *next_dist, float *terms,
                         hipStream_t stream);
 
-// Ordered per-row sums of one scale's term buffer into rows[2*y + c].
-hipError_t launch_rowsum(const float *terms, const ScaleGeom &g, float *rows,
+// Ordered row sums of all scales of one frame (`waves` = pair_base[4]).
+hipError_t launch_rowsum(const RowSumArgs &args, int waves,
                          hipStream_t stream);
 
 }  // namespace vifk

@@ -1,6 +1,6 @@
-// vif_kernels.hip -- HIP kernels of the float VIF feature for gfx950.
+// vif_kernels.hip -- HIP kernel of the float VIF feature for gfx950.
 //
-// Per scale s one kernel does, for a 112 x 16 tile of output pixels:
+// One kernel per scale s does, for a 112 x 16 tile of output pixels:
 //   1. stage the tile's input (+ halo of the filter radius) into LDS as fp32,
 //      normalising native samples on the way (Research-2130 "float_ssim
 //      decimation on the SYCL device", Sources: 8-bit as is, 10/12/16-bit
@@ -11,13 +11,12 @@
 //      x, y, x*x, y*y, x*y, one thread per column and 8 rows in registers,
 //      and the vertical pass of the next scale's low-pass at even rows;
 //   3. the horizontal pass (7 outputs per thread), the per-pixel statistic
-//      and the two terms, written to a row-strip-blocked term buffer;
+//      and the two terms, staged in LDS and written to the scale's term
+//      buffer in the order the row sums read them;
 //   4. the horizontal pass of the next scale's low-pass at even columns,
 //      written as the next scale's fp32 planes (2x decimation).
-// A second kernel adds each row's terms left to right in one fp32
-// accumulator (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...",
-// Context and Decision: one fp32 sum per row, no group or atomic
-// reduction).
+// A second kernel (one launch for all scales) adds each row's terms in
+// order.
 //
 // Every multiply and add is its own IEEE fp32 rounding (the library is
 // built with -ffp-contract=off), taps in ascending order, vertical pass
@@ -62,8 +61,8 @@ __device__ __forceinline__ float load_sample<float>(
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
-    float in_scale, TapArgs taps, TapArgs dtaps, float *__restrict__ terms,
-    float *__restrict__ next_ref, float *__restrict__ next_dist) {
+    float in_scale, TapArgs taps, TapArgs dtaps, float *__restrict__ next_ref,
+    float *__restrict__ next_dist, float *__restrict__ terms) {
   constexpr int N = 2 * R + 1;
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
@@ -78,11 +77,15 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   static_assert(CW <= 128, "one thread per vertical column in two halves");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
   static_assert(kTileH == 2 * VB, "two row blocks");
+  static_assert(kSeq * kTermPitch <= 5 * kTileH * CWP,
+                "terms fit in the dead V region");
   __shared__ float lds[kLds];
 
   const int tid = threadIdx.x;
-  const int x0 = blockIdx.x * kTileW;
-  const int y0 = blockIdx.y * kTileH;
+  const int tx = blockIdx.x;
+  const int strip = blockIdx.y;
+  const int x0 = tx * kTileW;
+  const int y0 = strip * kTileH;
 
   // 1. input tile [IR][CW] for ref then dist
   {
@@ -176,11 +179,12 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads();
 
-  // 4. horizontal pass, statistic and terms: thread (ty, seg) owns tile row
-  //    ty and columns seg*7 .. seg*7+6.
+  // 4. horizontal pass and statistic: thread (ty, seg) owns tile row ty and
+  //    columns seg*7 .. seg*7+6; the terms stay in registers.
+  const int ty = tid & 15;
+  const int seg = tid >> 4;
+  float tnum[HB], tden[HB];
   {
-    const int ty = tid & 15;
-    const int seg = tid >> 4;
     float f[5][HB];
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
@@ -198,24 +202,23 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         f[q][i] = a;
       }
     }
-    const int y = y0 + ty;
-    if (y < h) {
-      // term layout: [strip][x][row in strip][num, den]
-      float *tstrip = terms + static_cast<size_t>(blockIdx.y) * w * 32 + ty * 2;
 #pragma unroll
-      for (int i = 0; i < HB; ++i) {
-        const int x = x0 + seg * HB + i;
-        if (x < w) {
-          float num, den;
-          pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], num, den);
-          *reinterpret_cast<float2 *>(tstrip + static_cast<size_t>(x) * 32) =
-              make_float2(num, den);
-        }
-      }
-    }
+    for (int i = 0; i < HB; ++i)
+      pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], tnum[i],
+                  tden[i]);
+  }
+  __syncthreads(); // every read of V is done: its region takes the terms
+
+  // 5. terms to LDS as 32 sequences (row-major per row and component):
+  //    sT[2*ty + c][x], the order in which the row sums read them.
+  float *sT = lds;
+#pragma unroll
+  for (int i = 0; i < HB; ++i) {
+    sT[(2 * ty) * kTermPitch + seg * HB + i] = tnum[i];
+    sT[(2 * ty + 1) * kTermPitch + seg * HB + i] = tden[i];
   }
 
-  // 5. next scale's planes: horizontal low-pass at even columns of the even
+  // 6. next scale's planes: horizontal low-pass at even columns of the even
   //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1.
   if constexpr (RD > 0) {
     const int yd = tid & 7;
@@ -244,52 +247,102 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
       }
     }
   }
+  __syncthreads(); // terms complete in LDS
+
+  // 7. terms to the strip's term buffer: groups of 4 columns, each group
+  //    holding the 32 sequences' 4 values ([g][seq][4] floats); this tile's
+  //    28 groups are one contiguous 14 KiB block.
+  {
+    float4 *dst = reinterpret_cast<float4 *>(
+        terms + (static_cast<size_t>(strip) * term_groups(w) + x0 / 4) *
+                    (kSeq * 4));
+    const int groups = min(kTileW, w - x0 + 3) / 4;
+    for (int i = tid; i < groups * kSeq; i += kThreads) {
+      const int g = i / kSeq;
+      const int q = i - g * kSeq;
+      dst[i] = *reinterpret_cast<const float4 *>(sT + q * kTermPitch + 4 * g);
+    }
+  }
 }
 
-// Ordered row sums of one scale.  One block per 16-row strip.  Waves 1..3
-// stream the strip's terms into LDS, chunk by chunk (double-buffered); lane
-// l < 32 of wave 0 owns row l/2, component l%2 (num or den) and adds the
-// chunk's terms to its single fp32 accumulator in ascending x.
-constexpr int kRowChunk = 128; // columns per chunk (16 KiB)
+// Ordered row sums of every scale, one launch per frame.  One wave owns two
+// 16-row strips of one scale: lane l adds sequence l%32 (row (l%32)/2,
+// component l%2) of strip 2p + l/32 left to right into one fp32
+// accumulator starting at 0.0f, exactly the serial loop over the row
+// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Context and
+// Decision: one fp32 sum per row, in order, no group or atomic reduction).
+// Each float4 load brings four consecutive columns of a lane's sequence;
+// two register batches keep one batch of loads in flight while the other is
+// added.  No LDS, so these waves fit beside a running scale kernel.
+constexpr int kRowBatch = 12; // float4 loads per batch and lane
 
-__global__ __launch_bounds__(kThreads) void rowsum_kernel(
-    const float *__restrict__ terms, int w, int h, float *__restrict__ rows) {
-  __shared__ float4 buf[2][kRowChunk * 8];
-  const int tid = threadIdx.x;
-  const int strip = blockIdx.x;
-  const float4 *src = reinterpret_cast<const float4 *>(
-      terms + static_cast<size_t>(strip) * w * 32);
-  const int nchunks = (w + kRowChunk - 1) / kRowChunk;
+__device__ __forceinline__ void load_batch(float4 (&v)[kRowBatch],
+                                           const float4 *__restrict__ src,
+                                           int g0, int groups) {
+#pragma unroll
+  for (int k = 0; k < kRowBatch; ++k) {
+    const int g = min(g0 + k, groups - 1); // in-bounds; extras are not added
+    v[k] = src[static_cast<size_t>(g) * kSeq];
+  }
+}
 
-  auto load_chunk = [&](int c) {
-    const int ncols = min(kRowChunk, w - c * kRowChunk);
-    const float4 *s = src + static_cast<size_t>(c) * kRowChunk * 8;
-    float4 *d = buf[c & 1];
-    for (int i = tid - 64; i < ncols * 8; i += kThreads - 64)
-      d[i] = s[i];
-  };
-
-  if (tid >= 64)
-    load_chunk(0);
-  __syncthreads();
-  float acc = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    if (tid >= 64) {
-      if (c + 1 < nchunks)
-        load_chunk(c + 1);
-    } else if (tid < 32) {
-      const int ncols = min(kRowChunk, w - c * kRowChunk);
-      const float *b = reinterpret_cast<const float *>(buf[c & 1]) + tid;
-      for (int x = 0; x < ncols; ++x)
-        acc = acc + b[x * 32];
+__device__ __forceinline__ float add_batch(float acc, const float4 (&v)[kRowBatch],
+                                           int x0, int w) {
+  if (x0 + 4 * kRowBatch <= w) {
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+      acc = acc + v[k].x;
+      acc = acc + v[k].y;
+      acc = acc + v[k].z;
+      acc = acc + v[k].w;
     }
-    __syncthreads();
+  } else {
+    for (int k = 0; k < kRowBatch; ++k) {
+      const int x = x0 + 4 * k;
+      if (x < w)
+        acc = acc + v[k].x;
+      if (x + 1 < w)
+        acc = acc + v[k].y;
+      if (x + 2 < w)
+        acc = acc + v[k].z;
+      if (x + 3 < w)
+        acc = acc + v[k].w;
+    }
   }
-  if (tid < 32) {
-    const int y = strip * kTileH + (tid >> 1);
-    if (y < h)
-      rows[y * 2 + (tid & 1)] = acc;
+  return acc;
+}
+
+__global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
+  const int wave = blockIdx.x;
+  int s = 0;
+  while (s + 1 < kScales && wave >= a.pair_base[s + 1])
+    ++s;
+  const int lane = threadIdx.x;
+  const int strips = a.strips[s];
+  int strip = 2 * (wave - a.pair_base[s]) + (lane >> 5);
+  const bool live = strip < strips;
+  strip = live ? strip : strips - 1; // a real strip; its sums are dropped
+  const int seq = lane & 31;
+  const int w = a.w[s];
+  const int groups = term_groups(w);
+  const float4 *src = reinterpret_cast<const float4 *>(
+                          a.terms[s] +
+                          static_cast<size_t>(strip) * groups * (kSeq * 4)) +
+                      seq;
+  float acc = 0.0f;
+  float4 va[kRowBatch], vb[kRowBatch];
+  load_batch(va, src, 0, groups);
+  for (int g = 0; g < groups; g += 2 * kRowBatch) {
+    load_batch(vb, src, g + kRowBatch, groups);
+    acc = add_batch(acc, va, 4 * g, w);
+    if (g + kRowBatch >= groups)
+      break;
+    load_batch(va, src, g + 2 * kRowBatch, groups);
+    acc = add_batch(acc, vb, 4 * (g + kRowBatch), w);
   }
+  const int y = strip * kTileH + (seq >> 1);
+  if (live && y < a.h[s])
+    a.rows[s][2 * y + (seq & 1)] = acc;
 }
 
 // ------------------------------------------------------------------ launch
@@ -297,9 +350,9 @@ __global__ __launch_bounds__(kThreads) void rowsum_kernel(
 hipError_t launch_scale(int scale, int bpc, const void *in_ref,
                         const void *in_dist, const ScaleGeom &g,
                         const TapArgs &taps, const TapArgs &next_taps,
-                        float *terms, float *next_ref, float *next_dist,
+                        float *next_ref, float *next_dist, float *terms,
                         hipStream_t stream) {
-  const dim3 grid((g.w + kTileW - 1) / kTileW, g.strips);
+  const dim3 grid(static_cast<unsigned>(g.ntx), static_cast<unsigned>(g.strips));
   const dim3 block(kThreads);
   switch (scale) {
   case 0:
@@ -307,29 +360,29 @@ hipError_t launch_scale(int scale, int bpc, const void *in_ref,
       scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
           static_cast<const uint8_t *>(in_ref),
           static_cast<const uint8_t *>(in_dist), g.w, g.h, 1.0f, taps,
-          next_taps, terms, next_ref, next_dist);
+          next_taps, next_ref, next_dist, terms);
     } else {
       const float sc = bpc == 10 ? 0.25f : bpc == 12 ? 0.0625f : 0.00390625f;
       scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
           static_cast<const uint16_t *>(in_ref),
           static_cast<const uint16_t *>(in_dist), g.w, g.h, sc, taps,
-          next_taps, terms, next_ref, next_dist);
+          next_taps, next_ref, next_dist, terms);
     }
     break;
   case 1:
     scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, terms, next_ref, next_dist);
+        g.w, g.h, 1.0f, taps, next_taps, next_ref, next_dist, terms);
     break;
   case 2:
     scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, terms, next_ref, next_dist);
+        g.w, g.h, 1.0f, taps, next_taps, next_ref, next_dist, terms);
     break;
   case 3:
     scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, terms, nullptr, nullptr);
+        g.w, g.h, 1.0f, taps, next_taps, nullptr, nullptr, terms);
     break;
   default:
     return hipErrorInvalidValue;
@@ -337,10 +390,9 @@ hipError_t launch_scale(int scale, int bpc, const void *in_ref,
   return hipGetLastError();
 }
 
-hipError_t launch_rowsum(const float *terms, const ScaleGeom &g, float *rows,
+hipError_t launch_rowsum(const RowSumArgs &args, int waves,
                          hipStream_t stream) {
-  rowsum_kernel<<<dim3(g.strips), dim3(kThreads), 0, stream>>>(terms, g.w, g.h,
-                                                               rows);
+  rowsum_kernel<<<dim3(waves), dim3(64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
