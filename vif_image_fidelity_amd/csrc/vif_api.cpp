@@ -1,16 +1,20 @@
 // vif_api.cpp -- the C ABI of include/vif.h: context, launch sequence, one
 // read-back per frame and the host sums.
 //
-// Per frame, on the context's stream: the four per-scale kernels (filter,
-// statistic, terms and the next scale's planes), writing the terms into the
-// frame's slot of a small ring.  A second stream then runs the ordered
-// row sums of all scales (one launch) and copies them (two floats per row
-// per scale) to pinned host memory in one copy, while the next frame's
-// kernels already run on the first stream.  vif_collect adds the rows of
-// each scale top to bottom in fp32 on the host (ADR-1422 "float_vif_sycl
-// computes the CPU's arithmetic ...", Decision).  The scores are fp64
-// quotients of the fp32 sums; num and den add the four scales in order in
-// fp64.
+// Every frame has a slot of a small ring (its pyramid planes, term buffers
+// and row sums).  Its work runs on three streams:
+//   work stream   the scale-0 kernel (filter, statistic, terms, scale-1
+//                 planes) -- the caller's stream or the default one;
+//   scale stream  the kernels of scales 1..3, after the frame's scale 0;
+//   copy stream   the ordered row sums of all scales (one launch) and one
+//                 copy of them (two floats per row per scale) to pinned
+//                 host memory.
+// So the next frame's scale 0, which fills the whole GPU, runs while the
+// small scales, row sums and read-back of the previous frames finish.
+// vif_collect adds the rows of each scale top to bottom in fp32 on the host
+// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision).
+// The scores are fp64 quotients of the fp32 sums; num and den add the four
+// scales in order in fp64.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdlib>
@@ -30,10 +34,13 @@ constexpr int kDepth = VIF_QUEUE_DEPTH;
 constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
 
 struct Slot {
+  float *pyr_ref[kScales] = {};      // [0] unused: scale 0 reads the frames
+  float *pyr_dist[kScales] = {};
   float *terms[kScales] = {};        // term buffers of the four scales
   float *rows_dev = nullptr;         // 2 * total rows
   float *rows_host = nullptr;        // pinned
-  hipEvent_t kernels_done = nullptr; // on the work stream
+  hipEvent_t scale0_done = nullptr;  // on the work stream
+  hipEvent_t kernels_done = nullptr; // on the scale stream
   hipEvent_t copy_done = nullptr;    // on the copy stream
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
@@ -45,12 +52,11 @@ struct Slot {
 struct vif_ctx {
   int w = 0, h = 0, bpc = 0;
   int device = 0;
-  hipStream_t stream = nullptr;      // work stream (caller's or default)
-  hipStream_t copy_stream = nullptr; // owned: read-backs
+  hipStream_t stream = nullptr;       // work stream (caller's or default)
+  hipStream_t scale_stream = nullptr; // owned: scales 1..3
+  hipStream_t copy_stream = nullptr;  // owned: row sums and read-back
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
-  float *pyr_ref[kScales] = {}; // [0] unused: scale 0 reads the frames
-  float *pyr_dist[kScales] = {};
   Slot slots[kDepth];
   int total_rows = 0;
   int row_base[kScales] = {};
@@ -124,20 +130,20 @@ void destroy_event(hipEvent_t &e) {
 }
 
 void free_all(vif_ctx *c) {
-  for (int s = 0; s < kScales; ++s) {
-    if (c->pyr_ref[s])
-      (void)hipFree(c->pyr_ref[s]);
-    if (c->pyr_dist[s])
-      (void)hipFree(c->pyr_dist[s]);
-  }
   for (Slot &sl : c->slots) {
-    for (float *t : sl.terms)
-      if (t)
-        (void)hipFree(t);
+    for (int s = 0; s < kScales; ++s) {
+      if (sl.pyr_ref[s])
+        (void)hipFree(sl.pyr_ref[s]);
+      if (sl.pyr_dist[s])
+        (void)hipFree(sl.pyr_dist[s]);
+      if (sl.terms[s])
+        (void)hipFree(sl.terms[s]);
+    }
     if (sl.rows_dev)
       (void)hipFree(sl.rows_dev);
     if (sl.rows_host)
       (void)hipHostFree(sl.rows_host);
+    destroy_event(sl.scale0_done);
     destroy_event(sl.kernels_done);
     destroy_event(sl.copy_done);
     for (auto &p : sl.prof) {
@@ -145,6 +151,8 @@ void free_all(vif_ctx *c) {
       destroy_event(p[1]);
     }
   }
+  if (c->scale_stream)
+    (void)hipStreamDestroy(c->scale_stream);
   if (c->copy_stream)
     (void)hipStreamDestroy(c->copy_stream);
   std::free(c->last_rows);
@@ -157,30 +165,34 @@ template <typename T> hipError_t dev_alloc(T **p, size_t elems) {
 // Enqueues one frame into the slot at ctx->head.
 int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   Slot &sl = ctx->slots[ctx->head % kDepth];
-  hipStream_t st = ctx->stream;
   hipStream_t cs = ctx->copy_stream;
   hipError_t e = hipSuccess;
-  // the slot's terms and row sums are free once its last read-back is done
+  // the slot's buffers are free once its last read-back is done
   if (sl.used)
-    e = hipStreamWaitEvent(st, sl.copy_done, 0);
+    e = hipStreamWaitEvent(ctx->stream, sl.copy_done, 0);
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
-    const void *in_ref = s == 0 ? ref : ctx->pyr_ref[s];
-    const void *in_dist = s == 0 ? dist : ctx->pyr_dist[s];
-    float *nref = s + 1 < kScales ? ctx->pyr_ref[s + 1] : nullptr;
-    float *ndist = s + 1 < kScales ? ctx->pyr_dist[s + 1] : nullptr;
+    hipStream_t st = s == 0 ? ctx->stream : ctx->scale_stream;
+    if (s == 1)
+      e = hipStreamWaitEvent(st, sl.scale0_done, 0);
+    const void *in_ref = s == 0 ? ref : sl.pyr_ref[s];
+    const void *in_dist = s == 0 ? dist : sl.pyr_dist[s];
+    float *nref = s + 1 < kScales ? sl.pyr_ref[s + 1] : nullptr;
+    float *ndist = s + 1 < kScales ? sl.pyr_dist[s + 1] : nullptr;
     const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
     const bool timed = (sl.prof_mask >> s) & 1;
-    if (timed)
+    if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][0], st);
     if (e == hipSuccess)
       e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
                              ctx->taps[s], nt, nref, ndist, sl.terms[s], st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
+    if (e == hipSuccess && s == 0)
+      e = hipEventRecord(sl.scale0_done, st);
   }
   if (e == hipSuccess)
-    e = hipEventRecord(sl.kernels_done, st);
+    e = hipEventRecord(sl.kernels_done, ctx->scale_stream);
   if (e == hipSuccess)
     e = hipStreamWaitEvent(cs, sl.kernels_done, 0);
   vifk::RowSumArgs ra = ctx->rowsum;
@@ -321,13 +333,13 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
   if (c->last_rows == nullptr)
     e = hipErrorOutOfMemory;
 
-  for (int s = 1; s < kScales && e == hipSuccess; ++s) {
-    const size_t n = static_cast<size_t>(c->geom[s].w) * c->geom[s].h;
-    e = dev_alloc(&c->pyr_ref[s], n);
-    if (e == hipSuccess)
-      e = dev_alloc(&c->pyr_dist[s], n);
-  }
   for (Slot &sl : c->slots) {
+    for (int s = 1; s < kScales && e == hipSuccess; ++s) {
+      const size_t n = static_cast<size_t>(c->geom[s].w) * c->geom[s].h;
+      e = dev_alloc(&sl.pyr_ref[s], n);
+      if (e == hipSuccess)
+        e = dev_alloc(&sl.pyr_dist[s], n);
+    }
     for (int s = 0; s < kScales && e == hipSuccess; ++s)
       e = dev_alloc(&sl.terms[s], static_cast<size_t>(c->geom[s].strips) *
                                       vifk::term_groups(c->geom[s].w) *
@@ -338,6 +350,8 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
                         sizeof(float) * 2 * rows, hipHostMallocDefault);
     if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&sl.scale0_done, hipEventDisableTiming);
+    if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.kernels_done, hipEventDisableTiming);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.copy_done, hipEventDisableTiming);
@@ -346,6 +360,8 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
         if (e == hipSuccess)
           e = hipEventCreate(&ev);
   }
+  if (e == hipSuccess)
+    e = hipStreamCreateWithFlags(&c->scale_stream, hipStreamNonBlocking);
   if (e == hipSuccess)
     e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -365,6 +381,7 @@ __attribute__((visibility("default"))) void vif_destroy(vif_ctx *ctx) {
     DeviceScope scope(ctx->device);
     if (ctx->head != ctx->tail) {
       (void)hipStreamSynchronize(ctx->stream);
+      (void)hipStreamSynchronize(ctx->scale_stream);
       (void)hipStreamSynchronize(ctx->copy_stream);
     }
     free_all(ctx);
