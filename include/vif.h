@@ -103,12 +103,12 @@ int vif_pending(const vif_ctx *ctx);
 void vif_destroy(vif_ctx *ctx);
 
 /*
- * vif_set_stream -- the HIP stream (a hipStream_t passed as void*, e.g.
- * torch's current stream; NULL = default stream) on which a frame's first
- * kernel reads the frames; work queued on it before vif_submit is ordered
- * before that read.  The later kernels and the read-back run on two streams
- * the context owns.  The caller keeps the stream alive while the context
- * uses it.  VIF_EINVAL while frames are pending.
+ * vif_set_stream -- the caller's HIP stream (a hipStream_t passed as void*,
+ * e.g. torch's current stream; NULL = default stream): work queued on it
+ * before vif_submit (say, the copy that fills the frames) is ordered before
+ * the frame's kernels, which run on streams the context owns.  The caller
+ * keeps the stream alive while the context uses it.  VIF_EINVAL while
+ * frames are pending.
  */
 int vif_set_stream(vif_ctx *ctx, void *hip_stream);
 

@@ -2,15 +2,15 @@
 // read-back per frame and the host sums.
 //
 // Every frame has a slot of a small ring (its pyramid planes, term buffers
-// and row sums).  Its work runs on three streams:
-//   work stream   the scale-0 kernel (filter, statistic, terms, scale-1
-//                 planes) -- the caller's stream or the default one;
-//   scale stream  the kernels of scales 1..3, after the frame's scale 0;
+// and row sums).  Its work runs on streams the context owns:
+//   work stream   (two of them, alternating frames) the four per-scale
+//                 kernels (filter, statistic, terms, next scale's planes),
+//                 after an event recorded on the caller's stream;
 //   copy stream   the ordered row sums of all scales (one launch) and one
 //                 copy of them (two floats per row per scale) to pinned
 //                 host memory.
-// So the next frame's scale 0, which fills the whole GPU, runs while the
-// small scales, row sums and read-back of the previous frames finish.
+// So consecutive frames run concurrently: one frame's small scales, row
+// sums and read-back overlap the next frame's scale 0, which fills the GPU.
 // vif_collect adds the rows of each scale top to bottom in fp32 on the host
 // (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision).
 // The scores are fp64 quotients of the fp32 sums; num and den add the four
@@ -39,8 +39,8 @@ struct Slot {
   float *terms[kScales] = {};        // term buffers of the four scales
   float *rows_dev = nullptr;         // 2 * total rows
   float *rows_host = nullptr;        // pinned
-  hipEvent_t scale0_done = nullptr;  // on the work stream
-  hipEvent_t kernels_done = nullptr; // on the scale stream
+  hipEvent_t submitted = nullptr;    // on the caller's stream
+  hipEvent_t kernels_done = nullptr; // on the frame's work stream
   hipEvent_t copy_done = nullptr;    // on the copy stream
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
@@ -52,9 +52,9 @@ struct Slot {
 struct vif_ctx {
   int w = 0, h = 0, bpc = 0;
   int device = 0;
-  hipStream_t stream = nullptr;       // work stream (caller's or default)
-  hipStream_t scale_stream = nullptr; // owned: scales 1..3
-  hipStream_t copy_stream = nullptr;  // owned: row sums and read-back
+  hipStream_t stream = nullptr;         // caller's stream (or default)
+  hipStream_t work_stream[2] = {};      // owned: frames alternate
+  hipStream_t copy_stream = nullptr;    // owned: row sums and read-back
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
   Slot slots[kDepth];
@@ -143,7 +143,7 @@ void free_all(vif_ctx *c) {
       (void)hipFree(sl.rows_dev);
     if (sl.rows_host)
       (void)hipHostFree(sl.rows_host);
-    destroy_event(sl.scale0_done);
+    destroy_event(sl.submitted);
     destroy_event(sl.kernels_done);
     destroy_event(sl.copy_done);
     for (auto &p : sl.prof) {
@@ -151,8 +151,9 @@ void free_all(vif_ctx *c) {
       destroy_event(p[1]);
     }
   }
-  if (c->scale_stream)
-    (void)hipStreamDestroy(c->scale_stream);
+  for (hipStream_t &ws : c->work_stream)
+    if (ws)
+      (void)hipStreamDestroy(ws);
   if (c->copy_stream)
     (void)hipStreamDestroy(c->copy_stream);
   std::free(c->last_rows);
@@ -165,16 +166,17 @@ template <typename T> hipError_t dev_alloc(T **p, size_t elems) {
 // Enqueues one frame into the slot at ctx->head.
 int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   Slot &sl = ctx->slots[ctx->head % kDepth];
+  hipStream_t st = ctx->work_stream[ctx->head & 1];
   hipStream_t cs = ctx->copy_stream;
-  hipError_t e = hipSuccess;
+  // the frames are ready once the caller's stream reaches this point
+  hipError_t e = hipEventRecord(sl.submitted, ctx->stream);
+  if (e == hipSuccess)
+    e = hipStreamWaitEvent(st, sl.submitted, 0);
   // the slot's buffers are free once its last read-back is done
-  if (sl.used)
-    e = hipStreamWaitEvent(ctx->stream, sl.copy_done, 0);
+  if (e == hipSuccess && sl.used)
+    e = hipStreamWaitEvent(st, sl.copy_done, 0);
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
-    hipStream_t st = s == 0 ? ctx->stream : ctx->scale_stream;
-    if (s == 1)
-      e = hipStreamWaitEvent(st, sl.scale0_done, 0);
     const void *in_ref = s == 0 ? ref : sl.pyr_ref[s];
     const void *in_dist = s == 0 ? dist : sl.pyr_dist[s];
     float *nref = s + 1 < kScales ? sl.pyr_ref[s + 1] : nullptr;
@@ -188,11 +190,9 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
                              ctx->taps[s], nt, nref, ndist, sl.terms[s], st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
-    if (e == hipSuccess && s == 0)
-      e = hipEventRecord(sl.scale0_done, st);
   }
   if (e == hipSuccess)
-    e = hipEventRecord(sl.kernels_done, ctx->scale_stream);
+    e = hipEventRecord(sl.kernels_done, st);
   if (e == hipSuccess)
     e = hipStreamWaitEvent(cs, sl.kernels_done, 0);
   vifk::RowSumArgs ra = ctx->rowsum;
@@ -320,7 +320,12 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
     g.ntx = (ws + vifk::kTileW - 1) / vifk::kTileW;
     c->row_base[s] = rows;
     rows += hs;
-    vifk::gaussian_taps(s, c->taps[s].t);
+    const int nt = vifk::gaussian_taps(s, c->taps[s].t);
+    // the kernels rely on bitwise symmetric taps (see tap() there)
+    for (int k = 0; k < nt; ++k)
+      if (std::memcmp(&c->taps[s].t[k], &c->taps[s].t[nt - 1 - k],
+                      sizeof(float)) != 0)
+        e = hipErrorInvalidValue;
     c->rowsum.w[s] = ws;
     c->rowsum.h[s] = hs;
     c->rowsum.strips[s] = g.strips;
@@ -350,7 +355,7 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
                         sizeof(float) * 2 * rows, hipHostMallocDefault);
     if (e == hipSuccess)
-      e = hipEventCreateWithFlags(&sl.scale0_done, hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&sl.submitted, hipEventDisableTiming);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.kernels_done, hipEventDisableTiming);
     if (e == hipSuccess)
@@ -360,8 +365,9 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
         if (e == hipSuccess)
           e = hipEventCreate(&ev);
   }
-  if (e == hipSuccess)
-    e = hipStreamCreateWithFlags(&c->scale_stream, hipStreamNonBlocking);
+  for (hipStream_t &ws : c->work_stream)
+    if (e == hipSuccess)
+      e = hipStreamCreateWithFlags(&ws, hipStreamNonBlocking);
   if (e == hipSuccess)
     e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -380,8 +386,8 @@ __attribute__((visibility("default"))) void vif_destroy(vif_ctx *ctx) {
   {
     DeviceScope scope(ctx->device);
     if (ctx->head != ctx->tail) {
-      (void)hipStreamSynchronize(ctx->stream);
-      (void)hipStreamSynchronize(ctx->scale_stream);
+      for (hipStream_t ws : ctx->work_stream)
+        (void)hipStreamSynchronize(ws);
       (void)hipStreamSynchronize(ctx->copy_stream);
     }
     free_all(ctx);

@@ -56,6 +56,15 @@ __device__ __forceinline__ float load_sample<float>(
   return p[i];
 }
 
+// Tap k of an n-tap filter.  The taps are symmetric bit for bit (t[k] and
+// t[n-1-k] are the same fp32 value, checked on the host when the context is
+// created), so the kernels read only t[min(k, n-1-k)]: the products
+// t[k]*v and t[n-1-k]*v of the same sample are then one expression, which
+// the compiler computes once.  Same values, fewer multiplies.
+__device__ __forceinline__ float tap(const TapArgs &t, int k, int n) {
+  return t.t[k < n - 1 - k ? k : n - 1 - k];
+}
+
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
 template <int R, int RD, typename InT>
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
       for (int i = 0; i < VB; ++i) {
         const int k = j - i;
         if (k >= 0 && k < N) {
-          const float t = taps.t[k];
+          const float t = tap(taps, k, N);
           if (k == 0) {
             acc[0][i] = t * x;
             acc[1][i] = t * y;
@@ -145,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         for (int m = 0; m < VB / 2; ++m) {
           const int k = j - 2 * m - R + RD;
           if (k >= 0 && k < ND) {
-            const float t = dtaps.t[k];
+            const float t = tap(dtaps, k, ND);
             if (k == 0) {
               dacc[0][m] = t * x;
               dacc[1][m] = t * y;
@@ -195,10 +204,10 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         v[j] = row[j];
 #pragma unroll
       for (int i = 0; i < HB; ++i) {
-        float a = taps.t[0] * v[i];
+        float a = tap(taps, 0, N) * v[i];
 #pragma unroll
         for (int k = 1; k < N; ++k)
-          a = a + taps.t[k] * v[i + k];
+          a = a + tap(taps, k, N) * v[i + k];
         f[q][i] = a;
       }
     }
@@ -236,10 +245,10 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
           for (int p = 0; p < 2; ++p) {
             const float *row =
                 sVd + (p * (kTileH / 2) + yd) * CWP + 2 * xl + R - RD;
-            float a = dtaps.t[0] * row[0];
+            float a = tap(dtaps, 0, ND) * row[0];
 #pragma unroll
             for (int k = 1; k < ND; ++k)
-              a = a + dtaps.t[k] * row[k];
+              a = a + tap(dtaps, k, ND) * row[k];
             float *dst = p == 0 ? next_ref : next_dist;
             dst[static_cast<size_t>(ydg) * wd + xdg] = a;
           }
