@@ -6,7 +6,7 @@ One step scores one 3840x2160 8-bit luma frame pair (the whole path: four
 scales of filtering, statistic, decimation and ordered row sums, one
 read-back and the host sums).  The 20 synthetic 1/f-noise frame pairs are
 resident in HBM before the timed region; steps cycle through them and go
-through the context's asynchronous queue (submit / collect, up to three
+through the context's asynchronous queue (submit / collect, up to two
 frames in flight), so consecutive frames overlap their read-back and host
 work with the next frame's kernels.  Prints one JSON line.
 
@@ -28,6 +28,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -98,27 +100,73 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
     pairs = [(td(r), td(d)) for (r, d, _) in frames]
     ctx = V.Vif(w, h, bpc)
 
+    host = {"submit": 0.0, "collect": 0.0}
+
     def run(n):
         # keep the context's queue full: frame i+depth is submitted as soon
         # as frame i has been collected
+        clock = time.perf_counter
         for i in range(n):
             if ctx.pending() == V.QUEUE_DEPTH:
+                c0 = clock()
                 ctx.collect()
+                host["collect"] += clock() - c0
             r, d = pairs[i % len(pairs)]
+            c0 = clock()
             ctx.submit(r, d)
+            host["submit"] += clock() - c0
         while ctx.pending():
             ctx.collect()
 
     run(warmup)
     ctx.set_profiling(prof_kinds)
+    host["submit"] = host["collect"] = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = ctx.kernel_times()
+    kt["_host_submit_us"] = 1e6 * host["submit"] / max(steps, 1)
+    kt["_host_collect_us"] = 1e6 * host["collect"] / max(steps, 1)
     ctx.close()
     return (t1 - t0), kt
+
+
+def isolated_scale0_us(V, frames, w, h, bpc, n=50):
+    """Scale-0 kernel duration with one frame at a time (vif_score), i.e.
+    without the next frame's kernels sharing the GPU."""
+    import torch
+    dev = torch.device("cuda:0")
+    r, d, _ = frames[0]
+    tr = torch.from_numpy(np.ascontiguousarray(r)).to(dev)
+    tdd = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
+    ctx = V.Vif(w, h, bpc)
+    for _ in range(5):
+        ctx.score(tr, tdd)
+    ctx.set_profiling(["scale0"])
+    for _ in range(n):
+        ctx.score(tr, tdd)
+    ms, cnt = ctx.kernel_times()["scale0"]
+    ctx.close()
+    return 1000.0 * ms / max(cnt, 1)
+
+
+def path_ops(w, h):
+    """Plain fp32 operations the definition needs per frame, statistic
+    excluded: per scale the 3 products, 5 quantities x 2 passes x
+    (N mul + N-1 add) and 8 for the variances per pixel, the next scale's
+    low-pass (2 planes x 3 x (2N'-1) per decimated pixel) and 2 row-sum adds
+    per pixel."""
+    widths = (17, 9, 5, 3)
+    ops, ws, hs = 0.0, w, h
+    for s in range(4):
+        n = widths[s]
+        ops += (3 + 10 * (2 * n - 1) + 8 + 2) * ws * hs
+        if s < 3:
+            ops += 6 * (2 * widths[s + 1] - 1) * (ws // 2) * (hs // 2)
+        ws, hs = ws // 2, hs // 2
+    return ops
 
 
 COPY_BYTES = 256 << 20
@@ -200,15 +248,20 @@ def main():
     if args.mode == "frames":
         return
 
+    host_submit_us = kt["_host_submit_us"]
+    host_collect_us = kt["_host_collect_us"]
+    iso_s0_us = isolated_scale0_us(V, frames4k, w, h, bpc)
+
     # per-kernel split (all kinds timed; separate run, not the headline)
     _, kt_all = time_frames(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
                             prof_kinds=0x1F)
-    split = {k: round(1000.0 * ms / max(n, 1), 2) for k, (ms, n) in
-             kt_all.items()}
+    split = {k: round(1000.0 * v[0] / max(v[1], 1), 2)
+             for k, v in kt_all.items() if not k.startswith("_")}
 
     # 1080p (10-bit checkerboard workload) for the metric's second size
     f1080 = synth.checker_1080p_10bit()
-    dt1080, _ = time_frames(V, f1080, 1920, 1080, 10, args.steps_1080p, 10)
+    dt1080, kt1080 = time_frames(V, f1080, 1920, 1080, 10, args.steps_1080p,
+                                 10)
     fps1080 = args.steps_1080p / dt1080
 
     ops = OPS_PER_PIXEL_SCALE0 * w * h
@@ -219,9 +272,20 @@ def main():
                 "peak": round(peak, 2), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
+    pops = path_ops(w, h)
     extra = {"fps_1080p_10bit": round(fps1080, 1),
              "kernel_avg_us_4k": split,
-             "scale0_kernel_avg_us": round(1000 * s0_avg_ms, 2)}
+             "scale0_kernel_avg_us": round(1000 * s0_avg_ms, 2),
+             "scale0_kernel_isolated_us": round(iso_s0_us, 2),
+             "scale0_isolated_frac_of_valu_peak": round(
+                 ops / (iso_s0_us * 1e-6) / VALU_PEAK_OPS, 4),
+             "path_ops_per_frame": pops,
+             "path_frac_of_valu_peak": round(pops * fps / VALU_PEAK_OPS, 4),
+             "host_us_per_frame_4k": {"submit": round(host_submit_us, 2),
+                                      "collect": round(host_collect_us, 2)},
+             "host_us_per_frame_1080p": {
+                 "submit": round(kt1080["_host_submit_us"], 2),
+                 "collect": round(kt1080["_host_collect_us"], 2)}}
     if frame_bytes:
         gbs = frame_bytes * fps / 1e9
         extra["hbm_gbs_per_frame_counters"] = round(gbs, 1)

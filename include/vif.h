@@ -104,11 +104,13 @@ void vif_destroy(vif_ctx *ctx);
 
 /*
  * vif_set_stream -- the caller's HIP stream (a hipStream_t passed as void*,
- * e.g. torch's current stream; NULL = default stream): work queued on it
- * before vif_submit (say, the copy that fills the frames) is ordered before
- * the frame's kernels, which run on streams the context owns.  The caller
- * keeps the stream alive while the context uses it.  VIF_EINVAL while
- * frames are pending.
+ * e.g. torch's current stream; NULL = the default stream, the initial
+ * setting): work queued on it before vif_submit (say, the copy that fills
+ * the frames) is ordered before the frame's kernels, which run on two
+ * streams the context owns.  Those are blocking streams, so work on the
+ * default stream orders itself; a non-NULL stream costs one event per frame.
+ * The caller keeps the stream alive while the context uses it.  VIF_EINVAL
+ * while frames are pending.
  */
 int vif_set_stream(vif_ctx *ctx, void *hip_stream);
 

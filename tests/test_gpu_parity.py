@@ -172,6 +172,32 @@ def test_async_queue_matches_oracle(V, orc):
     ctx.close()
 
 
+def test_graph_replays_match_direct_launches(V, orc):
+    """Untimed frames replay a per-slot HIP graph whose frame pointers are
+    rewritten each time; timed frames launch directly.  Interleave both,
+    with host synchronisation between replays, over changing frames: every
+    replay must give the oracle's bits."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit(frames=3)
+    exps = [orc.score(r, d, b)[0] for (r, d, b) in frames]
+    dev = [(to_device(r), to_device(d)) for (r, d, _) in frames]
+    ctx = V.Vif(576, 324, 8)
+    for rnd in range(4):
+        ctx.set_profiling(0x1F if rnd % 2 else 0)
+        for i in range(7):
+            k = (i * 2 + rnd) % 3
+            got = ctx.score(*dev[k])
+            assert got.tobytes() == exps[k].tobytes(), (rnd, i)
+        for i in range(6):
+            k = (i + rnd) % 3
+            if ctx.pending() == V.QUEUE_DEPTH:
+                ctx.collect()
+            ctx.submit(*dev[k])
+        while ctx.pending():
+            ctx.collect()
+    ctx.close()
+
+
 def test_profiling_counts_launches(V):
     from vif_image_fidelity_amd import synth
     ref, dist, bpc = synth.netflix_576x324_8bit(frames=1)[0]

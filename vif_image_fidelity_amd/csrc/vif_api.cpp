@@ -1,18 +1,23 @@
 // vif_api.cpp -- the C ABI of include/vif.h: context, launch sequence, one
 // read-back per frame and the host sums.
 //
-// Every frame has a slot of a small ring (its pyramid planes, term buffers
-// and row sums).  Its work runs on streams the context owns:
-//   work stream   (two of them, alternating frames) the four per-scale
-//                 kernels (filter, statistic, terms, next scale's planes),
-//                 after an event recorded on the caller's stream;
-//   copy stream   the ordered row sums of all scales (one launch) and one
-//                 copy of them (two floats per row per scale) to pinned
-//                 host memory.
-// So consecutive frames run concurrently: one frame's small scales, row
-// sums and read-back overlap the next frame's scale 0, which fills the GPU.
-// vif_collect adds the rows of each scale top to bottom in fp32 on the host
-// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision).
+// Every frame has a slot of a three-slot ring, and every slot its own stream
+// and buffers (pyramid planes, term buffers, and its row sums in pinned
+// host memory).  The slot's stream runs the four per-scale kernels (filter,
+// statistic, terms, next scale's planes) and the ordered row sums of all
+// scales (one launch), which write two floats per row per scale straight
+// into the host buffer: one read-back per frame with no copy call
+// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision:
+// the row sums come back in one transfer and the host adds them).
+// Consecutive frames rotate over the slots, so one frame's small
+// scales and row sums overlap the next frame's scale 0, which fills the
+// GPU.  A submission is six runtime calls: five launches and one event.
+//
+// The slot streams are blocking streams, so they are ordered after work on
+// the default stream (where a caller typically fills the frames); a caller
+// stream set with vif_set_stream is joined with an event instead.
+//
+// vif_collect adds the rows of each scale top to bottom in fp32 on the host.
 // The scores are fp64 quotients of the fp32 sums; num and den add the four
 // scales in order in fp64.
 #include <hip/hip_runtime_api.h>
@@ -34,17 +39,15 @@ constexpr int kDepth = VIF_QUEUE_DEPTH;
 constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
 
 struct Slot {
-  float *pyr_ref[kScales] = {};      // [0] unused: scale 0 reads the frames
+  float *pyr_ref[kScales] = {};   // [0] unused: scale 0 reads the frames
   float *pyr_dist[kScales] = {};
-  float *terms[kScales] = {};        // term buffers of the four scales
-  float *rows_dev = nullptr;         // 2 * total rows
-  float *rows_host = nullptr;        // pinned
-  hipEvent_t submitted = nullptr;    // on the caller's stream
-  hipEvent_t kernels_done = nullptr; // on the frame's work stream
-  hipEvent_t copy_done = nullptr;    // on the copy stream
+  float *terms[kScales] = {};     // term buffers of the four scales
+  float *rows_host = nullptr;     // pinned, written by the row-sum kernel
+  hipStream_t stream = nullptr;   // owned: all of the slot's work
+  hipEvent_t submitted = nullptr; // on the caller's stream
+  hipEvent_t done = nullptr;      // on the slot's stream, after the row sums
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
-  bool used = false;
 };
 
 } // namespace
@@ -52,9 +55,7 @@ struct Slot {
 struct vif_ctx {
   int w = 0, h = 0, bpc = 0;
   int device = 0;
-  hipStream_t stream = nullptr;         // caller's stream (or default)
-  hipStream_t work_stream[2] = {};      // owned: frames alternate
-  hipStream_t copy_stream = nullptr;    // owned: row sums and read-back
+  hipStream_t stream = nullptr; // caller's stream (NULL: the default stream)
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
   Slot slots[kDepth];
@@ -139,23 +140,17 @@ void free_all(vif_ctx *c) {
       if (sl.terms[s])
         (void)hipFree(sl.terms[s]);
     }
-    if (sl.rows_dev)
-      (void)hipFree(sl.rows_dev);
     if (sl.rows_host)
       (void)hipHostFree(sl.rows_host);
     destroy_event(sl.submitted);
-    destroy_event(sl.kernels_done);
-    destroy_event(sl.copy_done);
+    destroy_event(sl.done);
     for (auto &p : sl.prof) {
       destroy_event(p[0]);
       destroy_event(p[1]);
     }
+    if (sl.stream)
+      (void)hipStreamDestroy(sl.stream);
   }
-  for (hipStream_t &ws : c->work_stream)
-    if (ws)
-      (void)hipStreamDestroy(ws);
-  if (c->copy_stream)
-    (void)hipStreamDestroy(c->copy_stream);
   std::free(c->last_rows);
 }
 
@@ -166,15 +161,15 @@ template <typename T> hipError_t dev_alloc(T **p, size_t elems) {
 // Enqueues one frame into the slot at ctx->head.
 int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   Slot &sl = ctx->slots[ctx->head % kDepth];
-  hipStream_t st = ctx->work_stream[ctx->head & 1];
-  hipStream_t cs = ctx->copy_stream;
-  // the frames are ready once the caller's stream reaches this point
-  hipError_t e = hipEventRecord(sl.submitted, ctx->stream);
-  if (e == hipSuccess)
-    e = hipStreamWaitEvent(st, sl.submitted, 0);
-  // the slot's buffers are free once its last read-back is done
-  if (e == hipSuccess && sl.used)
-    e = hipStreamWaitEvent(st, sl.copy_done, 0);
+  hipStream_t st = sl.stream;
+  hipError_t e = hipSuccess;
+  // the slot's previous frame is ordered before this one on its stream;
+  // work on the default stream is ordered before it by the blocking stream
+  if (ctx->stream != nullptr) {
+    e = hipEventRecord(sl.submitted, ctx->stream);
+    if (e == hipSuccess)
+      e = hipStreamWaitEvent(st, sl.submitted, 0);
+  }
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
     const void *in_ref = s == 0 ? ref : sl.pyr_ref[s];
@@ -183,7 +178,7 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
     float *ndist = s + 1 < kScales ? sl.pyr_dist[s + 1] : nullptr;
     const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
     const bool timed = (sl.prof_mask >> s) & 1;
-    if (e == hipSuccess && timed)
+    if (timed)
       e = hipEventRecord(sl.prof[s][0], st);
     if (e == hipSuccess)
       e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
@@ -191,31 +186,22 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
   }
-  if (e == hipSuccess)
-    e = hipEventRecord(sl.kernels_done, st);
-  if (e == hipSuccess)
-    e = hipStreamWaitEvent(cs, sl.kernels_done, 0);
   vifk::RowSumArgs ra = ctx->rowsum;
   for (int s = 0; s < kScales; ++s) {
     ra.terms[s] = sl.terms[s];
-    ra.rows[s] = sl.rows_dev + 2 * ctx->row_base[s];
+    ra.rows[s] = sl.rows_host + 2 * ctx->row_base[s];
   }
   const bool timed = (sl.prof_mask >> kScales) & 1;
   if (e == hipSuccess && timed)
-    e = hipEventRecord(sl.prof[kScales][0], cs);
+    e = hipEventRecord(sl.prof[kScales][0], st);
   if (e == hipSuccess)
-    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, cs);
+    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, st);
   if (e == hipSuccess && timed)
-    e = hipEventRecord(sl.prof[kScales][1], cs);
+    e = hipEventRecord(sl.prof[kScales][1], st);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(sl.rows_host, sl.rows_dev,
-                       sizeof(float) * 2 * ctx->total_rows,
-                       hipMemcpyDeviceToHost, cs);
-  if (e == hipSuccess)
-    e = hipEventRecord(sl.copy_done, cs);
+    e = hipEventRecord(sl.done, st);
   if (e != hipSuccess)
     return vifk::status_from_hip(e);
-  sl.used = true;
   ctx->head += 1;
   return vifk::set_status(VIF_OK);
 }
@@ -223,7 +209,7 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
 // Waits for the oldest pending frame and writes its outputs.
 int collect_frame(vif_ctx *ctx, double out[8]) {
   Slot &sl = ctx->slots[ctx->tail % kDepth];
-  hipError_t e = hipEventSynchronize(sl.copy_done);
+  hipError_t e = hipEventSynchronize(sl.done);
   if (e != hipSuccess) {
     ctx->tail += 1; // the frame is lost; keep the ring consistent
     return vifk::status_from_hip(e);
@@ -349,27 +335,23 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
       e = dev_alloc(&sl.terms[s], static_cast<size_t>(c->geom[s].strips) *
                                       vifk::term_groups(c->geom[s].w) *
                                       vifk::kSeq * 4);
-    if (e == hipSuccess)
-      e = dev_alloc(&sl.rows_dev, static_cast<size_t>(2) * rows);
+    // coherent pinned memory: the row-sum kernel's stores reach the host
+    // without a copy, visible once the slot's event has completed
     if (e == hipSuccess)
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
-                        sizeof(float) * 2 * rows, hipHostMallocDefault);
+                        sizeof(float) * 2 * rows, hipHostMallocCoherent);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.submitted, hipEventDisableTiming);
     if (e == hipSuccess)
-      e = hipEventCreateWithFlags(&sl.kernels_done, hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
     if (e == hipSuccess)
-      e = hipEventCreateWithFlags(&sl.copy_done, hipEventDisableTiming);
+      e = hipStreamCreate(&sl.stream); // blocking: ordered with the default
+                                       // stream
     for (auto &p : sl.prof)
       for (hipEvent_t &ev : p)
         if (e == hipSuccess)
           e = hipEventCreate(&ev);
   }
-  for (hipStream_t &ws : c->work_stream)
-    if (e == hipSuccess)
-      e = hipStreamCreateWithFlags(&ws, hipStreamNonBlocking);
-  if (e == hipSuccess)
-    e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     free_all(c);
     delete c;
@@ -386,9 +368,8 @@ __attribute__((visibility("default"))) void vif_destroy(vif_ctx *ctx) {
   {
     DeviceScope scope(ctx->device);
     if (ctx->head != ctx->tail) {
-      for (hipStream_t ws : ctx->work_stream)
-        (void)hipStreamSynchronize(ws);
-      (void)hipStreamSynchronize(ctx->copy_stream);
+      for (Slot &sl : ctx->slots)
+        (void)hipStreamSynchronize(sl.stream);
     }
     free_all(ctx);
   }

@@ -35,7 +35,7 @@ __host__ __device__ inline int term_groups(int w) { return (w + 3) / 4; }
 // owns the waves [pair_base[s], pair_base[s+1]), one wave per two strips.
 struct RowSumArgs {
   const float *terms[kScales];
-  float *rows[kScales]; // rows[s][2*y + c]
+  float *rows[kScales]; // rows[s][2*y + c], in pinned host memory
   int w[kScales], h[kScales], strips[kScales];
   int pair_base[kScales + 1];
 };
