@@ -33,26 +33,27 @@ namespace vifk {
 
 constexpr int kThreads = 256;
 
+// Planes hold at most 2^27 samples, so a 32-bit offset addresses them.
 template <typename InT>
 __device__ __forceinline__ float load_sample(const InT *__restrict__ p,
-                                             size_t i, float scale);
+                                             unsigned i, float scale);
 
 template <>
 __device__ __forceinline__ float load_sample<uint8_t>(
-    const uint8_t *__restrict__ p, size_t i, float) {
+    const uint8_t *__restrict__ p, unsigned i, float) {
   return static_cast<float>(p[i]);
 }
 
 template <>
 __device__ __forceinline__ float load_sample<uint16_t>(
-    const uint16_t *__restrict__ p, size_t i, float scale) {
+    const uint16_t *__restrict__ p, unsigned i, float scale) {
   // scale is an exact power of two (1/4, 1/16, 1/256): the product is exact
   return static_cast<float>(p[i]) * scale;
 }
 
 template <>
 __device__ __forceinline__ float load_sample<float>(
-    const float *__restrict__ p, size_t i, float) {
+    const float *__restrict__ p, unsigned i, float) {
   return p[i];
 }
 
@@ -96,15 +97,20 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
 
-  // 1. input tile [IR][CW] for ref then dist
+  // 1. input tile [IR][CW] for ref then dist.  Waves 0-1 load the even
+  //    rows, waves 2-3 the odd ones: the row (and its mirror) is uniform in a
+  //    wave, and all of a thread's loads are issued before the first use.
   {
     const int c = tid & 127;
-    const int half = tid >> 7;
+    const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+    static_assert(IR % 2 == 0, "the two row phases cover the tile");
     if (c < CW) {
-      const int gx = mirror_clamp(x0 - R + c, w);
-      for (int j = half; j < IR; j += 2) {
-        const int gy = mirror_clamp(y0 - R + j, h);
-        const size_t off = static_cast<size_t>(gy) * w + gx;
+      const unsigned gx = static_cast<unsigned>(mirror_clamp(x0 - R + c, w));
+#pragma unroll
+      for (int it = 0; it < IR / 2; ++it) {
+        const int j = half + 2 * it;
+        const unsigned gy = static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
+        const unsigned off = gy * static_cast<unsigned>(w) + gx;
         lds[j * CW + c] = load_sample<InT>(ref, off, in_scale);
         lds[IR * CW + j * CW + c] = load_sample<InT>(dist, off, in_scale);
       }
