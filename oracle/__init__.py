@@ -30,6 +30,40 @@ WIDTHS = (17, 9, 5, 3)
 _default = None
 
 
+class Options(ctypes.Structure):
+    """vifo_options: readings of the option names the pages give."""
+    _fields_ = [("sigma_nsq", ctypes.c_double),
+                ("enhn_gain_limit", ctypes.c_double),
+                ("kernelscale", ctypes.c_double),
+                ("scale_min_val", ctypes.c_double * 3),
+                ("skip_scale0", ctypes.c_int)]
+
+
+DEFAULT_OPTIONS = {"sigma_nsq": 2.0, "enhn_gain_limit": 100.0,
+                   "kernelscale": 1.0, "scale_min_val": (0.0, 0.0, 0.0),
+                   "skip_scale0": 0}
+
+
+def make_options(options=None):
+    """An Options structure from a dict of overrides of the defaults."""
+    d = dict(DEFAULT_OPTIONS)
+    if options:
+        unknown = set(options) - set(d)
+        if unknown:
+            raise ValueError("unknown options %s" % sorted(unknown))
+        d.update(options)
+    o = Options()
+    o.sigma_nsq = float(d["sigma_nsq"])
+    o.enhn_gain_limit = float(d["enhn_gain_limit"])
+    o.kernelscale = float(d["kernelscale"])
+    mv = tuple(d["scale_min_val"])
+    if len(mv) != 3:
+        raise ValueError("scale_min_val needs three floors")
+    o.scale_min_val[:] = [float(v) for v in mv]
+    o.skip_scale0 = int(d["skip_scale0"])
+    return o
+
+
 def build(src=_SRC, out=_LIB):
     """Compile the oracle C source into a shared library (default: in place)."""
     tmp = out + ".tmp%d" % os.getpid()
@@ -59,10 +93,21 @@ class Oracle:
         lib.vifo_ratio_arrays.argtypes = [f32p, f32p, f32p, f32p,
                                           ctypes.c_long]
         lib.vifo_ratio_arrays.restype = None
+        lib.vifo_ratio_arrays_nsq.argtypes = [f32p, f32p, ctypes.c_double,
+                                              f32p, f32p, ctypes.c_long]
+        lib.vifo_ratio_arrays_nsq.restype = None
         lib.vifo_statistic.argtypes = [ctypes.c_float] * 5 + [f32p, f32p]
         lib.vifo_statistic_array.argtypes = [f32p] * 7 + [ctypes.c_long]
         lib.vifo_statistic_array.restype = None
         lib.vifo_statistic.restype = None
+        lib.vifo_statistic_ex.argtypes = ([ctypes.c_float] * 5
+                                          + [ctypes.c_double] * 2
+                                          + [f32p, f32p])
+        lib.vifo_statistic_ex.restype = None
+        lib.vifo_statistic_array_ex.argtypes = ([f32p] * 5
+                                                + [ctypes.c_double] * 2
+                                                + [f32p, f32p, ctypes.c_long])
+        lib.vifo_statistic_array_ex.restype = None
         lib.vifo_normalise.argtypes = [ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, f32p]
         lib.vifo_normalise.restype = ctypes.c_int
@@ -77,6 +122,11 @@ class Oracle:
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    f64p, f32p, f32p]
         lib.vifo_score.restype = ctypes.c_int
+        lib.vifo_score_ex.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(Options), f64p, f32p,
+                                      f32p]
+        lib.vifo_score_ex.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -97,32 +147,49 @@ class Oracle:
         self.lib.vifo_log2_array(_fp(xs), _fp(out), xs.size)
         return out
 
-    def ratios(self, a, sv):
-        """(fl32(1 + a/(sv + nsq)), fl32(1 + a/nsq)) element-wise."""
+    def ratios(self, a, sv, nsq=None):
+        """(fl32(1 + a/(sv + nsq)), fl32(1 + a/nsq)) element-wise; nsq=None
+        is the default 2.0 through the default entry point."""
         a = np.ascontiguousarray(a, dtype=np.float32)
         sv = np.ascontiguousarray(sv, dtype=np.float32)
         num = np.empty_like(a)
         den = np.empty_like(a)
-        self.lib.vifo_ratio_arrays(_fp(a), _fp(sv), _fp(num), _fp(den), a.size)
+        if nsq is None:
+            self.lib.vifo_ratio_arrays(_fp(a), _fp(sv), _fp(num), _fp(den),
+                                       a.size)
+        else:
+            self.lib.vifo_ratio_arrays_nsq(_fp(a), _fp(sv), float(nsq),
+                                           _fp(num), _fp(den), a.size)
         return num, den
 
-    def statistic(self, mu1, mu2, xx, yy, xy):
+    def statistic(self, mu1, mu2, xx, yy, xy, nsq=None, gain_limit=None):
         n = ctypes.c_float()
         d = ctypes.c_float()
-        self.lib.vifo_statistic(float(np.float32(mu1)), float(np.float32(mu2)),
-                                float(np.float32(xx)), float(np.float32(yy)),
-                                float(np.float32(xy)), ctypes.byref(n),
-                                ctypes.byref(d))
+        args = [float(np.float32(v)) for v in (mu1, mu2, xx, yy, xy)]
+        if nsq is None and gain_limit is None:
+            self.lib.vifo_statistic(*args, ctypes.byref(n), ctypes.byref(d))
+        else:
+            self.lib.vifo_statistic_ex(
+                *args, 2.0 if nsq is None else float(nsq),
+                100.0 if gain_limit is None else float(gain_limit),
+                ctypes.byref(n), ctypes.byref(d))
         return np.float32(n.value), np.float32(d.value)
 
-    def statistic_array(self, mu1, mu2, xx, yy, xy):
+    def statistic_array(self, mu1, mu2, xx, yy, xy, nsq=None,
+                        gain_limit=None):
         """vifo_statistic element-wise over five float32 arrays."""
         ins = [np.ascontiguousarray(a, dtype=np.float32)
                for a in (mu1, mu2, xx, yy, xy)]
         num = np.empty_like(ins[0])
         den = np.empty_like(ins[0])
-        self.lib.vifo_statistic_array(*[_fp(a) for a in ins], _fp(num),
-                                      _fp(den), ins[0].size)
+        if nsq is None and gain_limit is None:
+            self.lib.vifo_statistic_array(*[_fp(a) for a in ins], _fp(num),
+                                          _fp(den), ins[0].size)
+        else:
+            self.lib.vifo_statistic_array_ex(
+                *[_fp(a) for a in ins], 2.0 if nsq is None else float(nsq),
+                100.0 if gain_limit is None else float(gain_limit),
+                _fp(num), _fp(den), ins[0].size)
         return num, den
 
     def normalise(self, plane, bpc):
@@ -160,8 +227,10 @@ class Oracle:
     def total_rows(self, w, h):
         return int(self.lib.vifo_total_rows(int(w), int(h)))
 
-    def score(self, ref, dist, bpc, want_rows=False):
-        """Return (out[8] float64, sums[8] float32[, rowsums (rows, 2)])."""
+    def score(self, ref, dist, bpc, want_rows=False, options=None):
+        """Return (out[8] float64, sums[8] float32[, rowsums (rows, 2)]).
+        options: None (the default entry point) or a dict of overrides of
+        DEFAULT_OPTIONS (through vifo_score_ex)."""
         ref = np.ascontiguousarray(ref)
         dist = np.ascontiguousarray(dist)
         if ref.shape != dist.shape or ref.ndim != 2:
@@ -178,9 +247,15 @@ class Oracle:
         if want_rows:
             rows = np.zeros((self.total_rows(w, h), 2), dtype=np.float32)
             rp = _fp(rows)
-        rc = self.lib.vifo_score(
-            ref.ctypes.data, dist.ctypes.data, w, h, int(bpc),
-            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _fp(sums), rp)
+        op = out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        if options is None:
+            rc = self.lib.vifo_score(ref.ctypes.data, dist.ctypes.data, w, h,
+                                     int(bpc), op, _fp(sums), rp)
+        else:
+            o = make_options(options)
+            rc = self.lib.vifo_score_ex(ref.ctypes.data, dist.ctypes.data, w,
+                                        h, int(bpc), ctypes.byref(o), op,
+                                        _fp(sums), rp)
         if rc != 0:
             raise ValueError("vifo_score rejected its arguments (rc=%d)" % rc)
         if want_rows:
@@ -209,16 +284,16 @@ def log2_array(xs):
     return _load().log2_array(xs)
 
 
-def ratios(a, sv):
-    return _load().ratios(a, sv)
+def ratios(a, sv, nsq=None):
+    return _load().ratios(a, sv, nsq)
 
 
-def statistic(mu1, mu2, xx, yy, xy):
-    return _load().statistic(mu1, mu2, xx, yy, xy)
+def statistic(mu1, mu2, xx, yy, xy, nsq=None, gain_limit=None):
+    return _load().statistic(mu1, mu2, xx, yy, xy, nsq, gain_limit)
 
 
-def statistic_array(mu1, mu2, xx, yy, xy):
-    return _load().statistic_array(mu1, mu2, xx, yy, xy)
+def statistic_array(mu1, mu2, xx, yy, xy, nsq=None, gain_limit=None):
+    return _load().statistic_array(mu1, mu2, xx, yy, xy, nsq, gain_limit)
 
 
 def normalise(plane, bpc):
@@ -237,5 +312,5 @@ def total_rows(w, h):
     return _load().total_rows(w, h)
 
 
-def score(ref, dist, bpc, want_rows=False):
-    return _load().score(ref, dist, bpc, want_rows)
+def score(ref, dist, bpc, want_rows=False, options=None):
+    return _load().score(ref, dist, bpc, want_rows, options)

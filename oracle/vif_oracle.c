@@ -42,6 +42,11 @@ static const int kWidths[VIFO_NSCALES] = {17, 9, 5, 3};
 /* Noise variance vif_sigma_nsq, kept in binary64 [ADR-1422 Context]. */
 static const double kNsq = 2.0;
 
+/* Default enhancement gain limit.  Reading: the pages print no default for
+ * vif_enhn_gain_limit; the sibling ADM option's default is 100
+ * [Research-1434 Findings 1], and VIF takes the same. */
+static const double kGainLimit = 100.0;
+
 /* ---------------------------------------------------------------------- */
 /* O3  Gaussian taps [ADR-1422 Decision: taps computed at run time per
  * scale].  Reading: width N_s = 17/9/5/3, sigma_s = N_s / 5 (the published
@@ -118,26 +123,42 @@ void vifo_log2_array(const float *x, float *y, long n)
  * in fp64 and each rounded to fp32 once; ADR-1422 Decision lists the fp64
  * steps: the sum sv_sq + nsq, the quotient, the sum with one, the
  * conversion].  num_arg is the fp32 product (g*g)*sigma1_sq.              */
-float vifo_num_ratio(float num_arg, float sv_sq)
+float vifo_num_ratio_nsq(float num_arg, float sv_sq, double nsq)
 {
-    const double num_den = (double)sv_sq + kNsq;
+    const double num_den = (double)sv_sq + nsq;
     const double num_q = (double)num_arg / num_den;
     return (float)(1.0 + num_q);
 }
 
+float vifo_den_ratio_nsq(float sigma1_sq, double nsq)
+{
+    const double den_q = (double)sigma1_sq / nsq;
+    return (float)(1.0 + den_q);
+}
+
+float vifo_num_ratio(float num_arg, float sv_sq)
+{
+    return vifo_num_ratio_nsq(num_arg, sv_sq, kNsq);
+}
+
 float vifo_den_ratio(float sigma1_sq)
 {
-    const double den_q = (double)sigma1_sq / kNsq;
-    return (float)(1.0 + den_q);
+    return vifo_den_ratio_nsq(sigma1_sq, kNsq);
+}
+
+void vifo_ratio_arrays_nsq(const float *a, const float *sv, double nsq,
+                           float *num_out, float *den_out, long n)
+{
+    for (long i = 0; i < n; i++) {
+        num_out[i] = vifo_num_ratio_nsq(a[i], sv[i], nsq);
+        den_out[i] = vifo_den_ratio_nsq(a[i], nsq);
+    }
 }
 
 void vifo_ratio_arrays(const float *a, const float *sv, float *num_out,
                        float *den_out, long n)
 {
-    for (long i = 0; i < n; i++) {
-        num_out[i] = vifo_num_ratio(a[i], sv[i]);
-        den_out[i] = vifo_den_ratio(a[i]);
-    }
+    vifo_ratio_arrays_nsq(a, sv, kNsq, num_out, den_out, n);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -147,12 +168,20 @@ void vifo_ratio_arrays(const float *a, const float *sv, float *num_out,
  * Decision].  Reading: below it both terms are 1.0f.  Above it, the
  * published pixel-domain VIF rules in order: g = sigma12 / sigma1_sq,
  * sv_sq = sigma2_sq - g*sigma12; sigma2_sq < eps -> g = sv_sq = 0; g < 0 ->
- * sv_sq = sigma2_sq, g = 0; sv_sq >= eps.  Then the two one-plus-ratio
- * expressions in fp64, each rounded to fp32 once [ADR-1422 Context;
- * ADR-1422 Decision lists the sequence fl64(sv_sq + nsq), fp64 quotient,
- * fp64 sum, conversion to fp32], and log2f_approx of each.               */
-void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
-                    float *num_t, float *den_t)
+ * sv_sq = sigma2_sq, g = 0; sv_sq >= eps.  Reading for the option
+ * vif_enhn_gain_limit [ADR-1422 Consequences; ADR-1444 Consequences name
+ * it]: it bounds the gain where the gain enters the numerator, once sv_sq
+ * is settled, as C's MIN(g, limit) does with a double limit: the
+ * comparison in fp64, the limit rounded to fp32 when it is taken (so a NaN
+ * gain becomes the limit).  Then the two one-plus-ratio expressions in
+ * fp64, each rounded to fp32 once [ADR-1422 Context; ADR-1422 Decision
+ * lists the sequence fl64(sv_sq + nsq), fp64 quotient, fp64 sum,
+ * conversion to fp32], and log2f_approx of each.  Reading for nsq = 0: no
+ * special rule; IEEE 754 arithmetic throughout (a zero sigma1_sq then
+ * divides by zero), and log2f_approx reads whatever bits arrive.         */
+void vifo_statistic_ex(float mu1, float mu2, float xx, float yy, float xy,
+                       double nsq, double gain_limit, float *num_t,
+                       float *den_t)
 {
     const float eps = 1e-10f;
     const float mu1_sq = mu1 * mu1;
@@ -166,7 +195,7 @@ void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
     if (sigma2_sq < 0.0f)
         sigma2_sq = 0.0f;
 
-    if ((double)sigma1_sq < kNsq) {
+    if ((double)sigma1_sq < nsq) {
         *num_t = 1.0f;
         *den_t = 1.0f;
         return;
@@ -185,20 +214,37 @@ void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
     }
     if (sv_sq < eps)
         sv_sq = eps;
+    if (!((double)g < gain_limit))
+        g = (float)gain_limit;
 
     const float g_sq = g * g;
     const float num_arg = g_sq * sigma1_sq;
-    *num_t = vifo_log2(vifo_num_ratio(num_arg, sv_sq));
-    *den_t = vifo_log2(vifo_den_ratio(sigma1_sq));
+    *num_t = vifo_log2(vifo_num_ratio_nsq(num_arg, sv_sq, nsq));
+    *den_t = vifo_log2(vifo_den_ratio_nsq(sigma1_sq, nsq));
+}
+
+void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
+                    float *num_t, float *den_t)
+{
+    vifo_statistic_ex(mu1, mu2, xx, yy, xy, kNsq, kGainLimit, num_t, den_t);
+}
+
+void vifo_statistic_array_ex(const float *mu1, const float *mu2,
+                             const float *xx, const float *yy,
+                             const float *xy, double nsq, double gain_limit,
+                             float *num_t, float *den_t, long n)
+{
+    for (long i = 0; i < n; i++)
+        vifo_statistic_ex(mu1[i], mu2[i], xx[i], yy[i], xy[i], nsq,
+                          gain_limit, &num_t[i], &den_t[i]);
 }
 
 void vifo_statistic_array(const float *mu1, const float *mu2, const float *xx,
                           const float *yy, const float *xy, float *num_t,
                           float *den_t, long n)
 {
-    for (long i = 0; i < n; i++)
-        vifo_statistic(mu1[i], mu2[i], xx[i], yy[i], xy[i], &num_t[i],
-                       &den_t[i]);
+    vifo_statistic_array_ex(mu1, mu2, xx, yy, xy, kNsq, kGainLimit, num_t,
+                            den_t, n);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -329,19 +375,64 @@ int vifo_total_rows(int w, int h)
 }
 
 /* ---------------------------------------------------------------------- */
+/* Options.  Reading: the pages name vif_sigma_nsq, vif_enhn_gain_limit,
+ * vif_skip_scale0, vif_kernelscale and vif_scale1..3_min_val (default 0)
+ * [ADR-1422 Decision and Consequences; ADR-1444 Decision and Consequences]
+ * without defining them beyond their names; see vif_oracle.h for the
+ * meaning taken for each. */
+void vifo_default_options(vifo_options *o)
+{
+    o->sigma_nsq = kNsq;
+    o->enhn_gain_limit = kGainLimit;
+    o->kernelscale = 1.0;
+    o->scale_min_val[0] = 0.0;
+    o->scale_min_val[1] = 0.0;
+    o->scale_min_val[2] = 0.0;
+    o->skip_scale0 = 0;
+}
+
+static int options_valid(const vifo_options *o)
+{
+    if (!(o->sigma_nsq >= 0.0) || isinf(o->sigma_nsq))
+        return 0;
+    if (!(o->enhn_gain_limit >= 0.0))
+        return 0;
+    if (o->kernelscale != 1.0)
+        return 0;
+    for (int i = 0; i < 3; i++)
+        if (isnan(o->scale_min_val[i]))
+            return 0;
+    return o->skip_scale0 == 0 || o->skip_scale0 == 1;
+}
+
 /* O1-O11  whole feature for one frame pair.  Sums [ADR-1422 Context and
  * Decision]: each row's terms are added left to right into one fp32
  * accumulator starting at 0.0f; the row sums are added top to bottom into
  * one fp32 accumulator per scale.  Scores (reading): fp64 quotients of the
- * fp32 sums; num and den added over the scales in scale order in fp64.    */
+ * fp32 sums; num and den added over the scales in scale order in fp64.
+ * A skipped scale 0 (reading) still feeds the pyramid, has no statistic,
+ * zero sums and zero rows, and reports the score 0.  The floors of scales
+ * 1..3 (reading) act on the reported scores only: score < floor -> floor.
+ */
 int vifo_score(const void *ref, const void *dist, int w, int h, int bpc,
                double out[8], float sums[8], float *rowsums)
 {
-    if (ref == NULL || dist == NULL || out == NULL)
+    vifo_options o;
+    vifo_default_options(&o);
+    return vifo_score_ex(ref, dist, w, h, bpc, &o, out, sums, rowsums);
+}
+
+int vifo_score_ex(const void *ref, const void *dist, int w, int h, int bpc,
+                  const vifo_options *opt, double out[8], float sums[8],
+                  float *rowsums)
+{
+    if (ref == NULL || dist == NULL || out == NULL || opt == NULL)
         return -1;
     if (w < 16 || h < 16)
         return -1;
     if (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16)
+        return -1;
+    if (!options_valid(opt))
         return -1;
 
     const size_t n0 = (size_t)w * (size_t)h;
@@ -380,6 +471,17 @@ int vifo_score(const void *ref, const void *dist, int w, int h, int bpc,
             memcpy(X, Xn, sizeof(float) * (size_t)ws * hs);
             memcpy(Y, Yn, sizeof(float) * (size_t)ws * hs);
         }
+        if (s == 0 && opt->skip_scale0) {
+            if (rowsums != NULL)
+                for (int y = 0; y < hs; y++) {
+                    rowsums[2 * (row_base + y)] = 0.0f;
+                    rowsums[2 * (row_base + y) + 1] = 0.0f;
+                }
+            row_base += (size_t)hs;
+            N[0] = 0.0f;
+            D[0] = 0.0f;
+            continue;
+        }
         const size_t ns = (size_t)ws * (size_t)hs;
         for (size_t i = 0; i < ns; i++) {
             XX[i] = X[i] * X[i];
@@ -399,8 +501,9 @@ int vifo_score(const void *ref, const void *dist, int w, int h, int bpc,
             for (int x = 0; x < ws; x++) {
                 const size_t i = (size_t)y * ws + x;
                 float num_t, den_t;
-                vifo_statistic(mu1[i], mu2[i], fxx[i], fyy[i], fxy[i],
-                               &num_t, &den_t);
+                vifo_statistic_ex(mu1[i], mu2[i], fxx[i], fyy[i], fxy[i],
+                                  opt->sigma_nsq, opt->enhn_gain_limit,
+                                  &num_t, &den_t);
                 n_y = n_y + num_t;
                 d_y = d_y + den_t;
             }
@@ -418,6 +521,11 @@ int vifo_score(const void *ref, const void *dist, int w, int h, int bpc,
 
     for (int s = 0; s < VIFO_NSCALES; s++)
         out[s] = (double)N[s] / (double)D[s];
+    if (opt->skip_scale0)
+        out[0] = 0.0;
+    for (int s = 1; s < VIFO_NSCALES; s++)
+        if (out[s] < opt->scale_min_val[s - 1])
+            out[s] = opt->scale_min_val[s - 1];
     double num = 0.0, den = 0.0;
     num = (double)N[0] + (double)N[1];
     num = num + (double)N[2];

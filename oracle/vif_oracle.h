@@ -42,18 +42,51 @@ void vifo_log2_array(const float *x, float *y, long n);
 float vifo_num_ratio(float num_arg, float sv_sq);
 float vifo_den_ratio(float sigma1_sq);
 
+/* The same with the noise variance nsq as an argument. */
+float vifo_num_ratio_nsq(float num_arg, float sv_sq, double nsq);
+float vifo_den_ratio_nsq(float sigma1_sq, double nsq);
+
 /* vifo_num_ratio / vifo_den_ratio over arrays (den uses a only). */
 void vifo_ratio_arrays(const float *a, const float *sv, float *num_out,
                        float *den_out, long n);
+void vifo_ratio_arrays_nsq(const float *a, const float *sv, double nsq,
+                           float *num_out, float *den_out, long n);
 
-/* Per-pixel statistic: from the five filtered values to the two terms. */
+/* Per-pixel statistic: from the five filtered values to the two terms,
+ * with nsq = 2 and the gain limit 100. */
 void vifo_statistic(float mu1, float mu2, float xx, float yy, float xy,
                     float *num_t, float *den_t);
 
-/* vifo_statistic over n pixels given as five arrays. */
+/* The same with the noise variance and the enhancement gain limit given. */
+void vifo_statistic_ex(float mu1, float mu2, float xx, float yy, float xy,
+                       double nsq, double gain_limit, float *num_t,
+                       float *den_t);
+
+/* vifo_statistic / vifo_statistic_ex over n pixels given as five arrays. */
 void vifo_statistic_array(const float *mu1, const float *mu2, const float *xx,
                           const float *yy, const float *xy, float *num_t,
                           float *den_t, long n);
+void vifo_statistic_array_ex(const float *mu1, const float *mu2,
+                             const float *xx, const float *yy,
+                             const float *xy, double nsq, double gain_limit,
+                             float *num_t, float *den_t, long n);
+
+/* Options of the feature (readings of the option names the pages give).
+ *   sigma_nsq        noise variance, finite, >= 0 (default 2.0)
+ *   enhn_gain_limit  upper bound of the gain g where it enters the
+ *                    numerator, >= 0, may be +inf (default 100.0)
+ *   kernelscale      filter scale; only 1.0 (widths 17/9/5/3) is defined
+ *   scale_min_val    floors of the reported vif_scale1..3 (default 0.0)
+ *   skip_scale0      1: scale 0 has no statistic, zero sums, score 0 */
+typedef struct vifo_options {
+    double sigma_nsq;
+    double enhn_gain_limit;
+    double kernelscale;
+    double scale_min_val[3];
+    int skip_scale0;
+} vifo_options;
+
+void vifo_default_options(vifo_options *o);
 
 /* Sample normalisation of a w*h plane to fp32. */
 int vifo_normalise(const void *src, int w, int h, int bpc, float *dst);
@@ -79,9 +112,15 @@ int vifo_total_rows(int w, int h);
  *   out[7]    0.0 (reserved)
  *   sums      (optional) N_0, D_0, N_1, D_1, ..., N_3, D_3 as fp32
  *   rowsums   (optional) per scale, per row y: n_y, d_y (2 * total rows)
- * Requires w, h >= 16 and bpc in {8, 10, 12, 16}. */
+ * Requires w, h >= 16 and bpc in {8, 10, 12, 16}.  Default options. */
 int vifo_score(const void *ref, const void *dist, int w, int h, int bpc,
                double out[8], float sums[8], float *rowsums);
+
+/* vifo_score with options; returns -1 for options outside the ranges
+ * above. */
+int vifo_score_ex(const void *ref, const void *dist, int w, int h, int bpc,
+                  const vifo_options *opt, double out[8], float sums[8],
+                  float *rowsums);
 
 #ifdef __cplusplus
 }

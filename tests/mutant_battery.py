@@ -16,6 +16,7 @@ sys.path.insert(0, HERE)
 
 import oracle  # noqa: E402
 import test_oracle_pins as P  # noqa: E402
+import test_oracle_options as Q  # noqa: E402
 
 
 def battery(orc):
@@ -57,7 +58,44 @@ def battery(orc):
         ("log2_e5", lambda: P.test_log2_other_binades(orc, 5)),
         ("pipe1", lambda: P.test_pipeline_vs_fp64_definition(orc, (32, 32), 1)),
         ("pipe3", lambda: P.test_pipeline_vs_fp64_definition(orc, (41, 73), 3)),
+        ("opt_default", lambda: Q.test_default_options_equal_default_entry(orc)),
+        ("opt_huge_nsq",
+         lambda: Q.test_huge_nsq_puts_every_pixel_in_the_low_branch(orc)),
+        ("opt_zero_nsq", lambda: Q.test_zero_nsq_follows_ieee_arithmetic(orc)),
+        ("opt_gain0",
+         lambda: Q.test_zero_gain_limit_zeroes_every_high_branch_numerator(
+             orc)),
+        ("opt_gain_mono",
+         lambda: Q.test_gain_limit_is_monotone_and_idle_above_the_largest_gain(
+             orc)),
+        ("opt_gain_self",
+         lambda: Q.test_gain_limit_one_leaves_identical_frames_alone(orc)),
+        ("opt_skip", lambda: Q.test_skip_scale0(orc)),
+        ("opt_floors",
+         lambda: Q.test_scale_floors_act_on_reported_scores_only(orc)),
     ]
+    for nsq in (2.0, 4.7):
+        cases.append(("opt_thr%g" % nsq,
+                      lambda v=nsq: Q.test_nsq_threshold_is_an_fp64_comparison(
+                          orc, v)))
+    for nsq in (1.5, 4.7):
+        cases.append(("opt_num%g" % nsq,
+                      lambda v=nsq:
+                      Q.test_num_ratio_with_nsq_vs_extended_precision(orc, v)))
+        cases.append(("opt_den%g" % nsq,
+                      lambda v=nsq:
+                      Q.test_den_ratio_with_nsq_vs_extended_precision(orc, v)))
+    for nsq, lim in ((2.0, 0.3), (4.7, 1.0), (0.5, 0.05)):
+        cases.append(("opt_stat%g_%g" % (nsq, lim),
+                      lambda v=nsq, l=lim:
+                      Q.test_statistic_with_options_vs_fp64_formula(orc, v, l)))
+    cases.append(("opt_pipe", lambda:
+                  Q.test_pipeline_with_options_vs_fp64_definition(orc, 4.7,
+                                                                  0.8)))
+    for opt in ({"kernelscale": 2.0}, {"sigma_nsq": -1.0},
+                {"enhn_gain_limit": -0.5}):
+        cases.append(("opt_bad_%s" % list(opt)[0],
+                      lambda o=opt: Q.test_bad_options_rejected(orc, o)))
     return cases
 
 

@@ -22,7 +22,14 @@ SRC = os.path.join(ROOT, "oracle", "vif_oracle.c")
 # clamp of sigma1_sq at zero, an equivalent mutant (a negative sigma1_sq
 # takes the low-variance branch either way, so no output can change), and
 # evaluating the denominator ratio in fp32 as 1.0f + sigma1_sq * 0.5f, which
-# is provably the same value (see test_den_ratio_closed_form).
+# is provably the same value (see test_den_ratio_closed_form); and comparing
+# the gain with fl32(limit) in fp32 in place of the fp64 comparison, which
+# selects the same value for every limit (no fp32 value lies strictly
+# between a limit and its nearest fp32, so the two comparisons can differ
+# only where g is that fp32 value, and then both results are it); and
+# letting a NaN gain pass the limit: a NaN gain comes only from 0/0, which
+# makes sv_sq NaN as well unless the sigma2_sq rule resets both, so the
+# numerator quotient is NaN whatever the gain is.
 MUTANTS = [
     ("sigma_n_over_6", "(double)n / 5.0", "(double)n / 6.0"),
     ("taps_unnormalised", "taps[k] = (float)(g[k] / sum);",
@@ -52,18 +59,18 @@ MUTANTS = [
      "const float sigma12 = mu1_mu2 - xy;"),
     ("sigma2_no_mean", "float sigma2_sq = yy - mu2_sq;",
      "float sigma2_sq = yy;"),
-    ("threshold_1", "if ((double)sigma1_sq < kNsq) {",
+    ("threshold_1", "if ((double)sigma1_sq < nsq) {",
      "if ((double)sigma1_sq < 1.0) {"),
-    ("threshold_le", "if ((double)sigma1_sq < kNsq) {",
-     "if ((double)sigma1_sq <= kNsq) {"),
+    ("threshold_le", "if ((double)sigma1_sq < nsq) {",
+     "if ((double)sigma1_sq <= nsq) {"),
     ("low_branch_num_0", "        *num_t = 1.0f;\n", "        *num_t = 0.0f;\n"),
-    ("no_nsq_in_num", "(double)sv_sq + kNsq;", "(double)sv_sq + 1.0;"),
+    ("no_nsq_in_num", "(double)sv_sq + nsq;", "(double)sv_sq + 1.0;"),
     ("nsq_fp32_num", "const double num_q = (double)num_arg / num_den;",
      "const double num_q = (double)(num_arg / (float)num_den);"),
     ("num_single_rounding_fp32", "return (float)(1.0 + num_q);",
      "return 1.0f + (float)num_q;"),
-    ("den_ratio_inverted", "const double den_q = (double)sigma1_sq / kNsq;",
-     "const double den_q = kNsq / (double)sigma1_sq;"),
+    ("den_ratio_inverted", "const double den_q = (double)sigma1_sq / nsq;",
+     "const double den_q = nsq / (double)sigma1_sq;"),
     ("no_negative_gain_rule", "if (g < 0.0f) {", "if (g < -1e30f) {"),
     ("sv_floor_1", "if (sv_sq < eps)\n        sv_sq = eps;",
      "if (sv_sq < 1.0f)\n        sv_sq = 1.0f;"),
@@ -78,6 +85,32 @@ MUTANTS = [
      "num = (double)N[0] + (double)N[0];"),
     ("score_inverted", "out[s] = (double)N[s] / (double)D[s];",
      "out[s] = (double)D[s] / (double)N[s];"),
+    # the option surface
+    ("nsq_threshold_fp32", "if ((double)sigma1_sq < nsq) {",
+     "if (sigma1_sq < (float)nsq) {"),
+    ("num_nsq_fixed", "(double)sv_sq + nsq;", "(double)sv_sq + kNsq;"),
+    ("den_nsq_fixed", "(double)sigma1_sq / nsq;", "(double)sigma1_sq / kNsq;"),
+    ("gain_limit_ignored", "if (!((double)g < gain_limit))", "if (0)"),
+    ("gain_limit_as_floor", "if (!((double)g < gain_limit))",
+     "if ((double)g < gain_limit)"),
+    ("gain_limit_before_sv",
+     "    float g = sigma12 / sigma1_sq;\n",
+     "    float g = sigma12 / sigma1_sq;\n"
+     "    if (!((double)g < gain_limit))\n"
+     "        g = (float)gain_limit;\n"),
+    ("gain_limit_squared_twice", "const float g_sq = g * g;",
+     "const float g_sq = (g < (float)gain_limit ? g * g : g);"),
+    ("skip_wrong_scale", "if (s == 0 && opt->skip_scale0) {",
+     "if (s == 1 && opt->skip_scale0) {"),
+    ("skip_keeps_score0", "        out[0] = 0.0;\n", "        out[0] = out[0];\n"),
+    ("skip_rows_kept", "rowsums[2 * (row_base + y)] = 0.0f;",
+     "rowsums[2 * (row_base + y)] = 1.0f;"),
+    ("floor_wrong_scale", "if (out[s] < opt->scale_min_val[s - 1])",
+     "if (out[s] < opt->scale_min_val[s % 3])"),
+    ("floor_as_cap", "if (out[s] < opt->scale_min_val[s - 1])",
+     "if (out[s] > opt->scale_min_val[s - 1])"),
+    ("kernelscale_unchecked", "if (o->kernelscale != 1.0)\n        return 0;",
+     "if (o->kernelscale != o->kernelscale)\n        return 0;"),
 ]
 
 

@@ -525,9 +525,10 @@ def test_log2_coefficients_are_the_fit(orc):
 
 # ------------------------------------------------------ whole pipeline fp64
 
-def _vif_fp64(ref, dist, bpc):
+def _vif_fp64(ref, dist, bpc, nsq=2.0, gain_limit=np.inf):
     """The whole definition in real (fp64) arithmetic with exact log2 and
-    numpy reflection padding: no fp32 rounding anywhere except the taps."""
+    numpy reflection padding: no fp32 rounding anywhere except the taps.
+    The gain limit bounds g where it enters the numerator."""
     div = 2.0 ** (bpc - 8)
     X = ref.astype(np.float64) / div
     Y = dist.astype(np.float64) / div
@@ -543,8 +544,8 @@ def _vif_fp64(ref, dist, bpc):
         s1 = np.maximum(_conv_fp64(X * X, t) - mu1 * mu1, 0)
         s2 = np.maximum(_conv_fp64(Y * Y, t) - mu2 * mu2, 0)
         s12 = _conv_fp64(X * Y, t) - mu1 * mu2
-        hi = s1 >= 2.0
-        near = np.abs(s1 - 2.0) < 1e-3
+        hi = s1 >= nsq
+        near = np.abs(s1 - nsq) < 1e-3
         assert not near.any()
         with np.errstate(divide="ignore", invalid="ignore"):
             g = np.where(hi, s12 / np.where(hi, s1, 1), 0)
@@ -556,8 +557,9 @@ def _vif_fp64(ref, dist, bpc):
         sv = np.where(neg, s2, sv)
         g = np.where(neg, 0, g)
         sv = np.maximum(sv, 1e-10)
-        num = np.where(hi, np.log2(1 + g * g * s1 / (sv + 2.0)), 1.0)
-        den = np.where(hi, np.log2(1 + s1 / 2.0), 1.0)
+        g = np.minimum(g, gain_limit)
+        num = np.where(hi, np.log2(1 + g * g * s1 / (sv + nsq)), 1.0)
+        den = np.where(hi, np.log2(1 + s1 / nsq), 1.0)
         N.append(num.sum())
         D.append(den.sum())
     out = [N[s] / D[s] for s in range(4)]
