@@ -46,6 +46,48 @@ extern "C" {
 typedef struct vif_ctx vif_ctx;
 
 /*
+ * Options of the feature.  The pages name them -- vif_sigma_nsq,
+ * vif_enhn_gain_limit, vif_skip_scale0, the floors vif_scale1..3_min_val
+ * (default 0) and the tap generator's vif_kernelscale (ADR-1422, Decision
+ * and Consequences; ADR-1444, Decision and Consequences) -- but print no
+ * arithmetic for them.  The meaning taken for each:
+ *   sigma_nsq        noise variance of the statistic, a double: the branch
+ *                    sigma1_sq < nsq (compared in fp64) and both
+ *                    one-plus-ratio expressions use it.  Finite, >= 0;
+ *                    default 2.0.  At 0 nothing is special-cased: IEEE
+ *                    arithmetic (a zero sigma1_sq divides by zero) and the
+ *                    log2 polynomial reads the bits that arrive (exponent
+ *                    field 255 counts as 128).
+ *   enhn_gain_limit  bound of the gain g where it enters the numerator,
+ *                    once sv_sq is settled: g = MIN(g, limit) as C computes
+ *                    it with a double limit (fp64 comparison, the limit
+ *                    rounded to fp32).  >= 0, may be +inf; default 100.0,
+ *                    the default of the sibling ADM option (Research-1434,
+ *                    Findings 1).  On samples in range no gain reaches 91,
+ *                    so the default never binds.
+ *   kernelscale      filter scale of the tap generator; only 1.0 (widths
+ *                    17/9/5/3) is defined.
+ *   scale_min_val    floors of the reported vif_scale1..3: a score below its
+ *                    floor is replaced by the floor.  Sums, num, den and the
+ *                    ratio are not floored.  Not NaN; default 0.0.
+ *   skip_scale0      0 or 1.  1: scale 0 still feeds the pyramid but
+ *                    contributes nothing: N_0 = D_0 = 0, its row sums read 0
+ *                    and vif_scale0 reports 0.0.
+ *   reserved         must be 0.
+ */
+typedef struct vif_options {
+  double sigma_nsq;
+  double enhn_gain_limit;
+  double kernelscale;
+  double scale_min_val[3];
+  int skip_scale0;
+  int reserved;
+} vif_options;
+
+/* vif_default_options -- fills *opt with the defaults above.  NULL-safe. */
+void vif_default_options(vif_options *opt);
+
+/*
  * vif_create -- a scoring context for frames of w x h samples at bpc bits.
  *   w, h   >= VIF_MIN_SIDE and w * h <= VIF_MAX_PIXELS.  The pages' smallest
  *          scored frame is 16x16 (ADR-1444, Consequences).
@@ -59,6 +101,16 @@ typedef struct vif_ctx vif_ctx;
  * never in the middle of a frame.
  */
 vif_ctx *vif_create(int w, int h, int bpc);
+
+/*
+ * vif_create_ex -- vif_create with options (NULL: the defaults, the same as
+ * vif_create).  The options are copied.  VIF_EINVAL for options outside the
+ * ranges of vif_options.
+ */
+vif_ctx *vif_create_ex(int w, int h, int bpc, const vif_options *opt);
+
+/* vif_get_options -- copies the context's options to *opt. */
+int vif_get_options(const vif_ctx *ctx, vif_options *opt);
 
 /*
  * vif_score -- score one frame pair.
@@ -121,6 +173,21 @@ int vif_set_stream(vif_ctx *ctx, void *hip_stream);
  * VIF_EINVAL if no frame has been returned yet.
  */
 int vif_get_sums(const vif_ctx *ctx, float sums[8]);
+
+/*
+ * vif_get_debug -- the values of the pages' debug mode (ADR-1444,
+ * Consequences, and ADR-1422, Consequences: fifteen values, the scores with
+ * the frame ratio and all eight per-scale sums) for the last frame returned
+ * by vif_score or vif_collect, as doubles:
+ *   [0..3]   vif_scale0..3, as in out[0..3] (floors applied)
+ *   [4]      vif, the frame ratio num / den (out[6])
+ *   [5], [6] num and den (out[4], out[5])
+ *   [7..14]  N_0, D_0, N_1, D_1, N_2, D_2, N_3, D_3 (the fp32 sums, exact
+ *            in fp64)
+ * VIF_EINVAL if no frame has been returned yet.
+ */
+#define VIF_NDEBUG 15
+int vif_get_debug(const vif_ctx *ctx, double out[VIF_NDEBUG]);
 
 /*
  * vif_get_row_sums -- the per-row fp32 sums of the last frame returned by

@@ -14,7 +14,7 @@
  * Every pointer is a DEVICE pointer owned by the caller; n >= 0 elements;
  * stream is a hipStream_t as void* (NULL = default stream).  Each call is
  * synchronous (it waits for its kernel).  Returns VIF_OK or VIF_EINVAL (NULL
- * pointer, n < 0) or VIF_EHIP.
+ * pointer, n < 0, an option out of range) or VIF_EHIP.
  */
 #ifndef VIF_SELFTEST_H
 #define VIF_SELFTEST_H
@@ -43,16 +43,22 @@ int vif_selftest_div32(const float *a, const float *b, long n, float *q,
 /* y[i] = the kernels' log2 polynomial of x[i] (x[i] finite, >= 1). */
 int vif_selftest_log2(const float *x, long n, float *y, void *stream);
 
-/* The kernels' one-plus-ratio values with the built-in noise variance 2.0:
- *   num[i] = fl32(1 + a[i] / (sv[i] + 2)),  den[i] = fl32(1 + a[i] / 2). */
-int vif_selftest_ratios(const float *a, const float *sv, long n, float *num,
-                        float *den, void *stream);
+/* The kernels' one-plus-ratio values for the noise variance nsq (finite,
+ * >= 0, as vif_options.sigma_nsq; else VIF_EINVAL), each through fp64 and
+ * one rounding to fp32:
+ *   num[i] = fl32(1 + a[i] / (sv[i] + nsq)),  den[i] = fl32(1 + a[i] / nsq).
+ * A power-of-two nsq takes the kernels' exact-reciprocal path. */
+int vif_selftest_ratios(const float *a, const float *sv, double nsq, long n,
+                        float *num, float *den, void *stream);
 
 /* The kernels' per-pixel statistic: from the five filtered values
- * (mu1, mu2, xx, yy, xy, each an array of n floats) to the two terms. */
+ * (mu1, mu2, xx, yy, xy, each an array of n floats) to the two terms, with
+ * the noise variance nsq and the enhancement gain limit gain_limit in the
+ * ranges of vif_options (else VIF_EINVAL). */
 int vif_selftest_statistic(const float *mu1, const float *mu2,
                            const float *xx, const float *yy, const float *xy,
-                           long n, float *num, float *den, void *stream);
+                           long n, double nsq, double gain_limit, float *num,
+                           float *den, void *stream);
 
 #ifdef __cplusplus
 }

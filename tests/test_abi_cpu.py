@@ -65,6 +65,64 @@ def test_create_rejects_bad_arguments(lib, w, h, bpc):
     assert _lib.vif_errno() == _lib.VIF_EINVAL
 
 
+def test_default_options(lib):
+    from vif_image_fidelity_amd import _lib
+    import vif_image_fidelity_amd as V
+    o = _lib.vif_default_options()
+    assert (o.sigma_nsq, o.enhn_gain_limit, o.kernelscale) == (2.0, 100.0,
+                                                               1.0)
+    assert tuple(o.scale_min_val) == (0.0, 0.0, 0.0)
+    assert (o.skip_scale0, o.reserved) == (0, 0)
+    m = V.make_options({})
+    for f, _ in _lib.VifOptions._fields_:
+        a, b = getattr(o, f), getattr(m, f)
+        if f == "scale_min_val":
+            a, b = tuple(a), tuple(b)
+        assert a == b, f
+    _lib.load().vif_default_options(None)  # NULL-safe
+
+
+@pytest.mark.parametrize("opt", [{"kernelscale": 2.0}, {"kernelscale": 0.0},
+                                 {"sigma_nsq": -1e-9},
+                                 {"sigma_nsq": float("nan")},
+                                 {"sigma_nsq": float("inf")},
+                                 {"enhn_gain_limit": -1.0},
+                                 {"enhn_gain_limit": float("nan")},
+                                 {"scale_min_val": (0.0, 0.0, float("nan"))},
+                                 {"skip_scale0": 2}, {"skip_scale0": -1}])
+def test_create_ex_rejects_bad_options(lib, opt):
+    """Options outside their ranges are refused at create time, before any
+    device call (so this runs without a GPU)."""
+    from vif_image_fidelity_amd import _lib
+    import vif_image_fidelity_amd as V
+    ctx = _lib.vif_create_ex(64, 64, 8, V.make_options(opt))
+    assert not ctx
+    assert _lib.vif_errno() == _lib.VIF_EINVAL
+
+
+def test_create_ex_rejects_reserved_field(lib):
+    from vif_image_fidelity_amd import _lib
+    o = _lib.vif_default_options()
+    o.reserved = 1
+    assert not _lib.vif_create_ex(64, 64, 8, o)
+    assert _lib.vif_errno() == _lib.VIF_EINVAL
+
+
+def test_options_struct_layout(lib):
+    """The ctypes mirror of struct vif_options has the C layout (six
+    doubles, two ints: 56 bytes, no padding)."""
+    import ctypes
+    from vif_image_fidelity_amd import _lib
+    assert ctypes.sizeof(_lib.VifOptions) == 56
+    assert _lib.VifOptions.skip_scale0.offset == 48
+
+
+def test_unknown_option_rejected(lib):
+    import vif_image_fidelity_amd as V
+    with pytest.raises(ValueError):
+        V.make_options({"nsq": 1.0})
+
+
 def test_null_handling(lib):
     from vif_image_fidelity_amd import _lib
     out = np.zeros(8)
@@ -75,6 +133,8 @@ def test_null_handling(lib):
     assert _lib.vif_submit(None, 1, 1) == _lib.VIF_EINVAL
     assert _lib.vif_collect(None, out) == _lib.VIF_EINVAL
     assert _lib.vif_pending(None) == _lib.VIF_EINVAL
+    assert _lib.vif_get_debug(None, np.zeros(15)) == _lib.VIF_EINVAL
+    assert _lib.vif_get_options(None, _lib.VifOptions()) == _lib.VIF_EINVAL
     _lib.vif_destroy(None)  # no-op
 
 
@@ -117,6 +177,7 @@ def test_package_import_needs_no_gpu():
     assert V.VIF_OK == 0
     assert len(V.KERNEL_KINDS) == 5
     assert V.QUEUE_DEPTH == 3
+    assert len(V.DEBUG_NAMES) == 15 and V.DEBUG_NAMES[4] == "vif"
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

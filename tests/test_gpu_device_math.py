@@ -124,25 +124,42 @@ def test_log2_exhaustive_bitwise(dev, orc):
         assert np.array_equal(_h(y).view(np.uint32), ref.view(np.uint32)), e
 
 
-def test_ratios_bitwise(dev, orc):
+def _same_bits_or_both_nan(x, y):
+    """Bitwise equality, except that NaNs compare by being NaN: the host's
+    default NaN has the sign bit set, the device's does not, and nothing
+    downstream reads a NaN's sign (the log2 polynomial masks it)."""
+    nx, ny = np.isnan(x), np.isnan(y)
+    return (np.array_equal(nx, ny)
+            and np.array_equal(x[~nx].view(np.uint32),
+                               y[~ny].view(np.uint32)))
+
+
+@pytest.mark.parametrize("nsq", [2.0, 1.5, 4.7, 0.5, 4.0, 1e-3, 0.0])
+def test_ratios_bitwise(dev, orc, nsq):
+    """Both one-plus-ratio values for the default noise variance, for
+    values that are not powers of two (the division path), for powers of two
+    (the exact-reciprocal path) and for zero (IEEE division by zero)."""
     import torch
     from vif_image_fidelity_amd import _lib
     g = np.random.Generator(np.random.PCG64(32))
-    n = 1 << 22
+    n = 1 << 22 if nsq == 2.0 else 1 << 20
     a = np.exp(g.uniform(np.log(1e-6), np.log(5e8), n)).astype(np.float32)
     sv = np.exp(g.uniform(np.log(1e-10), np.log(1e5), n)).astype(np.float32)
-    ta, tb = _near_ties(g, 1 << 18, 2.0)
+    a[:64] = 0.0
+    ta, tb = _near_ties(g, 1 << 18, max(nsq, 1e-3))
     a = np.concatenate([a, ta])
     sv = np.concatenate([sv, tb])
     num = torch.empty(a.size, dtype=torch.float32, device="cuda:0")
     den = torch.empty_like(num)
     da, dsv = _d(a), _d(sv)
     _check(_lib.load().vif_selftest_ratios(da.data_ptr(), dsv.data_ptr(),
-                                           a.size, num.data_ptr(),
+                                           nsq, a.size, num.data_ptr(),
                                            den.data_ptr(), None))
-    rn, rd = orc.ratios(a, sv)
-    assert np.array_equal(_h(num).view(np.uint32), rn.view(np.uint32))
-    assert np.array_equal(_h(den).view(np.uint32), rd.view(np.uint32))
+    rn, rd = orc.ratios(a, sv, nsq=nsq)
+    assert _same_bits_or_both_nan(_h(num), rn)
+    assert _same_bits_or_both_nan(_h(den), rd)
+    if nsq == 0.0:
+        assert np.isnan(rd[a == 0]).all() and np.isinf(rd[a > 0]).all()
 
 
 def _statistic_inputs(g, n):
@@ -163,22 +180,47 @@ def _statistic_inputs(g, n):
     return mu1, mu2, xx, yy, xy
 
 
-def test_statistic_bitwise(dev, orc):
+@pytest.mark.parametrize("nsq,limit", [(2.0, 100.0), (4.7, 1.0),
+                                       (1.5, 0.3), (0.5, np.inf),
+                                       (2.0, 0.0), (0.0, 100.0)])
+def test_statistic_bitwise(dev, orc, nsq, limit):
+    """The whole per-pixel statistic against the oracle's, for the default
+    options and for noise variances and gain limits that take every path:
+    the division and reciprocal paths of the denominator, a binding gain
+    limit, a zero limit, and nsq = 0 (zero variances divide by zero)."""
     import torch
     from vif_image_fidelity_amd import _lib
     g = np.random.Generator(np.random.PCG64(33))
-    n = 1 << 22
+    n = 1 << 22 if (nsq, limit) == (2.0, 100.0) else 1 << 20
     ins = _statistic_inputs(g, n)
     dins = [_d(a) for a in ins]
     num = torch.empty(n, dtype=torch.float32, device="cuda:0")
     den = torch.empty_like(num)
     _check(_lib.load().vif_selftest_statistic(
-        *[t.data_ptr() for t in dins], n, num.data_ptr(), den.data_ptr(),
-        None))
-    rn, rd = orc.statistic_array(*ins)
+        *[t.data_ptr() for t in dins], n, nsq, limit, num.data_ptr(),
+        den.data_ptr(), None))
+    rn, rd = orc.statistic_array(*ins, nsq=nsq, gain_limit=limit)
     assert np.array_equal(_h(num).view(np.uint32), rn.view(np.uint32))
     assert np.array_equal(_h(den).view(np.uint32), rd.view(np.uint32))
     # the sample really exercises both branches and every clamp
     hi = rd != 1.0
-    assert 0.2 < hi.mean() < 0.95
-    assert (rn[hi] == 0).any()
+    if nsq > 0:
+        assert 0.2 < hi.mean() < 0.95
+        assert (rn[hi] == 0).any()
+    else:
+        assert (rd >= 128.0).any()      # sigma1_sq / 0 reached the log2
+    if 0 < limit < 10:
+        un, _ = orc.statistic_array(*ins, nsq=nsq, gain_limit=np.inf)
+        assert (un > rn).any()          # the limit binds somewhere
+
+
+def test_selftests_reject_bad_options(dev):
+    from vif_image_fidelity_amd import _lib
+    L = _lib.load()
+    for nsq, lim in ((-1.0, 100.0), (np.nan, 100.0), (np.inf, 100.0),
+                     (2.0, -1.0), (2.0, np.nan)):
+        assert L.vif_selftest_statistic(None, None, None, None, None, 0, nsq,
+                                        lim, None, None, None) == \
+            _lib.VIF_EINVAL
+    assert L.vif_selftest_ratios(None, None, -2.0, 0, None, None, None) == \
+        _lib.VIF_EINVAL

@@ -85,6 +85,68 @@ EDGE_SHAPES = [(16, 16), (17, 16), (16, 17), (112, 16), (113, 17), (224, 32),
                (129, 97), (1000, 37), (37, 1000), (3841, 33)]
 
 
+OPTION_SETS = [
+    {"sigma_nsq": 4.7},
+    {"sigma_nsq": 1.5, "enhn_gain_limit": 1.0},
+    {"sigma_nsq": 0.5, "enhn_gain_limit": 0.25},
+    {"sigma_nsq": 0.0},
+    {"enhn_gain_limit": 0.0},
+    {"skip_scale0": 1},
+    {"scale_min_val": (0.999, 0.5, 2.0)},
+    {"sigma_nsq": 4.7, "enhn_gain_limit": 1.2, "skip_scale0": 1,
+     "scale_min_val": (0.9, 0.0, 1.5)},
+]
+
+
+@pytest.mark.parametrize("opt", OPTION_SETS,
+                         ids=["o%d" % i for i in range(len(OPTION_SETS))])
+def test_options_parity(V, orc, opt):
+    """Every option of struct vif_options against the oracle's reading of
+    it, bit for bit (out[8], sums, rows, and the fifteen debug values), on
+    the 576x324 8-bit workload's first frame, a bright 16-bit frame and a
+    ragged 8-bit frame with a flat region (zero variances, where nsq = 0
+    divides by zero)."""
+    from vif_image_fidelity_amd import synth
+    ref0, dist0, bpc0 = synth.WORKLOADS["netflix_576x324_8bit"]()[0]
+    g = np.random.Generator(np.random.PCG64(77))
+    wide = g.integers(40000, 65536, size=(70, 130)).astype(np.uint16)
+    wdist = np.clip(wide.astype(np.int64) + g.integers(-3000, 3000,
+                                                       size=wide.shape),
+                    0, 65535).astype(np.uint16)
+    flat = g.integers(0, 256, size=(61, 203)).astype(np.uint8)
+    flat[10:50, 20:120] = 77
+    fdist = flat.copy()
+    fdist[:, 150:] = np.clip(fdist[:, 150:].astype(int) + 9, 0, 255)
+    for ref, dist, bpc, label in ((ref0, dist0, bpc0, "netflix"),
+                                  (wide, wdist, 16, "bright16"),
+                                  (flat, fdist, 8, "flat")):
+        h, w = ref.shape
+        print("options case %s %s" % (label, opt), flush=True)
+        with V.Vif(w, h, bpc, options=opt) as ctx:
+            got = ctx.score(to_device(ref), to_device(dist))
+            gsums, grows, gdbg = ctx.sums(), ctx.row_sums(), ctx.debug()
+            back = ctx.options()
+        exp, esums, erows = orc.score(ref, dist, bpc, want_rows=True,
+                                      options=opt)
+        assert got.view(np.uint64).tolist() == exp.view(np.uint64).tolist(), \
+            (label, got, exp)
+        assert gsums.view(np.uint32).tolist() == esums.view(np.uint32).tolist()
+        assert np.array_equal(grows.view(np.uint32), erows.view(np.uint32))
+        want = list(exp[:4]) + [exp[6], exp[4], exp[5]] + \
+            [float(v) for v in esums]
+        assert [gdbg[k] for k in V.DEBUG_NAMES] == want
+        for k, v in opt.items():
+            assert back[k] == (tuple(v) if k == "scale_min_val" else v)
+
+
+@pytest.mark.parametrize("opt", [{"kernelscale": 2.0}, {"sigma_nsq": -1.0},
+                                 {"enhn_gain_limit": float("nan")},
+                                 {"skip_scale0": 3}])
+def test_bad_options_refused(V, opt):
+    with pytest.raises(V.VifError):
+        V.Vif(64, 64, 8, options=opt)
+
+
 @pytest.mark.parametrize("wh", EDGE_SHAPES)
 def test_edge_geometry_parity(V, orc, wh):
     w, h = wh

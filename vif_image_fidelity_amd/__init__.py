@@ -14,10 +14,38 @@ import numpy as np
 
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
-                   KERNEL_KINDS, QUEUE_DEPTH)
+                   DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH)
 
-__all__ = ["Vif", "VifError", "taps", "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM",
-           "VIF_EHIP", "KERNEL_KINDS", "QUEUE_DEPTH"]
+__all__ = ["Vif", "VifError", "taps", "make_options", "DEFAULT_OPTIONS",
+           "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
+           "KERNEL_KINDS", "QUEUE_DEPTH"]
+
+# Defaults of struct vif_options (include/vif.h states each option's
+# meaning and range).
+DEFAULT_OPTIONS = {"sigma_nsq": 2.0, "enhn_gain_limit": 100.0,
+                   "kernelscale": 1.0, "scale_min_val": (0.0, 0.0, 0.0),
+                   "skip_scale0": 0}
+
+
+def make_options(options=None):
+    """A struct vif_options from a dict of overrides of DEFAULT_OPTIONS."""
+    d = dict(DEFAULT_OPTIONS)
+    if options:
+        unknown = set(options) - set(d)
+        if unknown:
+            raise ValueError("unknown options %s" % sorted(unknown))
+        d.update(options)
+    o = _lib.VifOptions()
+    o.sigma_nsq = float(d["sigma_nsq"])
+    o.enhn_gain_limit = float(d["enhn_gain_limit"])
+    o.kernelscale = float(d["kernelscale"])
+    floors = [float(v) for v in d["scale_min_val"]]
+    if len(floors) != 3:
+        raise ValueError("scale_min_val needs three floors")
+    o.scale_min_val[:] = floors
+    o.skip_scale0 = int(d["skip_scale0"])
+    o.reserved = 0
+    return o
 
 
 def taps(scale):
@@ -42,11 +70,16 @@ def _ptr(x):
 
 
 class Vif:
-    """One scoring context for w x h frames of bpc bits (8, 10, 12, 16)."""
+    """One scoring context for w x h frames of bpc bits (8, 10, 12, 16).
+    options: None or a dict of overrides of DEFAULT_OPTIONS."""
 
-    def __init__(self, w, h, bpc, stream=None):
+    def __init__(self, w, h, bpc, stream=None, options=None):
         self.w, self.h, self.bpc = int(w), int(h), int(bpc)
-        ctx = _lib.vif_create(self.w, self.h, self.bpc)
+        if options is None:
+            ctx = _lib.vif_create(self.w, self.h, self.bpc)
+        else:
+            ctx = _lib.vif_create_ex(self.w, self.h, self.bpc,
+                                     make_options(options))
         if not ctx:
             raise VifError(_lib.vif_errno(), "vif_create")
         self._ctx = ctx
@@ -108,6 +141,27 @@ class Vif:
         if rc != VIF_OK:
             raise VifError(rc, "vif_get_sums")
         return s
+
+    def options(self):
+        """The context's options as a dict."""
+        o = _lib.VifOptions()
+        rc = _lib.vif_get_options(self._ctx, o)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_get_options")
+        return {"sigma_nsq": o.sigma_nsq,
+                "enhn_gain_limit": o.enhn_gain_limit,
+                "kernelscale": o.kernelscale,
+                "scale_min_val": tuple(o.scale_min_val),
+                "skip_scale0": o.skip_scale0}
+
+    def debug(self):
+        """The fifteen debug values of the last frame, {name: value} in
+        DEBUG_NAMES order."""
+        out = np.zeros(_lib.NDEBUG, dtype=np.float64)
+        rc = _lib.vif_get_debug(self._ctx, out)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_get_debug")
+        return dict(zip(DEBUG_NAMES, out.tolist()))
 
     def row_sums(self):
         rows = np.zeros((self.total_rows, 2), dtype=np.float32)

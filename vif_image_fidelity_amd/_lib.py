@@ -17,7 +17,23 @@ VIF_EHIP = -3
 NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
+NDEBUG = 15
 KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
+DEBUG_NAMES = ("vif_scale0", "vif_scale1", "vif_scale2", "vif_scale3",
+               "vif", "vif_num", "vif_den",
+               "vif_num_scale0", "vif_den_scale0", "vif_num_scale1",
+               "vif_den_scale1", "vif_num_scale2", "vif_den_scale2",
+               "vif_num_scale3", "vif_den_scale3")
+
+
+class VifOptions(ctypes.Structure):
+    """struct vif_options of include/vif.h."""
+    _fields_ = [("sigma_nsq", ctypes.c_double),
+                ("enhn_gain_limit", ctypes.c_double),
+                ("kernelscale", ctypes.c_double),
+                ("scale_min_val", ctypes.c_double * 3),
+                ("skip_scale0", ctypes.c_int),
+                ("reserved", ctypes.c_int)]
 
 _lib = None
 
@@ -44,6 +60,10 @@ def load():
     lp = ctypes.POINTER(ctypes.c_long)
     sig = {
         "vif_create": ([ip, ip, ip], vp),
+        "vif_create_ex": ([ip, ip, ip, ctypes.POINTER(VifOptions)], vp),
+        "vif_default_options": ([ctypes.POINTER(VifOptions)], None),
+        "vif_get_options": ([vp, ctypes.POINTER(VifOptions)], ip),
+        "vif_get_debug": ([vp, dp], ip),
         "vif_score": ([vp, vp, vp, dp], ip),
         "vif_submit": ([vp, vp, vp], ip),
         "vif_collect": ([vp, dp], ip),
@@ -61,8 +81,10 @@ def load():
                                vp, vp, vp], ip),
         "vif_selftest_div32": ([vp, vp, ctypes.c_long, vp, vp], ip),
         "vif_selftest_log2": ([vp, ctypes.c_long, vp, vp], ip),
-        "vif_selftest_ratios": ([vp, vp, ctypes.c_long, vp, vp, vp], ip),
-        "vif_selftest_statistic": ([vp, vp, vp, vp, vp, ctypes.c_long, vp, vp,
+        "vif_selftest_ratios": ([vp, vp, ctypes.c_double, ctypes.c_long, vp,
+                                 vp, vp], ip),
+        "vif_selftest_statistic": ([vp, vp, vp, vp, vp, ctypes.c_long,
+                                    ctypes.c_double, ctypes.c_double, vp, vp,
                                     vp], ip),
     }
     for name, (args, res) in sig.items():
@@ -75,8 +97,9 @@ def load():
 
 def exported_symbols():
     """Names of every C function this binding declares."""
-    return ["vif_create", "vif_score", "vif_submit", "vif_collect",
-            "vif_pending",
+    return ["vif_default_options", "vif_create", "vif_create_ex",
+            "vif_get_options", "vif_score", "vif_submit", "vif_collect",
+            "vif_pending", "vif_get_debug",
             "vif_destroy", "vif_set_stream",
             "vif_get_sums", "vif_get_row_sums", "vif_taps",
             "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
@@ -89,6 +112,27 @@ def exported_symbols():
 
 def vif_create(w, h, bpc):
     return load().vif_create(int(w), int(h), int(bpc))
+
+
+def vif_default_options():
+    o = VifOptions()
+    load().vif_default_options(ctypes.byref(o))
+    return o
+
+
+def vif_create_ex(w, h, bpc, options):
+    """options: a VifOptions or None (the defaults)."""
+    return load().vif_create_ex(int(w), int(h), int(bpc),
+                                None if options is None
+                                else ctypes.byref(options))
+
+
+def vif_get_options(ctx, options):
+    return load().vif_get_options(ctx, ctypes.byref(options))
+
+
+def vif_get_debug(ctx, out):
+    return load().vif_get_debug(ctx, _dptr(out))
 
 
 def vif_score(ctx, ref_ptr, dist_ptr, out):

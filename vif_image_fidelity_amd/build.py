@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvif_amd.so")
 
 SOURCES = ["vif_kernels.hip", "vif_selftest.hip", "vif_api.cpp",
-           "vif_taps.cpp"]
+           "vif_taps.cpp", "vif_options.cpp"]
 
 ARCH = "gfx950"
 

@@ -55,6 +55,8 @@ struct Slot {
 struct vif_ctx {
   int w = 0, h = 0, bpc = 0;
   int device = 0;
+  vif_options opt = {};
+  vifk::StatArgs stat = {};
   hipStream_t stream = nullptr; // caller's stream (NULL: the default stream)
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
@@ -65,6 +67,7 @@ struct vif_ctx {
   vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
   long head = 0, tail = 0;      // submitted / collected frame counts
   float sums[8] = {};
+  double last_out[8] = {};
   float *last_rows = nullptr; // host copy of the last collected row sums
   bool have_sums = false;
   int prof_mask = 0;
@@ -182,7 +185,8 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
       e = hipEventRecord(sl.prof[s][0], st);
     if (e == hipSuccess)
       e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
-                             ctx->taps[s], nt, nref, ndist, sl.terms[s], st);
+                             ctx->taps[s], nt, ctx->stat, nref, ndist,
+                             sl.terms[s], st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
   }
@@ -224,9 +228,16 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
       ctx->kernel_launches[k] += 1;
     }
   }
+  // a skipped scale 0 contributes nothing: its rows read 0 (the kernels
+  // still build the pyramid from it)
+  const bool skip0 = ctx->opt.skip_scale0 != 0;
+  std::memcpy(ctx->last_rows, sl.rows_host,
+              sizeof(float) * 2 * ctx->total_rows);
+  if (skip0)
+    std::memset(ctx->last_rows, 0, sizeof(float) * 2 * ctx->geom[0].h);
   float N[kScales], D[kScales];
   for (int s = 0; s < kScales; ++s) {
-    const float *r = sl.rows_host + 2 * ctx->row_base[s];
+    const float *r = ctx->last_rows + 2 * ctx->row_base[s];
     float n = 0.0f, d = 0.0f;
     for (int y = 0; y < ctx->geom[s].h; ++y) {
       n = n + r[2 * y];
@@ -237,12 +248,16 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
     ctx->sums[2 * s] = n;
     ctx->sums[2 * s + 1] = d;
   }
-  std::memcpy(ctx->last_rows, sl.rows_host,
-              sizeof(float) * 2 * ctx->total_rows);
   ctx->have_sums = true;
   ctx->tail += 1;
   for (int s = 0; s < kScales; ++s)
     out[s] = static_cast<double>(N[s]) / static_cast<double>(D[s]);
+  if (skip0)
+    out[0] = 0.0;
+  // floors of the reported scores of scales 1..3
+  for (int s = 1; s < kScales; ++s)
+    if (out[s] < ctx->opt.scale_min_val[s - 1])
+      out[s] = ctx->opt.scale_min_val[s - 1];
   double num = static_cast<double>(N[0]) + static_cast<double>(N[1]);
   num = num + static_cast<double>(N[2]);
   num = num + static_cast<double>(N[3]);
@@ -253,7 +268,19 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
   out[5] = den;
   out[6] = num / den;
   out[7] = 0.0;
+  std::memcpy(ctx->last_out, out, sizeof(ctx->last_out));
   return vifk::set_status(VIF_OK);
+}
+
+bool options_ok(const vif_options &o) {
+  vifk::OptionValues v{};
+  v.sigma_nsq = o.sigma_nsq;
+  v.enhn_gain_limit = o.enhn_gain_limit;
+  v.kernelscale = o.kernelscale;
+  for (int i = 0; i < 3; ++i)
+    v.scale_min_val[i] = o.scale_min_val[i];
+  v.skip_scale0 = o.skip_scale0;
+  return o.reserved == 0 && vifk::options_valid(v);
 }
 
 bool bad_frame_ptrs(const vif_ctx *ctx, const void *ref, const void *dist) {
@@ -267,11 +294,30 @@ bool bad_frame_ptrs(const vif_ctx *ctx, const void *ref, const void *dist) {
 
 extern "C" {
 
+__attribute__((visibility("default"))) void
+vif_default_options(vif_options *opt) {
+  if (opt == nullptr)
+    return;
+  std::memset(opt, 0, sizeof(*opt));
+  opt->sigma_nsq = 2.0;
+  opt->enhn_gain_limit = 100.0;
+  opt->kernelscale = 1.0;
+}
+
 __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
                                                            int bpc) {
+  return vif_create_ex(w, h, bpc, nullptr);
+}
+
+__attribute__((visibility("default"))) vif_ctx *
+vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
+  vif_options o;
+  vif_default_options(&o);
+  if (opt != nullptr)
+    o = *opt;
   if (w < VIF_MIN_SIDE || h < VIF_MIN_SIDE ||
       static_cast<long>(w) * h > VIF_MAX_PIXELS ||
-      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16)) {
+      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) || !options_ok(o)) {
     vifk::set_status(VIF_EINVAL);
     return nullptr;
   }
@@ -287,6 +333,8 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
   c->w = w;
   c->h = h;
   c->bpc = bpc;
+  c->opt = o;
+  c->stat = vifk::make_stat_args(o.sigma_nsq, o.enhn_gain_limit);
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) {
     delete c;
@@ -431,6 +479,28 @@ __attribute__((visibility("default"))) int vif_get_sums(const vif_ctx *ctx,
   if (ctx == nullptr || sums == nullptr || !ctx->have_sums)
     return vifk::set_status(VIF_EINVAL);
   std::memcpy(sums, ctx->sums, sizeof(ctx->sums));
+  return vifk::set_status(VIF_OK);
+}
+
+__attribute__((visibility("default"))) int
+vif_get_options(const vif_ctx *ctx, vif_options *opt) {
+  if (ctx == nullptr || opt == nullptr)
+    return vifk::set_status(VIF_EINVAL);
+  *opt = ctx->opt;
+  return vifk::set_status(VIF_OK);
+}
+
+__attribute__((visibility("default"))) int
+vif_get_debug(const vif_ctx *ctx, double out[VIF_NDEBUG]) {
+  if (ctx == nullptr || out == nullptr || !ctx->have_sums)
+    return vifk::set_status(VIF_EINVAL);
+  for (int s = 0; s < kScales; ++s)
+    out[s] = ctx->last_out[s];
+  out[4] = ctx->last_out[6];
+  out[5] = ctx->last_out[4];
+  out[6] = ctx->last_out[5];
+  for (int k = 0; k < 2 * kScales; ++k)
+    out[7 + k] = static_cast<double>(ctx->sums[k]);
   return vifk::set_status(VIF_OK);
 }
 

@@ -13,11 +13,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace vifk {
+#include "vif_internal.h"
 
-// Noise variance of the statistic, kept in binary64 (ADR-1422
-// "float_vif_sycl computes the CPU's arithmetic ...", Context).
-constexpr double kNoiseVar = 2.0;
+namespace vifk {
 
 // Floor of the variance terms: the fp32 value nearest 1e-10.
 constexpr float kEps = 1e-10f;
@@ -38,7 +36,9 @@ __device__ __forceinline__ int mirror_clamp(int i, int n) {
 // polynomial in fp32, not a library log2).  This method's coefficients:
 // Chebyshev interpolation of log2(1+t)/t on [0,1], degree 9, rounded to
 // fp32; c1 first.  x = 2^e * (1 + t); returns (float)e + t * P(t), Horner
-// from the highest coefficient.  Valid for finite x >= 1.
+// from the highest coefficient.  Meant for finite x >= 1; an infinite or NaN
+// x (a zero noise variance can produce them) is read the same way: its
+// exponent field 255 gives e = 128.
 __device__ __forceinline__ float bits_f32(uint32_t u) {
   return __builtin_bit_cast(float, u);
 }
@@ -63,17 +63,24 @@ __device__ __forceinline__ float log2_poly(float x) {
 }
 
 // fl32(1 + a / (sv + nsq)) with the sum, quotient and sum with one in fp64
-// and a single conversion to fp32 at the end (ADR-1422, Context and
-// Decision).
-__device__ __forceinline__ float num_ratio(float a, float sv) {
-  const double d = static_cast<double>(sv) + kNoiseVar;
+// and a single conversion to fp32 at the end; nsq is the noise variance,
+// kept in binary64 (ADR-1422 "float_vif_sycl computes the CPU's arithmetic
+// ...", Context and Decision).
+__device__ __forceinline__ float num_ratio(float a, float sv, double nsq) {
+  const double d = static_cast<double>(sv) + nsq;
   const double q = static_cast<double>(a) / d;
   return static_cast<float>(1.0 + q);
 }
 
-// fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.
-__device__ __forceinline__ float den_ratio(float s1) {
-  const double q = static_cast<double>(s1) / kNoiseVar;
+// fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.  For a
+// power-of-two nsq the quotient is the exact product with 1 / nsq.
+__device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
+  const double s = static_cast<double>(s1);
+  double q;
+  if (sa.inv_nsq != 0.0)
+    q = s * sa.inv_nsq;
+  else
+    q = s / sa.nsq;
   return static_cast<float>(1.0 + q);
 }
 
@@ -83,9 +90,13 @@ __device__ __forceinline__ float den_ratio(float s1) {
 //   ADR-1422, Decision) both terms are 1.  Above it: g = sigma12 /
 //   sigma1_sq, sv_sq = sigma2_sq - g * sigma12; sigma2_sq < eps sets g and
 //   sv_sq to 0; g < 0 sets sv_sq = sigma2_sq and g = 0; sv_sq is floored at
-//   eps; then the two ratios and their log2.
+//   eps; the enhancement gain limit then bounds g where it enters the
+//   numerator (C's MIN(g, limit), see StatArgs); then the two ratios and
+//   their log2.  With nsq = 0 nothing is special-cased: IEEE arithmetic
+//   throughout, as in the plain definition.
 __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
-                                            float yy, float xy, float &num,
+                                            float yy, float xy,
+                                            const StatArgs &sa, float &num,
                                             float &den) {
   const float m11 = mu1 * mu1;
   const float m22 = mu2 * mu2;
@@ -95,7 +106,7 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
   const float s12 = xy - m12;
   s1 = s1 < 0.0f ? 0.0f : s1;
   s2 = s2 < 0.0f ? 0.0f : s2;
-  if (static_cast<double>(s1) < kNoiseVar) {
+  if (static_cast<double>(s1) < sa.nsq) {
     num = 1.0f;
     den = 1.0f;
     return;
@@ -112,10 +123,11 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
     g = 0.0f;
   }
   sv = sv < kEps ? kEps : sv;
+  g = g < sa.gain ? g : sa.gain;
   const float gg = g * g;
   const float a = gg * s1;
-  num = log2_poly(num_ratio(a, sv));
-  den = log2_poly(den_ratio(s1));
+  num = log2_poly(num_ratio(a, sv, sa.nsq));
+  den = log2_poly(den_ratio(s1, sa));
 }
 
 }  // namespace vifk

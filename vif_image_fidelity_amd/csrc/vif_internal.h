@@ -21,6 +21,32 @@ struct TapArgs {
   float t[kMaxTaps];
 };
 
+// Constants of the per-pixel statistic, built on the host from the options
+// and passed to every scale kernel by value.
+//   nsq      the noise variance (a double, as the branch and both ratios
+//            use it)
+//   inv_nsq  1 / nsq when that is a power of two, so that s * inv_nsq is
+//            the quotient s / nsq exactly; 0 otherwise (divide)
+//   gain     the enhancement gain limit rounded to fp32.  C's MIN(g, limit)
+//            with a double limit selects the same value as the fp32
+//            comparison g < gain: no fp32 value lies strictly between a
+//            limit and its nearest fp32, so the two comparisons can differ
+//            only where g is that fp32 value, and then both results are g.
+struct StatArgs {
+  double nsq;
+  double inv_nsq;
+  float gain;
+};
+
+// Option checks and the statistic constants (vif_options.cpp).  Returns
+// false for options outside their documented ranges.
+struct OptionValues {
+  double sigma_nsq, enhn_gain_limit, kernelscale, scale_min_val[3];
+  int skip_scale0;
+};
+bool options_valid(const OptionValues &o);
+StatArgs make_stat_args(double nsq, double gain_limit);
+
 // Terms of a 16-row strip: 32 sequences (16 rows x {num, den}).  In the
 // term buffer of a scale, strip p holds term_groups(w) groups of 4 columns,
 // each group the 32 sequences' 4 values: floats
@@ -58,8 +84,8 @@ struct ScaleGeom {
 hipError_t launch_scale(int scale, int bpc, const void *in_ref,
                         const void *in_dist, const ScaleGeom &g,
                         const TapArgs &taps, const TapArgs &next_taps,
-                        float *next_ref, float *next_dist, float *terms,
-                        hipStream_t stream);
+                        const StatArgs &stat, float *next_ref,
+                        float *next_dist, float *terms, hipStream_t stream);
 
 // Ordered row sums of all scales of one frame (`waves` = pair_base[4]).
 hipError_t launch_rowsum(const RowSumArgs &args, int waves,

@@ -71,8 +71,9 @@ __device__ __forceinline__ float tap(const TapArgs &t, int k, int n) {
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
-    float in_scale, TapArgs taps, TapArgs dtaps, float *__restrict__ next_ref,
-    float *__restrict__ next_dist, float *__restrict__ terms) {
+    float in_scale, TapArgs taps, TapArgs dtaps, StatArgs stat,
+    float *__restrict__ next_ref, float *__restrict__ next_dist,
+    float *__restrict__ terms) {
   constexpr int N = 2 * R + 1;
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
@@ -219,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
     }
 #pragma unroll
     for (int i = 0; i < HB; ++i)
-      pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], tnum[i],
-                  tden[i]);
+      pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], stat,
+                  tnum[i], tden[i]);
   }
   __syncthreads(); // every read of V is done: its region takes the terms
 
@@ -365,8 +366,8 @@ __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
 hipError_t launch_scale(int scale, int bpc, const void *in_ref,
                         const void *in_dist, const ScaleGeom &g,
                         const TapArgs &taps, const TapArgs &next_taps,
-                        float *next_ref, float *next_dist, float *terms,
-                        hipStream_t stream) {
+                        const StatArgs &stat, float *next_ref,
+                        float *next_dist, float *terms, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(g.ntx), static_cast<unsigned>(g.strips));
   const dim3 block(kThreads);
   switch (scale) {
@@ -375,29 +376,29 @@ hipError_t launch_scale(int scale, int bpc, const void *in_ref,
       scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
           static_cast<const uint8_t *>(in_ref),
           static_cast<const uint8_t *>(in_dist), g.w, g.h, 1.0f, taps,
-          next_taps, next_ref, next_dist, terms);
+          next_taps, stat, next_ref, next_dist, terms);
     } else {
       const float sc = bpc == 10 ? 0.25f : bpc == 12 ? 0.0625f : 0.00390625f;
       scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
           static_cast<const uint16_t *>(in_ref),
           static_cast<const uint16_t *>(in_dist), g.w, g.h, sc, taps,
-          next_taps, next_ref, next_dist, terms);
+          next_taps, stat, next_ref, next_dist, terms);
     }
     break;
   case 1:
     scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, next_ref, next_dist, terms);
+        g.w, g.h, 1.0f, taps, next_taps, stat, next_ref, next_dist, terms);
     break;
   case 2:
     scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, next_ref, next_dist, terms);
+        g.w, g.h, 1.0f, taps, next_taps, stat, next_ref, next_dist, terms);
     break;
   case 3:
     scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
         static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, nullptr, nullptr, terms);
+        g.w, g.h, 1.0f, taps, next_taps, stat, nullptr, nullptr, terms);
     break;
   default:
     return hipErrorInvalidValue;

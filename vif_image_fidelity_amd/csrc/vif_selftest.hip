@@ -46,12 +46,12 @@ __global__ void log2_kernel(const float *__restrict__ x, long n,
 
 __global__ void ratios_kernel(const float *__restrict__ a,
                               const float *__restrict__ sv, long n,
-                              float *__restrict__ num,
+                              vifk::StatArgs sa, float *__restrict__ num,
                               float *__restrict__ den) {
   const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
   if (i < n) {
-    num[i] = vifk::num_ratio(a[i], sv[i]);
-    den[i] = vifk::den_ratio(a[i]);
+    num[i] = vifk::num_ratio(a[i], sv[i], sa.nsq);
+    den[i] = vifk::den_ratio(a[i], sa);
   }
 }
 
@@ -60,12 +60,12 @@ __global__ void statistic_kernel(const float *__restrict__ mu1,
                                  const float *__restrict__ xx,
                                  const float *__restrict__ yy,
                                  const float *__restrict__ xy, long n,
-                                 float *__restrict__ num,
+                                 vifk::StatArgs sa, float *__restrict__ num,
                                  float *__restrict__ den) {
   const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
   if (i < n) {
     float a, b;
-    vifk::pixel_terms(mu1[i], mu2[i], xx[i], yy[i], xy[i], a, b);
+    vifk::pixel_terms(mu1[i], mu2[i], xx[i], yy[i], xy[i], sa, a, b);
     num[i] = a;
     den[i] = b;
   }
@@ -84,6 +84,15 @@ int finish(hipStream_t s) {
 
 // grid.x is limited to 2^31-1 blocks; n up to 2^38 stays well inside.
 bool bad_n(long n) { return n < 0 || n > (1L << 36); }
+
+// The statistic's options as the library checks them.
+bool bad_stat_options(double nsq, double gain_limit) {
+  vifk::OptionValues o{};
+  o.sigma_nsq = nsq;
+  o.enhn_gain_limit = gain_limit;
+  o.kernelscale = 1.0;
+  return !vifk::options_valid(o);
+}
 
 } // namespace
 
@@ -127,29 +136,33 @@ vif_selftest_log2(const float *x, long n, float *y, void *stream) {
 }
 
 __attribute__((visibility("default"))) int
-vif_selftest_ratios(const float *a, const float *sv, long n, float *num,
-                    float *den, void *stream) {
-  if (bad_n(n) || (n > 0 && (!a || !sv || !num || !den)))
+vif_selftest_ratios(const float *a, const float *sv, double nsq, long n,
+                    float *num, float *den, void *stream) {
+  if (bad_n(n) || bad_stat_options(nsq, 100.0) ||
+      (n > 0 && (!a || !sv || !num || !den)))
     return vifk::set_status(VIF_EINVAL);
   if (n == 0)
     return vifk::set_status(VIF_OK);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ratios_kernel<<<grid_for(n), kBlock, 0, s>>>(a, sv, n, num, den);
+  ratios_kernel<<<grid_for(n), kBlock, 0, s>>>(
+      a, sv, n, vifk::make_stat_args(nsq, 100.0), num, den);
   return finish(s);
 }
 
 __attribute__((visibility("default"))) int
 vif_selftest_statistic(const float *mu1, const float *mu2, const float *xx,
-                       const float *yy, const float *xy, long n, float *num,
-                       float *den, void *stream) {
-  if (bad_n(n) ||
+                       const float *yy, const float *xy, long n, double nsq,
+                       double gain_limit, float *num, float *den,
+                       void *stream) {
+  if (bad_n(n) || bad_stat_options(nsq, gain_limit) ||
       (n > 0 && (!mu1 || !mu2 || !xx || !yy || !xy || !num || !den)))
     return vifk::set_status(VIF_EINVAL);
   if (n == 0)
     return vifk::set_status(VIF_OK);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  statistic_kernel<<<grid_for(n), kBlock, 0, s>>>(mu1, mu2, xx, yy, xy, n,
-                                                  num, den);
+  statistic_kernel<<<grid_for(n), kBlock, 0, s>>>(
+      mu1, mu2, xx, yy, xy, n, vifk::make_stat_args(nsq, gain_limit), num,
+      den);
   return finish(s);
 }
 
