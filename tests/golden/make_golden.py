@@ -41,12 +41,33 @@ def main():
                 "sums_hex": [fhex(v) for v in sums],
                 "out": [float(v) for v in out],
             })
+    ref, dist, bpc = synth.WORKLOADS["netflix_576x324_8bit"]()[0]
+    option_cases = []
+    for opt in OPTION_SETS:
+        out, sums = oracle.score(ref, dist, bpc, options=opt)
+        option_cases.append({
+            "workload": "netflix_576x324_8bit", "frame": 0, "options": opt,
+            "out_hex": [dhex(v) for v in out],
+            "sums_hex": [fhex(v) for v in sums],
+        })
     path = os.path.join(HERE, "oracle_regression.json")
     with open(path, "w") as f:
         json.dump({"_comment": "written by tests/golden/make_golden.py from "
                    "oracle/ only; regression guard of the oracle",
-                   "cases": cases}, f, indent=1)
-    print("wrote %d cases to %s" % (len(cases), path))
+                   "cases": cases, "option_cases": option_cases}, f, indent=1)
+    print("wrote %d + %d cases to %s" % (len(cases), len(option_cases), path))
+
+
+# Option sets frozen on the first 576x324 frame (see vif_oracle.h for their
+# meaning).
+OPTION_SETS = [
+    {"sigma_nsq": 4.7},
+    {"sigma_nsq": 1.5, "enhn_gain_limit": 1.0},
+    {"sigma_nsq": 0.0},
+    {"enhn_gain_limit": 0.5},
+    {"skip_scale0": 1},
+    {"scale_min_val": [0.999, 0.5, 2.0]},
+]
 
 
 if __name__ == "__main__":

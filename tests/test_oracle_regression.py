@@ -29,3 +29,15 @@ def test_oracle_matches_frozen_outputs(orc, name):
         assert [struct.pack(">d", float(v)).hex() for v in out] == c["out_hex"]
         assert [struct.pack(">f", float(v)).hex() for v in sums] == \
             c["sums_hex"]
+
+
+def test_oracle_matches_frozen_option_outputs(orc):
+    ref, dist, bpc = _frames("netflix_576x324_8bit")[0]
+    cases = GOLD["option_cases"]
+    assert len(cases) >= 6
+    for c in cases:
+        out, sums = orc.score(ref, dist, bpc, options=c["options"])
+        assert [struct.pack(">d", float(v)).hex() for v in out] == \
+            c["out_hex"], c["options"]
+        assert [struct.pack(">f", float(v)).hex() for v in sums] == \
+            c["sums_hex"], c["options"]
