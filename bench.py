@@ -6,7 +6,7 @@ One step scores one 3840x2160 8-bit luma frame pair (the whole path: four
 scales of filtering, statistic, decimation and ordered row sums, one
 read-back and the host sums).  The 20 synthetic 1/f-noise frame pairs are
 resident in HBM before the timed region; steps cycle through them and go
-through the context's asynchronous queue (submit / collect, up to two
+through the context's asynchronous queue (submit / collect, up to three
 frames in flight), so consecutive frames overlap their read-back and host
 work with the next frame's kernels.  Prints one JSON line.
 
@@ -19,7 +19,9 @@ The line carries, besides the contract fields:
                 kernel source has not changed since they were taken, else null.
   cpu_baseline  the CPU oracle on this host, one core, on a bounded sample of
                 the same workload.
-  extra         1920x1080 frames/s, HBM GB/s of the whole frame from counters
+  extra         1920x1080 and 576x324 frames/s, the 4K rate when the frames
+                come from pinned host memory (PCIe copies included, never the
+                headline value), HBM GB/s of the whole frame from counters
                 when available, and the per-kernel split.
 """
 import argparse
@@ -47,9 +49,16 @@ METRIC = ("VIF frames/sec at 1080p and 4K on 1 MI355X; achieved HBM GB/s vs "
 # the figure is a lower bound of the work done.
 OPS_PER_PIXEL_SCALE0 = 341.0 + 102.0 / 4.0
 
-# VALU peak for plain (unfused, unpacked) fp32 operations: 256 CUs x 4 SIMDs
-# x 16 lanes x 2.4 GHz = 39.3e12 operations/s.
-VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+# VALU peak for plain (unfused, unpacked) fp32 operations.  MI355X's fp32
+# vector figure, 157.3 TFLOP/s, is 256 CUs x 4 SIMDs x 32 lanes x 2 flops (an
+# FMA) x 2.4 GHz: a SIMD retires two wave64 VALU instructions per four
+# cycles.  Unpacked code reaches that rate too, by dual issue (the SIMD
+# issues VALU instructions of two waves in one quad-cycle; rocprofv3's
+# SQ_ACTIVE_INST_VALU2 counts those quad-cycles, and the scale-0 kernel
+# retires more wave instructions than one per quad-cycle per SIMD allows).
+# A plain add or multiply is one operation, so the ceiling is
+# 256 x 4 x 32 x 2.4e9 = 78.6e12 operations/s.
+VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
 
 HBM_PEAK_GBS = 8000.0
 
@@ -131,6 +140,39 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
     kt["_host_collect_us"] = 1e6 * host["collect"] / max(steps, 1)
     ctx.close()
     return (t1 - t0), kt
+
+
+def time_host_frames(V, frames, w, h, bpc, steps, warmup):
+    """The queue fed from host memory: pinned host planes, each frame copied
+    to the slot's device buffers by the library (vif_submit_host).  The
+    rate includes the host-to-device copies over PCIe."""
+    import torch
+    dt = torch.uint8 if bpc == 8 else torch.int16
+    pairs = []
+    for r, d, _ in frames[:4]:
+        pr = torch.empty((h, w), dtype=dt, pin_memory=True)
+        pd = torch.empty((h, w), dtype=dt, pin_memory=True)
+        pr.numpy().view(r.dtype)[:] = r
+        pd.numpy().view(d.dtype)[:] = d
+        pairs.append((pr, pd))
+    ctx = V.Vif(w, h, bpc)
+
+    def run(n):
+        for i in range(n):
+            if ctx.pending() == V.QUEUE_DEPTH:
+                ctx.collect()
+            ctx.submit_host(*pairs[i % len(pairs)])
+        while ctx.pending():
+            ctx.collect()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ctx.close()
+    return steps / (t1 - t0)
 
 
 def isolated_scale0_us(V, frames, w, h, bpc, n=50):
@@ -264,6 +306,12 @@ def main():
                                  10)
     fps1080 = args.steps_1080p / dt1080
 
+    # 576x324 (the launch-bound small frame) and 4K fed from host memory
+    fsmall = synth.netflix_576x324_8bit()
+    dts, kts = time_frames(V, fsmall, 576, 324, 8, 2000, 50)
+    fps_small = 2000 / dts
+    fps_host = time_host_frames(V, frames4k, w, h, bpc, 200, 10)
+
     ops = OPS_PER_PIXEL_SCALE0 * w * h
     achieved = ops / (s0_avg_ms / 1000.0) / 1e12
     peak = VALU_PEAK_OPS / 1e12
@@ -274,6 +322,11 @@ def main():
 
     pops = path_ops(w, h)
     extra = {"fps_1080p_10bit": round(fps1080, 1),
+             "fps_576x324_8bit": round(fps_small, 1),
+             "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
+             "host_us_per_frame_576x324": {
+                 "submit": round(kts["_host_submit_us"], 2),
+                 "collect": round(kts["_host_collect_us"], 2)},
              "kernel_avg_us_4k": split,
              "scale0_kernel_avg_us": round(1000 * s0_avg_ms, 2),
              "scale0_kernel_isolated_us": round(iso_s0_us, 2),

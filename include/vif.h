@@ -148,6 +148,24 @@ int vif_score(vif_ctx *ctx, const void *ref, const void *dist, double out[8]);
 int vif_submit(vif_ctx *ctx, const void *ref, const void *dist);
 int vif_collect(vif_ctx *ctx, double out[8]);
 
+/*
+ * Frames in HOST memory.  vif_submit_host enqueues a pair whose planes
+ * (same layout as for vif_submit) are in host memory: the context copies
+ * them into device buffers of the frame's queue slot with asynchronous
+ * copies on the slot's stream, then scores them as vif_submit does, so one
+ * frame's upload overlaps the other frames' kernels (double buffering over
+ * the VIF_QUEUE_DEPTH slots).  Host memory from hipHostMalloc makes the
+ * copies asynchronous; pageable memory also works, but the runtime then
+ * stages the copy and the call may wait for it.  The host planes must stay
+ * valid and unchanged until the frame's vif_collect returns.  Collect with
+ * vif_collect.  vif_score_host is the synchronous form (submit, collect).
+ * Errors and queue limits as for vif_submit / vif_score.  The per-slot frame
+ * buffers are allocated by vif_create; these calls allocate nothing.
+ */
+int vif_submit_host(vif_ctx *ctx, const void *ref, const void *dist);
+int vif_score_host(vif_ctx *ctx, const void *ref, const void *dist,
+                   double out[8]);
+
 /* vif_pending -- frames submitted and not yet collected (or VIF_EINVAL). */
 int vif_pending(const vif_ctx *ctx);
 

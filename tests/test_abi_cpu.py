@@ -133,6 +133,8 @@ def test_null_handling(lib):
     assert _lib.vif_submit(None, 1, 1) == _lib.VIF_EINVAL
     assert _lib.vif_collect(None, out) == _lib.VIF_EINVAL
     assert _lib.vif_pending(None) == _lib.VIF_EINVAL
+    assert _lib.vif_submit_host(None, 1, 1) == _lib.VIF_EINVAL
+    assert _lib.vif_score_host(None, 1, 1, out) == _lib.VIF_EINVAL
     assert _lib.vif_get_debug(None, np.zeros(15)) == _lib.VIF_EINVAL
     assert _lib.vif_get_options(None, _lib.VifOptions()) == _lib.VIF_EINVAL
     _lib.vif_destroy(None)  # no-op

@@ -284,3 +284,47 @@ def test_score_rejects_misaligned_wide_pointer(V):
     p = buf.data_ptr() + 1
     assert _lib.vif_score(ctx._ctx, p, p, out) == _lib.VIF_EINVAL
     ctx.close()
+
+
+def test_host_frames_match_device_frames(V, orc):
+    """Frames in host memory (pageable numpy arrays and pinned tensors) go
+    through the per-slot upload and score bit for bit as the same frames in
+    device memory; the queue keeps order over more frames than slots, and a
+    host buffer refilled after its frame was collected is scored anew."""
+    import torch
+    from vif_image_fidelity_amd import synth
+    frames = synth.WORKLOADS["netflix_576x324_8bit"]()
+    h, w = frames[0][0].shape
+    ctx = _ctx(V, w, h, 8)
+    want = [orc.score(r, d, 8)[0] for r, d, _ in frames]
+    print("host frames: pageable", flush=True)
+    for (r, d, _), exp in zip(frames, want):
+        got = ctx.score_host(r, d)
+        assert got.tobytes() == exp.tobytes()
+    print("host frames: pinned queue", flush=True)
+    pinned = []
+    for r, d, _ in frames:
+        pr = torch.empty((h, w), dtype=torch.uint8, pin_memory=True)
+        pd = torch.empty((h, w), dtype=torch.uint8, pin_memory=True)
+        pr.numpy()[:] = r
+        pd.numpy()[:] = d
+        pinned.append((pr, pd))
+    order = [0, 1, 2, 1, 0, 2, 2]
+    outs = []
+    for k, i in enumerate(order):
+        if ctx.pending() == V.QUEUE_DEPTH:
+            outs.append(ctx.collect())
+        ctx.submit_host(*pinned[i])
+    while ctx.pending():
+        outs.append(ctx.collect())
+    for i, got in zip(order, outs):
+        assert got.tobytes() == want[i].tobytes(), i
+    # refill a host buffer once nothing is pending and score it again
+    pinned[0][1].numpy()[:] = frames[1][1]
+    got = ctx.score_host(*pinned[0])
+    exp = orc.score(frames[0][0], frames[1][1], 8)[0]
+    assert got.tobytes() == exp.tobytes()
+    with pytest.raises(ValueError):
+        ctx.score_host(frames[0][0][:, :-1], frames[0][1][:, :-1])
+    with pytest.raises(ValueError):
+        ctx.score_host(frames[0][0].astype(np.uint16), frames[0][1])

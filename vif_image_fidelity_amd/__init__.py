@@ -115,6 +115,46 @@ class Vif:
             raise VifError(rc, "vif_score")
         return out
 
+    def _host_ptr(self, a):
+        """Address of a host plane: a C-contiguous numpy array (or a CPU
+        tensor) of shape (h, w) with the context's sample width."""
+        if hasattr(a, "data_ptr"):
+            if a.is_cuda:
+                raise ValueError("host frames must be CPU memory")
+            if not a.is_contiguous():
+                raise ValueError("frames must be contiguous")
+            self._check_frame(a)
+            return a.data_ptr()
+        if not isinstance(a, np.ndarray):
+            raise TypeError("expected a numpy array or a CPU tensor")
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("frames must be contiguous")
+        if a.shape != (self.h, self.w):
+            raise ValueError("frame shape %s, context is (%d, %d)"
+                             % (a.shape, self.h, self.w))
+        if a.dtype != (np.uint8 if self.bpc == 8 else np.uint16):
+            raise ValueError("bpc %d needs %s samples"
+                             % (self.bpc, "uint8" if self.bpc == 8
+                                else "uint16"))
+        return a.ctypes.data
+
+    def score_host(self, ref, dist):
+        """Score one pair held in host memory (copied by the library)."""
+        out = np.zeros(8, dtype=np.float64)
+        rc = _lib.vif_score_host(self._ctx, self._host_ptr(ref),
+                                 self._host_ptr(dist), out)
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_score_host")
+        return out
+
+    def submit_host(self, ref, dist):
+        """Enqueue one pair held in host memory; the arrays must stay alive
+        and unchanged until the matching collect() returns."""
+        rc = _lib.vif_submit_host(self._ctx, self._host_ptr(ref),
+                                  self._host_ptr(dist))
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_submit_host")
+
     def submit(self, ref, dist):
         """Enqueue one pair (at most QUEUE_DEPTH pending); the frames must
         stay valid until the matching collect() returns."""

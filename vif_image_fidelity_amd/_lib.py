@@ -66,6 +66,8 @@ def load():
         "vif_get_debug": ([vp, dp], ip),
         "vif_score": ([vp, vp, vp, dp], ip),
         "vif_submit": ([vp, vp, vp], ip),
+        "vif_submit_host": ([vp, vp, vp], ip),
+        "vif_score_host": ([vp, vp, vp, dp], ip),
         "vif_collect": ([vp, dp], ip),
         "vif_pending": ([vp], ip),
         "vif_destroy": ([vp], None),
@@ -99,6 +101,7 @@ def exported_symbols():
     """Names of every C function this binding declares."""
     return ["vif_default_options", "vif_create", "vif_create_ex",
             "vif_get_options", "vif_score", "vif_submit", "vif_collect",
+            "vif_submit_host", "vif_score_host",
             "vif_pending", "vif_get_debug",
             "vif_destroy", "vif_set_stream",
             "vif_get_sums", "vif_get_row_sums", "vif_taps",
@@ -142,6 +145,14 @@ def vif_score(ctx, ref_ptr, dist_ptr, out):
 
 def vif_submit(ctx, ref_ptr, dist_ptr):
     return load().vif_submit(ctx, ref_ptr, dist_ptr)
+
+
+def vif_submit_host(ctx, ref_ptr, dist_ptr):
+    return load().vif_submit_host(ctx, ref_ptr, dist_ptr)
+
+
+def vif_score_host(ctx, ref_ptr, dist_ptr, out):
+    return load().vif_score_host(ctx, ref_ptr, dist_ptr, _dptr(out))
 
 
 def vif_collect(ctx, out):

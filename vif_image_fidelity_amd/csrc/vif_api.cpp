@@ -9,6 +9,8 @@
 // into the host buffer: one read-back per frame with no copy call
 // (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision:
 // the row sums come back in one transfer and the host adds them).
+// Frames in host memory are first copied into the slot's own frame buffers
+// on the slot's stream (vif_submit_host).
 // Consecutive frames rotate over the slots, so one frame's small
 // scales and row sums overlap the next frame's scale 0, which fills the
 // GPU.  A submission is six runtime calls: five launches and one event.
@@ -41,6 +43,8 @@ constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
 struct Slot {
   float *pyr_ref[kScales] = {};   // [0] unused: scale 0 reads the frames
   float *pyr_dist[kScales] = {};
+  void *frame_ref = nullptr;      // device copies of host frames
+  void *frame_dist = nullptr;
   float *terms[kScales] = {};     // term buffers of the four scales
   float *rows_host = nullptr;     // pinned, written by the row-sum kernel
   hipStream_t stream = nullptr;   // owned: all of the slot's work
@@ -143,6 +147,10 @@ void free_all(vif_ctx *c) {
       if (sl.terms[s])
         (void)hipFree(sl.terms[s]);
     }
+    if (sl.frame_ref)
+      (void)hipFree(sl.frame_ref);
+    if (sl.frame_dist)
+      (void)hipFree(sl.frame_dist);
     if (sl.rows_host)
       (void)hipHostFree(sl.rows_host);
     destroy_event(sl.submitted);
@@ -208,6 +216,23 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
     return vifk::status_from_hip(e);
   ctx->head += 1;
   return vifk::set_status(VIF_OK);
+}
+
+// Enqueues one frame whose planes are in host memory: two copies into the
+// slot's frame buffers on the slot's stream, then the frame itself.  The
+// slot's previous frame read those buffers earlier on the same stream.
+int submit_host_frame(vif_ctx *ctx, const void *ref, const void *dist) {
+  Slot &sl = ctx->slots[ctx->head % kDepth];
+  const size_t bytes = static_cast<size_t>(ctx->w) * ctx->h *
+                       (ctx->bpc == 8 ? 1 : 2);
+  hipError_t e = hipMemcpyAsync(sl.frame_ref, ref, bytes,
+                                hipMemcpyHostToDevice, sl.stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(sl.frame_dist, dist, bytes, hipMemcpyHostToDevice,
+                       sl.stream);
+  if (e != hipSuccess)
+    return vifk::status_from_hip(e);
+  return submit_frame(ctx, sl.frame_ref, sl.frame_dist);
 }
 
 // Waits for the oldest pending frame and writes its outputs.
@@ -379,6 +404,11 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
       if (e == hipSuccess)
         e = dev_alloc(&sl.pyr_dist[s], n);
     }
+    const size_t frame_bytes = static_cast<size_t>(w) * h * (bpc == 8 ? 1 : 2);
+    if (e == hipSuccess)
+      e = hipMalloc(&sl.frame_ref, frame_bytes);
+    if (e == hipSuccess)
+      e = hipMalloc(&sl.frame_dist, frame_bytes);
     for (int s = 0; s < kScales && e == hipSuccess; ++s)
       e = dev_alloc(&sl.terms[s], static_cast<size_t>(c->geom[s].strips) *
                                       vifk::term_groups(c->geom[s].w) *
@@ -441,6 +471,32 @@ vif_submit(vif_ctx *ctx, const void *ref, const void *dist) {
   if (scope.error() != hipSuccess)
     return vifk::status_from_hip(scope.error());
   return submit_frame(ctx, ref, dist);
+}
+
+__attribute__((visibility("default"))) int
+vif_submit_host(vif_ctx *ctx, const void *ref, const void *dist) {
+  if (ctx == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
+      ctx->head - ctx->tail >= kDepth)
+    return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  return submit_host_frame(ctx, ref, dist);
+}
+
+__attribute__((visibility("default"))) int
+vif_score_host(vif_ctx *ctx, const void *ref, const void *dist,
+               double out[8]) {
+  if (ctx == nullptr || out == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
+      ctx->head != ctx->tail)
+    return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  const int rc = submit_host_frame(ctx, ref, dist);
+  if (rc != VIF_OK)
+    return rc;
+  return collect_frame(ctx, out);
 }
 
 __attribute__((visibility("default"))) int vif_collect(vif_ctx *ctx,
