@@ -1,16 +1,17 @@
 // vif_kernels.hip -- HIP kernel of the float VIF feature for gfx950.
 //
 // One kernel per scale s does, for a 112 x 16 tile of output pixels:
-//   1. stage the tile's input (+ halo of the filter radius) into LDS as fp32,
-//      normalising native samples on the way (Research-2130 "float_ssim
-//      decimation on the SYCL device", Sources: 8-bit as is, 10/12/16-bit
-//      divided by 4/16/256) and mirroring out-of-plane indices by one
+//   1. stage the tile's input (+ halo of the filter radius) into LDS in the
+//      plane's sample type, mirroring out-of-plane indices by one
 //      reflection and a clamp (ADR-1444 "float_vif_hip runs the arithmetic
-//      of the CUDA twin ...", Decision);
+//      of the CUDA twin ...", Decision); samples are normalised to fp32 where
+//      they are read (Research-2130 "float_ssim decimation on the SYCL
+//      device", Sources: 8-bit as is, 10/12/16-bit divided by 4/16/256);
 //   2. the vertical pass of the separable Gaussian for the five quantities
 //      x, y, x*x, y*y, x*y, one thread per column and 8 rows in registers,
 //      and the vertical pass of the next scale's low-pass at even rows;
-//   3. the horizontal pass (7 outputs per thread), the per-pixel statistic
+//   3. the horizontal pass (7 outputs per thread, in two rounds of
+//      quantities so the block's LDS stays small), the per-pixel statistic
 //      and the two terms, staged in LDS and written to the scale's term
 //      buffer in the order the row sums read them;
 //   4. the horizontal pass of the next scale's low-pass at even columns,
@@ -34,27 +35,27 @@ namespace vifk {
 constexpr int kThreads = 256;
 
 // Planes hold at most 2^27 samples, so a 32-bit offset addresses them.
+// The input tile stays in LDS in the plane's own sample type (one byte per
+// 8-bit sample); to_float normalises a sample where the vertical pass reads
+// it (Research-2130 "float_ssim decimation on the SYCL device", Sources:
+// 8-bit samples as they are, wider ones divided by 4, 16 or 256).
 template <typename InT>
-__device__ __forceinline__ float load_sample(const InT *__restrict__ p,
-                                             unsigned i, float scale);
+__device__ __forceinline__ float to_float(InT v, float scale);
 
 template <>
-__device__ __forceinline__ float load_sample<uint8_t>(
-    const uint8_t *__restrict__ p, unsigned i, float) {
-  return static_cast<float>(p[i]);
+__device__ __forceinline__ float to_float<uint8_t>(uint8_t v, float) {
+  return static_cast<float>(v);
 }
 
 template <>
-__device__ __forceinline__ float load_sample<uint16_t>(
-    const uint16_t *__restrict__ p, unsigned i, float scale) {
+__device__ __forceinline__ float to_float<uint16_t>(uint16_t v, float scale) {
   // scale is an exact power of two (1/4, 1/16, 1/256): the product is exact
-  return static_cast<float>(p[i]) * scale;
+  return static_cast<float>(v) * scale;
 }
 
 template <>
-__device__ __forceinline__ float load_sample<float>(
-    const float *__restrict__ p, unsigned i, float) {
-  return p[i];
+__device__ __forceinline__ float to_float<float>(float v, float) {
+  return v;
 }
 
 // Tap k of an n-tap filter.  The taps are symmetric bit for bit (t[k] and
@@ -66,8 +67,60 @@ __device__ __forceinline__ float tap(const TapArgs &t, int k, int n) {
   return t.t[k < n - 1 - k ? k : n - 1 - k];
 }
 
+// Makes each value of v exist in a register at this point of the program.
+// The empty asm takes the values as register operands, so the arithmetic
+// that produces them cannot be moved below it (past a barrier, towards its
+// later use), which would keep its many inputs live instead of the few
+// results.  It emits no instruction.
+template <int A, int B>
+__device__ __forceinline__ void settle(float (&v)[A][B]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      asm volatile("" : "+v"(v[a][b]));
+}
+
+// Horizontal pass of NQ quantities stored in LDS as [q][kTileH][pitch]:
+// thread (ty, seg) computes tile row ty, columns seg*HB .. seg*HB+HB-1.
+template <int R, int NQ, int HB>
+__device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
+                                      int seg, const TapArgs &taps,
+                                      float (&f)[NQ][HB]) {
+  constexpr int N = 2 * R + 1;
+  constexpr int CWP = kTileW + 2 * R + 1;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const float *row = sV + (q * kTileH + ty) * CWP + seg * HB;
+    float v[HB + 2 * R];
+#pragma unroll
+    for (int j = 0; j < HB + 2 * R; ++j)
+      v[j] = row[j];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+      float a = tap(taps, 0, N) * v[i];
+#pragma unroll
+      for (int k = 1; k < N; ++k)
+        a = a + tap(taps, k, N) * v[i + k];
+      f[q][i] = a;
+    }
+  }
+}
+
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
+//
+// LDS is reused phase by phase so that a block needs about 24 KiB and six
+// blocks fit a CU:
+//   phases 1-2  input tile, native samples     [2][IR][CW] InT
+//   phases 3-4  vertical results of x, y, x*x  [3][kTileH][CWP]
+//   phases 5-6  vertical results of y*y, x*y   [2][kTileH][CWP]
+//               + the low-pass at even rows    [2][kTileH/2][CWP] at kVdOff
+//   phases 7-8  terms                          [kSeq][kTermPitch]
+//               + the low-pass (still)         at kVdOff
+// The horizontal pass therefore runs in two rounds (three quantities, then
+// two); the low-pass results of the vertical pass wait in registers until
+// the second round's write.
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
@@ -81,16 +134,21 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   constexpr int CWP = CW + 1;        // odd pitch: conflict-free row reads
   constexpr int VB = 8;              // rows per thread in the vertical pass
   constexpr int HB = 7;              // outputs per thread, horizontal pass
-  constexpr int kIn = 2 * IR * CW;
+  constexpr int kQA = 3;             // quantities of the first round
+  constexpr int kInFloats =
+      (2 * IR * CW * static_cast<int>(sizeof(InT)) + 3) / 4;
+  constexpr int kVA = kQA * kTileH * CWP;
+  constexpr int kVB = (5 - kQA) * kTileH * CWP;
+  constexpr int kT = kSeq * kTermPitch;
+  constexpr int kVdOff = kVB > kT ? kVB : kT;
   constexpr int kVd = RD > 0 ? 2 * (kTileH / 2) * CWP : 0;
-  constexpr int kV = 5 * kTileH * CWP + kVd;
-  constexpr int kLds = kIn > kV ? kIn : kV;
+  constexpr int kLds0 = kVA > kVdOff + kVd ? kVA : kVdOff + kVd;
+  constexpr int kLds = kLds0 > kInFloats ? kLds0 : kInFloats;
   static_assert(CW <= 128, "one thread per vertical column in two halves");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
   static_assert(kTileH == 2 * VB, "two row blocks");
-  static_assert(kSeq * kTermPitch <= 5 * kTileH * CWP,
-                "terms fit in the dead V region");
   __shared__ float lds[kLds];
+  InT *sIn = reinterpret_cast<InT *>(lds);
 
   const int tid = threadIdx.x;
   const int tx = blockIdx.x;
@@ -112,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         const int j = half + 2 * it;
         const unsigned gy = static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
         const unsigned off = gy * static_cast<unsigned>(w) + gx;
-        lds[j * CW + c] = load_sample<InT>(ref, off, in_scale);
-        lds[IR * CW + j * CW + c] = load_sample<InT>(dist, off, in_scale);
+        sIn[j * CW + c] = ref[off];
+        sIn[IR * CW + j * CW + c] = dist[off];
       }
     }
   }
@@ -127,12 +185,12 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   float acc[5][VB];
   float dacc[2][VB / 2];
   if (vact) {
-    const float *sx = lds + (vb * VB) * CW + vc;
-    const float *sy = sx + IR * CW;
+    const InT *sx = sIn + (vb * VB) * CW + vc;
+    const InT *sy = sx + IR * CW;
 #pragma unroll
     for (int j = 0; j < VB + 2 * R; ++j) {
-      const float x = sx[j * CW];
-      const float y = sy[j * CW];
+      const float x = to_float<InT>(sx[j * CW], in_scale);
+      const float y = to_float<InT>(sy[j * CW], in_scale);
       const float xx = x * x;
       const float yy = y * y;
       const float xy = x * y;
@@ -173,18 +231,41 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         }
       }
     }
+    settle(acc);
+    if constexpr (RD > 0)
+      settle(dacc);
   }
   __syncthreads(); // the input tile is dead from here on
 
-  // 3. vertical results to LDS: V[q][16][CWP], Vd[p][8][CWP]
   float *sV = lds;
-  float *sVd = lds + 5 * kTileH * CWP;
+  float *sVd = lds + kVdOff;
+  const int ty = tid & 15;
+  const int seg = tid >> 4;
+
+  // 3. round A: vertical results of x, y, x*x to LDS
   if (vact) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q)
+    for (int q = 0; q < kQA; ++q)
 #pragma unroll
       for (int i = 0; i < VB; ++i)
         sV[(q * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
+  }
+  __syncthreads();
+
+  // 4. horizontal pass of x, y, x*x: thread (ty, seg) owns tile row ty and
+  //    columns seg*7 .. seg*7+6
+  float fa[kQA][HB];
+  hpass<R, kQA, HB>(sV, ty, seg, taps, fa);
+  settle(fa);
+  __syncthreads(); // round A's region is free
+
+  // 5. round B: y*y, x*y and the next scale's vertical low-pass to LDS
+  if (vact) {
+#pragma unroll
+    for (int q = kQA; q < 5; ++q)
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        sV[((q - kQA) * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
     if constexpr (RD > 0) {
 #pragma unroll
       for (int p = 0; p < 2; ++p)
@@ -195,37 +276,20 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads();
 
-  // 4. horizontal pass and statistic: thread (ty, seg) owns tile row ty and
-  //    columns seg*7 .. seg*7+6; the terms stay in registers.
-  const int ty = tid & 15;
-  const int seg = tid >> 4;
+  // 6. horizontal pass of y*y, x*y, then the statistic; the terms stay in
+  //    registers
   float tnum[HB], tden[HB];
   {
-    float f[5][HB];
-#pragma unroll
-    for (int q = 0; q < 5; ++q) {
-      const float *row = sV + (q * kTileH + ty) * CWP + seg * HB;
-      float v[HB + 2 * R];
-#pragma unroll
-      for (int j = 0; j < HB + 2 * R; ++j)
-        v[j] = row[j];
-#pragma unroll
-      for (int i = 0; i < HB; ++i) {
-        float a = tap(taps, 0, N) * v[i];
-#pragma unroll
-        for (int k = 1; k < N; ++k)
-          a = a + tap(taps, k, N) * v[i + k];
-        f[q][i] = a;
-      }
-    }
+    float fb[5 - kQA][HB];
+    hpass<R, 5 - kQA, HB>(sV, ty, seg, taps, fb);
 #pragma unroll
     for (int i = 0; i < HB; ++i)
-      pixel_terms(f[0][i], f[1][i], f[2][i], f[3][i], f[4][i], stat,
+      pixel_terms(fa[0][i], fa[1][i], fa[2][i], fb[0][i], fb[1][i], stat,
                   tnum[i], tden[i]);
   }
-  __syncthreads(); // every read of V is done: its region takes the terms
+  __syncthreads(); // every read of round B is done: its region takes the terms
 
-  // 5. terms to LDS as 32 sequences (row-major per row and component):
+  // 7. terms to LDS as 32 sequences (row-major per row and component):
   //    sT[2*ty + c][x], the order in which the row sums read them.
   float *sT = lds;
 #pragma unroll
@@ -234,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
     sT[(2 * ty + 1) * kTermPitch + seg * HB + i] = tden[i];
   }
 
-  // 6. next scale's planes: horizontal low-pass at even columns of the even
+  //    next scale's planes: horizontal low-pass at even columns of the even
   //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1.
   if constexpr (RD > 0) {
     const int yd = tid & 7;
@@ -265,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads(); // terms complete in LDS
 
-  // 7. terms to the strip's term buffer: groups of 4 columns, each group
+  // 8. terms to the strip's term buffer: groups of 4 columns, each group
   //    holding the 32 sequences' 4 values ([g][seq][4] floats); this tile's
   //    28 groups are one contiguous 14 KiB block.
   {
