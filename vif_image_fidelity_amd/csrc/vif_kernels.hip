@@ -104,23 +104,24 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
         a = a + tap(taps, k, N) * v[i + k];
       f[q][i] = a;
     }
+    // one quantity's row at a time: keeps the next row's loads from being
+    // hoisted here, which would hold them all in registers at once
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
 //
-// LDS is reused phase by phase so that a block needs about 24 KiB and six
-// blocks fit a CU:
-//   phases 1-2  input tile, native samples     [2][IR][CW] InT
-//   phases 3-4  vertical results of x, y, x*x  [3][kTileH][CWP]
-//   phases 5-6  vertical results of y*y, x*y   [2][kTileH][CWP]
-//               + the low-pass at even rows    [2][kTileH/2][CWP] at kVdOff
-//   phases 7-8  terms                          [kSeq][kTermPitch]
-//               + the low-pass (still)         at kVdOff
-// The horizontal pass therefore runs in two rounds (three quantities, then
-// two); the low-pass results of the vertical pass wait in registers until
-// the second round's write.
+// LDS is reused phase by phase so that a block needs about 24 KiB:
+//   phases 1-2  input tile, native samples       [2][IR][CW] InT
+//   phases 3-4  vertical results of x, y         [2][kTileH][CWP]
+//               + the low-pass at even rows      [2][kTileH/2][CWP]
+//   phases 5-6  vertical results of x*x, y*y, x*y [3][kTileH][CWP]
+//   phases 7-8  terms                            [kSeq][kTermPitch]
+// The horizontal pass therefore runs in two rounds (x, y and the next
+// scale's planes, then the three second moments); the second round's
+// vertical results wait in registers until its write.
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
@@ -134,16 +135,16 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   constexpr int CWP = CW + 1;        // odd pitch: conflict-free row reads
   constexpr int VB = 8;              // rows per thread in the vertical pass
   constexpr int HB = 7;              // outputs per thread, horizontal pass
-  constexpr int kQA = 3;             // quantities of the first round
+  constexpr int kQA = 2;             // quantities of the first round
   constexpr int kInFloats =
       (2 * IR * CW * static_cast<int>(sizeof(InT)) + 3) / 4;
-  constexpr int kVA = kQA * kTileH * CWP;
+  constexpr int kVd = RD > 0 ? 2 * (kTileH / 2) * CWP : 0;
+  constexpr int kVA = kQA * kTileH * CWP + kVd;
   constexpr int kVB = (5 - kQA) * kTileH * CWP;
   constexpr int kT = kSeq * kTermPitch;
-  constexpr int kVdOff = kVB > kT ? kVB : kT;
-  constexpr int kVd = RD > 0 ? 2 * (kTileH / 2) * CWP : 0;
-  constexpr int kLds0 = kVA > kVdOff + kVd ? kVA : kVdOff + kVd;
-  constexpr int kLds = kLds0 > kInFloats ? kLds0 : kInFloats;
+  constexpr int kL0 = kVA > kVB ? kVA : kVB;
+  constexpr int kL1 = kL0 > kT ? kL0 : kT;
+  constexpr int kLds = kL1 > kInFloats ? kL1 : kInFloats;
   static_assert(CW <= 128, "one thread per vertical column in two halves");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
   static_assert(kTileH == 2 * VB, "two row blocks");
@@ -155,7 +156,6 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   const int strip = blockIdx.y;
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
-
   // 1. input tile [IR][CW] for ref then dist.  Waves 0-1 load the even
   //    rows, waves 2-3 the odd ones: the row (and its mirror) is uniform in a
   //    wave, and all of a thread's loads are issued before the first use.
@@ -238,34 +238,18 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   __syncthreads(); // the input tile is dead from here on
 
   float *sV = lds;
-  float *sVd = lds + kVdOff;
+  float *sVd = lds + kQA * kTileH * CWP;
   const int ty = tid & 15;
   const int seg = tid >> 4;
 
-  // 3. round A: vertical results of x, y, x*x to LDS
+  // 3. round A: vertical results of x, y and the next scale's vertical
+  //    low-pass to LDS
   if (vact) {
 #pragma unroll
     for (int q = 0; q < kQA; ++q)
 #pragma unroll
       for (int i = 0; i < VB; ++i)
         sV[(q * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
-  }
-  __syncthreads();
-
-  // 4. horizontal pass of x, y, x*x: thread (ty, seg) owns tile row ty and
-  //    columns seg*7 .. seg*7+6
-  float fa[kQA][HB];
-  hpass<R, kQA, HB>(sV, ty, seg, taps, fa);
-  settle(fa);
-  __syncthreads(); // round A's region is free
-
-  // 5. round B: y*y, x*y and the next scale's vertical low-pass to LDS
-  if (vact) {
-#pragma unroll
-    for (int q = kQA; q < 5; ++q)
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-        sV[((q - kQA) * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
     if constexpr (RD > 0) {
 #pragma unroll
       for (int p = 0; p < 2; ++p)
@@ -276,27 +260,11 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads();
 
-  // 6. horizontal pass of y*y, x*y, then the statistic; the terms stay in
-  //    registers
-  float tnum[HB], tden[HB];
-  {
-    float fb[5 - kQA][HB];
-    hpass<R, 5 - kQA, HB>(sV, ty, seg, taps, fb);
-#pragma unroll
-    for (int i = 0; i < HB; ++i)
-      pixel_terms(fa[0][i], fa[1][i], fa[2][i], fb[0][i], fb[1][i], stat,
-                  tnum[i], tden[i]);
-  }
-  __syncthreads(); // every read of round B is done: its region takes the terms
-
-  // 7. terms to LDS as 32 sequences (row-major per row and component):
-  //    sT[2*ty + c][x], the order in which the row sums read them.
-  float *sT = lds;
-#pragma unroll
-  for (int i = 0; i < HB; ++i) {
-    sT[(2 * ty) * kTermPitch + seg * HB + i] = tnum[i];
-    sT[(2 * ty + 1) * kTermPitch + seg * HB + i] = tden[i];
-  }
+  // 4. horizontal pass of x, y: thread (ty, seg) owns tile row ty and
+  //    columns seg*7 .. seg*7+6.
+  float fa[kQA][HB];
+  hpass<R, kQA, HB>(sV, ty, seg, taps, fa);
+  settle(fa);
 
   //    next scale's planes: horizontal low-pass at even columns of the even
   //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1.
@@ -326,6 +294,40 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         }
       }
     }
+  }
+  __syncthreads(); // round A's region is free
+
+  // 5. round B: vertical results of x*x, y*y, x*y to LDS
+  if (vact) {
+#pragma unroll
+    for (int q = kQA; q < 5; ++q)
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        sV[((q - kQA) * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
+  }
+  __syncthreads();
+
+  // 6. horizontal pass of x*x, y*y, x*y, then the statistic; the terms stay
+  //    in registers
+  float tnum[HB], tden[HB];
+  {
+    float fb[5 - kQA][HB];
+    hpass<R, 5 - kQA, HB>(sV, ty, seg, taps, fb);
+    settle(fb);
+#pragma unroll
+    for (int i = 0; i < HB; ++i)
+      pixel_terms(fa[0][i], fa[1][i], fb[0][i], fb[1][i], fb[2][i], stat,
+                  tnum[i], tden[i]);
+  }
+  __syncthreads(); // every read of round B is done: its region takes the terms
+
+  // 7. terms to LDS as 32 sequences (row-major per row and component):
+  //    sT[2*ty + c][x], the order in which the row sums read them.
+  float *sT = lds;
+#pragma unroll
+  for (int i = 0; i < HB; ++i) {
+    sT[(2 * ty) * kTermPitch + seg * HB + i] = tnum[i];
+    sT[(2 * ty + 1) * kTermPitch + seg * HB + i] = tden[i];
   }
   __syncthreads(); // terms complete in LDS
 
