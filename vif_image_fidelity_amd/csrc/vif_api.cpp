@@ -13,7 +13,12 @@
 // on the slot's stream (vif_submit_host).
 // Consecutive frames rotate over the slots, so one frame's small
 // scales and row sums overlap the next frame's scale 0, which fills the
-// GPU.  A submission is six runtime calls: five launches and one event.
+// GPU.  When one scale-0 kernel covers the GPU twice over, consecutive
+// frames' scale-0 kernels run one after the other (a stream wait on the
+// previous frame's scale-0 event): two of them side by side gain nothing,
+// and each launch's duration then is its own.  A submission is six runtime
+// calls (five launches, one event), plus an event and that stream wait when
+// the scale-0 kernels are ordered.
 //
 // The slot streams are blocking streams, so they are ordered after work on
 // the default stream (where a caller typically fills the frames); a caller
@@ -50,6 +55,7 @@ struct Slot {
   hipStream_t stream = nullptr;   // owned: all of the slot's work
   hipEvent_t submitted = nullptr; // on the caller's stream
   hipEvent_t done = nullptr;      // on the slot's stream, after the row sums
+  hipEvent_t s0_end = nullptr;    // on the slot's stream, after scale 0
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
 };
@@ -68,6 +74,7 @@ struct vif_ctx {
   int total_rows = 0;
   int row_base[kScales] = {};
   int rowsum_waves = 0;
+  bool order_scale0 = false; // consecutive frames' scale-0 kernels ordered
   vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
   long head = 0, tail = 0;      // submitted / collected frame counts
   float sums[8] = {};
@@ -155,6 +162,7 @@ void free_all(vif_ctx *c) {
       (void)hipHostFree(sl.rows_host);
     destroy_event(sl.submitted);
     destroy_event(sl.done);
+    destroy_event(sl.s0_end);
     for (auto &p : sl.prof) {
       destroy_event(p[0]);
       destroy_event(p[1]);
@@ -181,6 +189,12 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
     if (e == hipSuccess)
       e = hipStreamWaitEvent(st, sl.submitted, 0);
   }
+  // consecutive frames' scale-0 kernels run one after the other when each
+  // fills the GPU (the small scales and row sums of one frame still overlap
+  // the next frame's scale 0)
+  if (e == hipSuccess && ctx->order_scale0 && ctx->head > 0)
+    e = hipStreamWaitEvent(st, ctx->slots[(ctx->head - 1) % kDepth].s0_end,
+                           0);
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
     const void *in_ref = s == 0 ? ref : sl.pyr_ref[s];
@@ -197,6 +211,8 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
                              sl.terms[s], st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
+    if (e == hipSuccess && s == 0 && ctx->order_scale0)
+      e = hipEventRecord(sl.s0_end, st);
   }
   vifk::RowSumArgs ra = ctx->rowsum;
   for (int s = 0; s < kScales; ++s) {
@@ -391,6 +407,17 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
     c->rowsum.pair_base[s + 1] = c->rowsum.pair_base[s] + (g.strips + 1) / 2;
   }
   c->rowsum_waves = c->rowsum.pair_base[kScales];
+  // order consecutive scale-0 kernels when one covers the device's resident
+  // blocks at least twice: two side by side then gain nothing, and the wait
+  // (a cross-stream dependency, a few tens of microseconds of host time) is
+  // hidden behind the GPU.  Smaller frames leave CUs free and are host-bound,
+  // so their scale-0 kernels may overlap.
+  if (e == hipSuccess) {
+    int resident = 0;
+    e = vifk::scale0_resident_blocks(bpc, &resident);
+    c->order_scale0 =
+        e == hipSuccess && c->geom[0].tiles() >= 2 * static_cast<size_t>(resident);
+  }
   c->total_rows = rows;
   c->last_rows =
       static_cast<float *>(std::calloc(static_cast<size_t>(2) * rows, 4));
@@ -422,6 +449,8 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
       e = hipEventCreateWithFlags(&sl.submitted, hipEventDisableTiming);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&sl.s0_end, hipEventDisableTiming);
     if (e == hipSuccess)
       e = hipStreamCreate(&sl.stream); // blocking: ordered with the default
                                        // stream

@@ -87,6 +87,10 @@ hipError_t launch_scale(int scale, int bpc, const void *in_ref,
                         const StatArgs &stat, float *next_ref,
                         float *next_dist, float *terms, hipStream_t stream);
 
+// Blocks of the scale-0 kernel the current device keeps resident at once
+// (blocks per CU times CUs).
+hipError_t scale0_resident_blocks(int bpc, int *blocks);
+
 // Ordered row sums of all scales of one frame (`waves` = pair_base[4]).
 hipError_t launch_rowsum(const RowSumArgs &args, int waves,
                          hipStream_t stream);

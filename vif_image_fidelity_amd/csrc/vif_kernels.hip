@@ -472,6 +472,23 @@ hipError_t launch_scale(int scale, int bpc, const void *in_ref,
   return hipGetLastError();
 }
 
+hipError_t scale0_resident_blocks(int bpc, int *blocks) {
+  int per_cu = 0;
+  hipError_t e =
+      bpc == 8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     &per_cu, scale_kernel<8, 4, uint8_t>, kThreads, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     &per_cu, scale_kernel<8, 4, uint16_t>, kThreads, 0);
+  int dev = 0, cus = 0;
+  if (e == hipSuccess)
+    e = hipGetDevice(&dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev);
+  *blocks = per_cu * cus;
+  return e;
+}
+
 hipError_t launch_rowsum(const RowSumArgs &args, int waves,
                          hipStream_t stream) {
   rowsum_kernel<<<dim3(waves), dim3(64), 0, stream>>>(args);
