@@ -18,6 +18,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vif_oracle.c")
+_FSSIM_SRC = os.path.join(_HERE, "fssim_oracle.c")
 _LIB = os.path.join(_HERE, "libvif_oracle.so")
 
 CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
@@ -64,10 +65,12 @@ def make_options(options=None):
     return o
 
 
-def build(src=_SRC, out=_LIB):
-    """Compile the oracle C source into a shared library (default: in place)."""
+def build(src=_SRC, out=_LIB, fssim_src=_FSSIM_SRC):
+    """Compile the oracle C sources (the VIF oracle, possibly a mutated
+    copy, and the float SSIM oracle) into one shared library (default: in
+    place)."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc"] + CFLAGS + ["-I", _HERE, "-o", tmp, src, "-lm"]
+    cmd = ["gcc"] + CFLAGS + ["-I", _HERE, "-o", tmp, src, fssim_src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -127,6 +130,25 @@ class Oracle:
                                       ctypes.POINTER(Options), f64p, f32p,
                                       f32p]
         lib.vifo_score_ex.restype = ctypes.c_int
+        lib.fssimo_scale.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.fssimo_scale.restype = ctypes.c_int
+        lib.fssimo_decimated_size.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.fssimo_decimated_size.restype = ctypes.c_int
+        lib.fssimo_symmetric.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.fssimo_symmetric.restype = ctypes.c_int
+        lib.fssimo_decimate.argtypes = [f32p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, f32p]
+        lib.fssimo_decimate.restype = ctypes.c_int
+        lib.fssimo_taps.argtypes = [f32p]
+        lib.fssimo_taps.restype = None
+        lib.fssimo_filter.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p]
+        lib.fssimo_filter.restype = ctypes.c_int
+        lib.fssimo_pixel.argtypes = [ctypes.c_float] * 5
+        lib.fssimo_pixel.restype = ctypes.c_float
+        lib.fssimo_score.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     f64p, f32p, f32p, f64p]
+        lib.fssimo_score.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -263,6 +285,76 @@ class Oracle:
         return out, sums
 
 
+    # ----------------------------------------------------- float SSIM
+    def fssim_scale(self, w, h):
+        return int(self.lib.fssimo_scale(int(w), int(h)))
+
+    def fssim_decimated_size(self, n, f):
+        return int(self.lib.fssimo_decimated_size(int(n), int(f)))
+
+    def fssim_symmetric(self, i, n):
+        return int(self.lib.fssimo_symmetric(int(i), int(n)))
+
+    def fssim_decimate(self, plane, f):
+        plane = np.ascontiguousarray(plane, dtype=np.float32)
+        h, w = plane.shape
+        ow = self.fssim_decimated_size(w, f)
+        oh = self.fssim_decimated_size(h, f)
+        out = np.empty((oh, ow), dtype=np.float32)
+        if self.lib.fssimo_decimate(_fp(plane), w, h, int(f), _fp(out)) != 0:
+            raise ValueError("fssimo_decimate rejected its arguments")
+        return out
+
+    def fssim_taps(self):
+        t = np.zeros(11, dtype=np.float32)
+        self.lib.fssimo_taps(_fp(t))
+        return t
+
+    def fssim_filter(self, plane):
+        plane = np.ascontiguousarray(plane, dtype=np.float32)
+        h, w = plane.shape
+        out = np.empty((h, w), dtype=np.float32)
+        if self.lib.fssimo_filter(_fp(plane), w, h, _fp(out)) != 0:
+            raise ValueError("fssimo_filter rejected its arguments")
+        return out
+
+    def fssim_pixel(self, mu1, mu2, xx, yy, xy):
+        return np.float32(self.lib.fssimo_pixel(
+            *[float(np.float32(v)) for v in (mu1, mu2, xx, yy, xy)]))
+
+    def fssim_score(self, ref, dist, bpc, want=False):
+        """Return out[2] (float_ssim, factor); with want=True also the SSIM
+        map, the decimated planes (2, h', w') and the fp64 row sums."""
+        ref = np.ascontiguousarray(ref)
+        dist = np.ascontiguousarray(dist)
+        if ref.shape != dist.shape or ref.ndim != 2:
+            raise ValueError("ref and dist must be equal 2-D planes")
+        wantt = np.uint8 if bpc == 8 else np.uint16
+        if ref.dtype != wantt or dist.dtype != wantt:
+            raise ValueError("bpc %d needs %s samples"
+                             % (bpc, np.dtype(wantt).name))
+        h, w = ref.shape
+        f = self.fssim_scale(w, h)
+        ow = self.fssim_decimated_size(w, f) if f > 1 else w
+        oh = self.fssim_decimated_size(h, f) if f > 1 else h
+        out = np.zeros(2, dtype=np.float64)
+        smap = np.zeros((oh, ow), dtype=np.float32) if want else None
+        planes = np.zeros((2, oh, ow), dtype=np.float32) if want else None
+        rows = np.zeros(oh, dtype=np.float64) if want else None
+        rc = self.lib.fssimo_score(
+            ref.ctypes.data, dist.ctypes.data, w, h, int(bpc),
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            _fp(smap) if want else None, _fp(planes) if want else None,
+            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+            if want else None)
+        if rc != 0:
+            raise ValueError("fssimo_score rejected its arguments (rc=%d)"
+                             % rc)
+        if want:
+            return out, smap, planes, rows
+        return out
+
+
 def _load():
     global _default
     if _default is None:
@@ -314,3 +406,35 @@ def total_rows(w, h):
 
 def score(ref, dist, bpc, want_rows=False, options=None):
     return _load().score(ref, dist, bpc, want_rows, options)
+
+
+def fssim_scale(w, h):
+    return _load().fssim_scale(w, h)
+
+
+def fssim_decimated_size(n, f):
+    return _load().fssim_decimated_size(n, f)
+
+
+def fssim_symmetric(i, n):
+    return _load().fssim_symmetric(i, n)
+
+
+def fssim_decimate(plane, f):
+    return _load().fssim_decimate(plane, f)
+
+
+def fssim_taps():
+    return _load().fssim_taps()
+
+
+def fssim_filter(plane):
+    return _load().fssim_filter(plane)
+
+
+def fssim_pixel(mu1, mu2, xx, yy, xy):
+    return _load().fssim_pixel(mu1, mu2, xx, yy, xy)
+
+
+def fssim_score(ref, dist, bpc, want=False):
+    return _load().fssim_score(ref, dist, bpc, want)

@@ -17,6 +17,7 @@ sys.path.insert(0, HERE)
 import oracle  # noqa: E402
 import test_oracle_pins as P  # noqa: E402
 import test_oracle_options as Q  # noqa: E402
+import test_fssim_oracle as S  # noqa: E402
 
 
 def battery(orc):
@@ -92,6 +93,30 @@ def battery(orc):
     cases.append(("opt_pipe", lambda:
                   Q.test_pipeline_with_options_vs_fp64_definition(orc, 4.7,
                                                                   0.8)))
+    # float SSIM
+    cases += [
+        ("fs_scale", lambda: S.test_scale_examples_from_the_page(orc)),
+        ("fs_round", lambda: S.test_scale_rounds_half_away_from_zero(orc, 384,
+                                                                     1000, 2)),
+        ("fs_size", lambda: S.test_decimated_size(orc, 1921, 4, 481)),
+        ("fs_sym", lambda: S.test_symmetric_border_matches_numpy(orc, 7)),
+        ("fs_dec3", lambda: S.test_decimation_is_the_exact_sum_rounded_once(
+            orc, 3, 8)),
+        ("fs_dec4", lambda: S.test_decimation_is_the_exact_sum_rounded_once(
+            orc, 4, 10)),
+        ("fs_pow2", lambda: S.test_power_of_two_factor_is_the_plain_mean(orc,
+                                                                         4)),
+        ("fs_win", lambda: S.test_decimation_window_position_and_offsets(orc)),
+        ("fs_taps", lambda: S.test_gaussian_taps(orc)),
+        ("fs_filt", lambda: S.test_filter_interior_impulse_and_border(orc)),
+        ("fs_self", lambda: S.test_frame_against_itself_scores_exactly_one(
+            orc)),
+        ("fs_flat", lambda: S.test_flat_frames_closed_form(orc, 10, 240)),
+        ("fs_fp64", lambda: S.test_score_vs_fp64_definition(orc, (120, 160), 8,
+                                                            1)),
+        ("fs_auto",
+         lambda: S.test_score_decimates_both_planes_with_the_auto_factor(orc)),
+    ]
     for opt in ({"kernelscale": 2.0}, {"sigma_nsq": -1.0},
                 {"enhn_gain_limit": -0.5}):
         cases.append(("opt_bad_%s" % list(opt)[0],

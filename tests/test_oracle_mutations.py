@@ -114,21 +114,63 @@ MUTANTS = [
 ]
 
 
+# Mutants of the float SSIM oracle (fssim_oracle.c).
+FSSIM_MUTANTS = [
+    ("fs_scale_floor", "const int s = (int)round((double)m / 256.0);",
+     "const int s = (int)floor((double)m / 256.0);"),
+    ("fs_scale_by_max", "const int m = w < h ? w : h;",
+     "const int m = w > h ? w : h;"),
+    ("fs_size_no_odd", "return n / f + (n & 1);", "return n / f;"),
+    ("fs_mirror_whole_sample", "        m = p - 1 - m;\n",
+     "        m = p - 2 - m;\n"),
+    ("fs_tap_wrong", "const float tap = 1.0f / (float)(f * f);",
+     "const float tap = 1.0f / (float)(f * f + 1);"),
+    ("fs_window_centred_odd", "const int hi = f / 2 - (f % 2 == 0 ? 1 : 0);",
+     "const int hi = f / 2;"),
+    ("fs_window_origin", "const int yy = fssimo_symmetric(y * f + dy, h);",
+     "const int yy = fssimo_symmetric(y * f + dy + 1, h);"),
+    ("fs_sum_fp32", "            double sum = 0.0;\n            for (int dy",
+     "            float sum = 0.0f;\n            for (int dy"),
+    ("fs_sigma_2", "const double sigma = 1.5;", "const double sigma = 2.0;"),
+    ("fs_filter_no_vertical",
+     "acc = acc + t[k] * src[(size_t)yy * w + x];",
+     "acc = acc + t[k] * src[(size_t)y * w + x];"),
+    ("fs_c2_wrong", "(float)((0.03 * 255.0) * (0.03 * 255.0));",
+     "(float)((0.01 * 255.0) * (0.01 * 255.0));"),
+    ("fs_sigma12_sign", "const float s12 = xy - m12;",
+     "const float s12 = m12 - xy;"),
+    ("fs_num_no_c1", "const float num = (2.0f * m12 + c1)",
+     "const float num = (2.0f * m12)"),
+    ("fs_mean_fp64", "out[0] = (double)(float)(total / (double)n);",
+     "out[0] = total / (double)n;"),
+    ("fs_ref_twice", "normalise(dist, w, h, bpc, Y0);",
+     "normalise(ref, w, h, bpc, Y0);"),
+    ("fs_no_decimation", "    if (f > 1) {\n        if (fssimo_decimate",
+     "    if (f > 1000) {\n        if (fssimo_decimate"),
+]
+
+
 def _run(path):
     return subprocess.run([sys.executable, os.path.join(HERE,
                                                         "mutant_battery.py"),
                            path], capture_output=True, text=True, timeout=600)
 
 
-def _build_mutant(tmp, name, old, new):
+FSSIM_SRC = os.path.join(ROOT, "oracle", "fssim_oracle.c")
+
+
+def _build_mutant(tmp, name, old, new, fssim=False):
     import oracle
-    src = open(SRC).read()
+    src = open(FSSIM_SRC if fssim else SRC).read()
     assert src.count(old) >= 1, "mutation %s does not apply" % name
     mutated = src.replace(old, new, 1)
     cpath = os.path.join(tmp, name + ".c")
     with open(cpath, "w") as f:
         f.write(mutated)
-    return oracle.build(src=cpath, out=os.path.join(tmp, name + ".so"))
+    out = os.path.join(tmp, name + ".so")
+    if fssim:
+        return oracle.build(out=out, fssim_src=cpath)
+    return oracle.build(src=cpath, out=out)
 
 
 def test_real_oracle_passes_battery():
@@ -142,6 +184,8 @@ def test_every_mutant_is_caught(tmp_path):
     tmp = str(tmp_path)
     libs = [(name, _build_mutant(tmp, name, old, new))
             for (name, old, new) in MUTANTS]
+    libs += [(name, _build_mutant(tmp, name, old, new, fssim=True))
+             for (name, old, new) in FSSIM_MUTANTS]
     with ThreadPoolExecutor(max_workers=4) as ex:
         results = list(ex.map(lambda nl: (nl[0], _run(nl[1])), libs))
     survivors = [name for name, r in results if r.returncode == 0]
