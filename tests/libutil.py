@@ -23,7 +23,7 @@ def header_functions():
         text = open(os.path.join(INCLUDE, fn)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
-        for m in re.finditer(r"\b(vif_[a-z0-9_]+)\s*\(", text):
+        for m in re.finditer(r"\b((?:vif|fssim)_[a-z0-9_]+)\s*\(", text):
             names.append(m.group(1))
     return sorted(set(names))
 

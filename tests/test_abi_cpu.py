@@ -188,3 +188,32 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_fssim_taps_equal_oracle_taps(lib, orc):
+    """The library's SSIM window taps and the oracle's, written separately,
+    agree bit for bit and are symmetric bit for bit (the kernel reads
+    t[min(k, 10-k)])."""
+    import vif_image_fidelity_amd as V
+    a = V.fssim_taps()
+    assert a.tobytes() == orc.fssim_taps().tobytes()
+    assert a.tobytes() == a[::-1].copy().tobytes()
+
+
+@pytest.mark.parametrize("w,h,bpc", [(0, 5, 8), (5, 0, 8), (-1, 5, 8),
+                                     (16, 16, 9), (16, 16, 7), (16, 16, 0),
+                                     (1 << 14, 1 << 14, 8)])
+def test_fssim_create_rejects_bad_arguments(lib, w, h, bpc):
+    from vif_image_fidelity_amd import _lib
+    assert not _lib.fssim_create(w, h, bpc)
+    assert _lib.vif_errno() == _lib.VIF_EINVAL
+
+
+def test_fssim_null_context_calls(lib):
+    from vif_image_fidelity_amd import _lib
+    out = np.zeros(2)
+    assert _lib.fssim_score(None, None, None, out) == _lib.VIF_EINVAL
+    assert _lib.fssim_collect(None, out) == _lib.VIF_EINVAL
+    assert _lib.fssim_pending(None) == _lib.VIF_EINVAL
+    assert _lib.fssim_geometry(None, np.zeros(3, np.int32)) == _lib.VIF_EINVAL
+    _lib.fssim_destroy(None)

@@ -1,11 +1,13 @@
-"""MI355X-native float VIF (visual information fidelity) feature.
+"""MI355X-native float VIF (visual information fidelity) feature, and the
+float SSIM feature with its exact decimation.
 
 ``Vif(w, h, bpc)`` wraps one scoring context of the C-ABI library
-(include/vif.h).  Frames are device buffers (torch tensors on a ROCm
-device, or raw device pointers); every step of the feature runs in the
-library's HIP kernels for gfx950, and torch only supplies memory and
-streams.  There is no CPU fallback: if the library is not built, using
-``Vif`` raises.
+(include/vif.h); ``FloatSsim(w, h, bpc)`` one of include/fssim.h.  Frames
+are device buffers (torch tensors on a ROCm device, or raw device
+pointers); every step of either feature runs in the library's HIP kernels
+for gfx950, and torch only supplies memory and streams.  There is no CPU
+fallback: if the library is not built, using ``Vif`` or ``FloatSsim``
+raises.
 
 The synthetic workload generators live in ``vif_image_fidelity_amd.synth``
 and need neither the library nor a GPU.
@@ -14,11 +16,14 @@ import numpy as np
 
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
-                   DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH)
+                   DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH,
+                   FSSIM_KERNEL_KINDS, FSSIM_QUEUE_DEPTH)
 
-__all__ = ["Vif", "VifError", "taps", "make_options", "DEFAULT_OPTIONS",
+__all__ = ["Vif", "VifError", "FloatSsim", "fssim_taps", "taps",
+           "make_options", "DEFAULT_OPTIONS",
            "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
-           "KERNEL_KINDS", "QUEUE_DEPTH"]
+           "KERNEL_KINDS", "QUEUE_DEPTH", "FSSIM_KERNEL_KINDS",
+           "FSSIM_QUEUE_DEPTH"]
 
 # Defaults of struct vif_options (include/vif.h states each option's
 # meaning and range).
@@ -237,6 +242,134 @@ class Vif:
     def close(self):
         if getattr(self, "_ctx", None):
             _lib.vif_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def fssim_taps():
+    """The 11 fp32 SSIM window taps as the library passes them."""
+    buf = np.zeros(_lib.FSSIM_TAPS, dtype=np.float32)
+    n = _lib.fssim_taps(buf)
+    if n < 0:
+        raise VifError(n, "fssim_taps")
+    return buf
+
+
+class FloatSsim:
+    """One float SSIM scoring context for w x h frames of bpc bits (8, 10,
+    12, 16).  The frame is decimated by factor() first when that is above
+    1; geometry() gives (factor, w', h')."""
+
+    def __init__(self, w, h, bpc, stream=None):
+        self.w, self.h, self.bpc = int(w), int(h), int(bpc)
+        ctx = _lib.fssim_create(self.w, self.h, self.bpc)
+        if not ctx:
+            raise VifError(_lib.vif_errno(), "fssim_create")
+        self._ctx = ctx
+        g = np.zeros(3, dtype=np.int32)
+        rc = _lib.fssim_geometry(ctx, g)
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_geometry")
+        self.factor, self.ow, self.oh = (int(v) for v in g)
+        if stream is not None:
+            self.set_stream(stream)
+
+    def geometry(self):
+        return self.factor, self.ow, self.oh
+
+    def set_stream(self, stream):
+        ptr = getattr(stream, "cuda_stream", stream)
+        rc = _lib.fssim_set_stream(self._ctx, ptr)
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_set_stream")
+
+    def _check_frame(self, t):
+        if hasattr(t, "shape"):
+            if tuple(t.shape) != (self.h, self.w):
+                raise ValueError("frame shape %s, context is (%d, %d)"
+                                 % (tuple(t.shape), self.h, self.w))
+            want = 1 if self.bpc == 8 else 2
+            if t.element_size() != want:
+                raise ValueError("bpc %d needs %d-byte samples"
+                                 % (self.bpc, want))
+
+    def score(self, ref, dist):
+        """Score one pair; returns float64[2]: float_ssim, factor."""
+        self._check_frame(ref)
+        self._check_frame(dist)
+        out = np.zeros(2, dtype=np.float64)
+        rc = _lib.fssim_score(self._ctx, _ptr(ref), _ptr(dist), out)
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_score")
+        return out
+
+    def submit(self, ref, dist):
+        self._check_frame(ref)
+        self._check_frame(dist)
+        rc = _lib.fssim_submit(self._ctx, _ptr(ref), _ptr(dist))
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_submit")
+
+    def collect(self):
+        out = np.zeros(2, dtype=np.float64)
+        rc = _lib.fssim_collect(self._ctx, out)
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_collect")
+        return out
+
+    def pending(self):
+        return _lib.fssim_pending(self._ctx)
+
+    def row_sums(self):
+        rows = np.zeros(self.oh, dtype=np.float64)
+        rc = _lib.fssim_get_row_sums(self._ctx, rows, self.oh)
+        if rc < 0:
+            raise VifError(rc, "fssim_get_row_sums")
+        return rows
+
+    def ssim_map(self):
+        m = np.zeros((self.oh, self.ow), dtype=np.float32)
+        rc = _lib.fssim_get_map(self._ctx, m, m.size)
+        if rc < 0:
+            raise VifError(int(rc), "fssim_get_map")
+        return m
+
+    def planes(self):
+        p = np.zeros((2, self.oh, self.ow), dtype=np.float32)
+        rc = _lib.fssim_get_planes(self._ctx, p, p.size)
+        if rc < 0:
+            raise VifError(int(rc), "fssim_get_planes")
+        return p
+
+    def set_profiling(self, kinds=0x7):
+        rc = _lib.fssim_set_profiling(self._ctx, int(kinds))
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_set_profiling")
+
+    def kernel_times(self):
+        k = len(FSSIM_KERNEL_KINDS)
+        ms = np.zeros(k, dtype=np.float64)
+        n = np.zeros(k, dtype=np.int64)
+        rc = _lib.fssim_get_kernel_times(self._ctx, ms, n, k)
+        if rc < 0:
+            raise VifError(rc, "fssim_get_kernel_times")
+        return {kk: (float(ms[i]), int(n[i]))
+                for i, kk in enumerate(FSSIM_KERNEL_KINDS)}
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            _lib.fssim_destroy(self._ctx)
             self._ctx = None
 
     def __del__(self):

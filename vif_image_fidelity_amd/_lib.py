@@ -1,4 +1,5 @@
-"""ctypes binding of libvif_amd.so (include/vif.h, include/vif_selftest.h).
+"""ctypes binding of libvif_amd.so (include/vif.h, include/vif_selftest.h,
+include/fssim.h).
 
 Argument marshalling only: every step of the feature runs in the library's
 HIP kernels.  The functions keep the C names.  Loading fails loudly when the
@@ -19,6 +20,9 @@ MAX_TAPS = 17
 QUEUE_DEPTH = 3
 NDEBUG = 15
 KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
+FSSIM_TAPS = 11
+FSSIM_QUEUE_DEPTH = 3
+FSSIM_KERNEL_KINDS = ("decimate", "ssim", "rowsum")
 DEBUG_NAMES = ("vif_scale0", "vif_scale1", "vif_scale2", "vif_scale3",
                "vif", "vif_num", "vif_den",
                "vif_num_scale0", "vif_den_scale0", "vif_num_scale1",
@@ -88,6 +92,20 @@ def load():
         "vif_selftest_statistic": ([vp, vp, vp, vp, vp, ctypes.c_long,
                                     ctypes.c_double, ctypes.c_double, vp, vp,
                                     vp], ip),
+        "fssim_create": ([ip, ip, ip], vp),
+        "fssim_destroy": ([vp], None),
+        "fssim_geometry": ([vp, ctypes.POINTER(ctypes.c_int)], ip),
+        "fssim_score": ([vp, vp, vp, dp], ip),
+        "fssim_submit": ([vp, vp, vp], ip),
+        "fssim_collect": ([vp, dp], ip),
+        "fssim_pending": ([vp], ip),
+        "fssim_set_stream": ([vp, vp], ip),
+        "fssim_get_row_sums": ([vp, dp, ip], ip),
+        "fssim_get_map": ([vp, fp, ctypes.c_long], ctypes.c_long),
+        "fssim_get_planes": ([vp, fp, ctypes.c_long], ctypes.c_long),
+        "fssim_taps": ([fp], ip),
+        "fssim_set_profiling": ([vp, ip], ip),
+        "fssim_get_kernel_times": ([vp, dp, lp, ip], ip),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -108,7 +126,12 @@ def exported_symbols():
             "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
             "vif_selftest_log2", "vif_selftest_ratios",
-            "vif_selftest_statistic"]
+            "vif_selftest_statistic",
+            "fssim_create", "fssim_destroy", "fssim_geometry", "fssim_score",
+            "fssim_submit", "fssim_collect", "fssim_pending",
+            "fssim_set_stream", "fssim_get_row_sums", "fssim_get_map",
+            "fssim_get_planes", "fssim_taps", "fssim_set_profiling",
+            "fssim_get_kernel_times"]
 
 
 # ------------------------------------------------------- C-named wrappers
@@ -200,6 +223,67 @@ def vif_errno():
 
 def vif_strerror(code):
     return load().vif_strerror(int(code)).decode()
+
+
+def fssim_create(w, h, bpc):
+    return load().fssim_create(int(w), int(h), int(bpc))
+
+
+def fssim_destroy(ctx):
+    load().fssim_destroy(ctx)
+
+
+def fssim_geometry(ctx, geom):
+    """geom: a contiguous int32 numpy array of 3."""
+    return load().fssim_geometry(
+        ctx, ctypes.cast(geom.ctypes.data, ctypes.POINTER(ctypes.c_int)))
+
+
+def fssim_score(ctx, ref_ptr, dist_ptr, out):
+    return load().fssim_score(ctx, ref_ptr, dist_ptr, _dptr(out))
+
+
+def fssim_submit(ctx, ref_ptr, dist_ptr):
+    return load().fssim_submit(ctx, ref_ptr, dist_ptr)
+
+
+def fssim_collect(ctx, out):
+    return load().fssim_collect(ctx, _dptr(out))
+
+
+def fssim_pending(ctx):
+    return load().fssim_pending(ctx)
+
+
+def fssim_set_stream(ctx, stream_ptr):
+    return load().fssim_set_stream(ctx, stream_ptr)
+
+
+def fssim_get_row_sums(ctx, rows, capacity):
+    return load().fssim_get_row_sums(ctx, _dptr(rows), int(capacity))
+
+
+def fssim_get_map(ctx, smap, capacity):
+    return load().fssim_get_map(ctx, _fptr(smap), int(capacity))
+
+
+def fssim_get_planes(ctx, planes, capacity):
+    return load().fssim_get_planes(ctx, _fptr(planes), int(capacity))
+
+
+def fssim_taps(taps):
+    return load().fssim_taps(_fptr(taps))
+
+
+def fssim_set_profiling(ctx, kinds):
+    return load().fssim_set_profiling(ctx, int(kinds))
+
+
+def fssim_get_kernel_times(ctx, ms, launches, capacity):
+    return load().fssim_get_kernel_times(
+        ctx, _dptr(ms), ctypes.cast(launches.ctypes.data,
+                                    ctypes.POINTER(ctypes.c_long)),
+        int(capacity))
 
 
 def _fptr(a):

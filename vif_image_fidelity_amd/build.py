@@ -1,4 +1,5 @@
-"""Builds libvif_amd.so (the C-ABI library of include/vif.h) in-tree.
+"""Builds libvif_amd.so (the C-ABI library of include/vif.h and
+include/fssim.h) in-tree.
 
   python -m vif_image_fidelity_amd.build
 
@@ -18,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvif_amd.so")
 
 SOURCES = ["vif_kernels.hip", "vif_selftest.hip", "vif_api.cpp",
-           "vif_taps.cpp", "vif_options.cpp"]
+           "vif_taps.cpp", "vif_options.cpp", "fssim_kernels.hip",
+           "fssim_api.cpp", "fssim_taps.cpp"]
 
 ARCH = "gfx950"
 

@@ -1,0 +1,429 @@
+// fssim_kernels.hip -- HIP kernels of the float SSIM feature for gfx950.
+//
+// Three kernels per frame pair:
+//   decimate_kernel  both planes decimated by the factor f > 1: the f x f
+//                    box window of tap fl32(1 / f^2) at (x*f, y*f), each
+//                    product an fp32 value, summed exactly in fp64 and
+//                    rounded to fp32 once (Research-2130 "float_ssim
+//                    decimation on the SYCL device", Sources and Findings);
+//   ssim_kernel      the 11-tap Gaussian window of x, y, x*x, y*y, x*y
+//                    (vertical pass, then horizontal) and the per-pixel
+//                    SSIM value, stored column-major;
+//   rowsum_kernel    each row's values added left to right in fp64, one
+//                    lane per row, straight into the context's pinned host
+//                    buffer.
+// Every border index goes through the symmetric mirror of period 2n
+// (Research-2130, Sources), so planes of any size >= 1 stay in bounds.
+//
+// Exactness of the decimation in any order.  Samples are multiples of 2^-8
+// below 256; for f <= 128 the tap is at least 2^-14, so a non-zero product
+// is at least 2^-22 and a multiple of 2^-45, and all products of a window
+// add up to less than 256 (Research-2130, Findings).  Every partial sum of
+// any subset of them is therefore a multiple of 2^-45 below 2^8, which fits
+// the 53 bits of a double: each fp64 addition is exact whatever the order.
+// The kernel adds each column's products over the window's rows first and
+// then the columns; the result is the CPU's exact sum, and one conversion
+// to fp32 (round to nearest even) gives the CPU's plane bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fssim_internal.h"
+
+namespace fssimk {
+
+// Index into [0, n) by the symmetric border of period 2n: -1 -> 0,
+// -2 -> 1, n -> n-1, n+1 -> n-2, repeating for indices further out.
+__device__ __forceinline__ int sym_index(int i, int n) {
+  if (static_cast<unsigned>(i) < static_cast<unsigned>(n))
+    return i;
+  const int p = 2 * n;
+  int m = i % p;
+  m = m < 0 ? m + p : m;
+  return m < n ? m : p - 1 - m;
+}
+
+// A sample normalised to fp32: 8-bit as it is, wider samples times 1/4,
+// 1/16 or 1/256 (exact).
+__device__ __forceinline__ float norm(uint8_t v, float) {
+  return static_cast<float>(v);
+}
+__device__ __forceinline__ float norm(uint16_t v, float s) {
+  return static_cast<float>(v) * s;
+}
+__device__ __forceinline__ float norm(float v, float) { return v; }
+
+// Four consecutive samples from row + c.  kVec: one aligned 4- or 8-byte
+// load (the host checked the alignment and that c + 3 < w); otherwise one
+// load per sample, those at or beyond w read as 0 (never used).
+template <bool kVec>
+__device__ __forceinline__ void load4(const uint8_t *p, int c, int w,
+                                      float s, float (&v)[4]) {
+  if constexpr (kVec) {
+    const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = static_cast<float>((u >> (8 * j)) & 0xffu);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = c + j < w ? norm(p[j], s) : 0.0f;
+  }
+}
+
+template <bool kVec>
+__device__ __forceinline__ void load4(const uint16_t *p, int c, int w,
+                                      float s, float (&v)[4]) {
+  if constexpr (kVec) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    v[0] = norm(static_cast<uint16_t>(u.x & 0xffffu), s);
+    v[1] = norm(static_cast<uint16_t>(u.x >> 16), s);
+    v[2] = norm(static_cast<uint16_t>(u.y & 0xffffu), s);
+    v[3] = norm(static_cast<uint16_t>(u.y >> 16), s);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = c + j < w ? norm(p[j], s) : 0.0f;
+  }
+}
+
+// One block: decimated row y = blockIdx.y, decimated columns
+// [x0, x1) with x0 = blockIdx.x * xpb.  Their windows (mirrored) read plane
+// columns [lo, hi]; thread t covers columns a + 4t .. a + 4t + 3 with a = lo
+// rounded down to a multiple of 4.
+//   1. every thread adds, for each of its 4 columns, the products of the f
+//      window rows (mirrored row indices are uniform in the block) into an
+//      fp64 column sum, for both planes; the sums go to LDS;
+//   2. decimated pixel x adds the column sums of its f window columns
+//      (mirrored) and rounds the sum to fp32 once.
+template <typename InT, bool kVec>
+__global__ __launch_bounds__(kDecThreads) void decimate_kernel(
+    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
+    int f, float tap, float in_scale, int ow, int xpb,
+    float *__restrict__ dref, float *__restrict__ ddist) {
+  __shared__ double cs[2][kDecSpan];
+  const int t = threadIdx.x;
+  const int y = blockIdx.y;
+  const int half = f / 2;
+  const int x0 = blockIdx.x * xpb;
+  const int x1 = min(ow, x0 + xpb);
+  // the f columns left of the first window cover the mirror images of the
+  // columns right of the plane (which lie within f of its edge)
+  const int lo = max(0, x0 * f - half - f);
+  const int a = lo & ~3;
+  const int hi = min(w - 1, (x1 - 1) * f - half + f - 1);
+  const int c = a + 4 * t;
+  double sr[4] = {0.0, 0.0, 0.0, 0.0};
+  double sd[4] = {0.0, 0.0, 0.0, 0.0};
+  if (c <= hi) {
+    const int ry = y * f - half;
+#pragma unroll 2
+    for (int dy = 0; dy < f; ++dy) {
+      const size_t off =
+          static_cast<size_t>(sym_index(ry + dy, h)) * static_cast<size_t>(w) +
+          static_cast<size_t>(c);
+      float vr[4], vd[4];
+      load4<kVec>(ref + off, c, w, in_scale, vr);
+      load4<kVec>(dist + off, c, w, in_scale, vd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pr = vr[j] * tap;
+        const float pd = vd[j] * tap;
+        sr[j] = sr[j] + static_cast<double>(pr);
+        sd[j] = sd[j] + static_cast<double>(pd);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cs[0][4 * t + j] = sr[j];
+    cs[1][4 * t + j] = sd[j];
+  }
+  __syncthreads();
+  for (int xo = x0 + t; xo < x1; xo += kDecThreads) {
+    const int cx = xo * f - half;
+    double u = 0.0, v = 0.0;
+    for (int dx = 0; dx < f; ++dx) {
+      const int k = sym_index(cx + dx, w) - a;
+      u = u + cs[0][k];
+      v = v + cs[1][k];
+    }
+    const size_t o = static_cast<size_t>(y) * static_cast<size_t>(ow) +
+                     static_cast<size_t>(xo);
+    dref[o] = static_cast<float>(u);
+    ddist[o] = static_cast<float>(v);
+  }
+}
+
+// SSIM value of one pixel from its five window means: the combined formula
+// of the published SSIM in fp32, in the order written, with a correctly
+// rounded division (the library is built with IEEE fp32 division and no
+// contraction).
+__device__ __forceinline__ float ssim_value(float mu1, float mu2, float xx,
+                                            float yy, float xy, float c1,
+                                            float c2) {
+  const float m11 = mu1 * mu1;
+  const float m22 = mu2 * mu2;
+  const float m12 = mu1 * mu2;
+  const float s11 = xx - m11;
+  const float s22 = yy - m22;
+  const float s12 = xy - m12;
+  const float num = (2.0f * m12 + c1) * (2.0f * s12 + c2);
+  const float den = (m11 + m22 + c1) * (s11 + s22 + c2);
+  return num / den;
+}
+
+// Tap k of the window: the taps are symmetric bit for bit (checked on the
+// host), so t[k] and t[10-k] are read from one place and the products of a
+// sample with both are one expression.
+__device__ __forceinline__ float wtap(const SsimArgs &sa, int k) {
+  return sa.t[k < kTaps - 1 - k ? k : kTaps - 1 - k];
+}
+
+// One block: a 64 x 16 tile of SSIM values.
+//   1. the (16+10) x (64+10) input tile of both planes to LDS as fp32,
+//      mirrored;
+//   2. vertical passes of x, y, x*x, y*y, x*y: thread (column, half) owns 8
+//      rows; the five products of a sample are formed once per read;
+//   3. the vertical results to LDS (the input tile's region);
+//   4. horizontal passes, 4 pixels per thread, and the SSIM value, stored at
+//      map[x * pitch + y].
+// A window accumulator starts at its first product instead of 0 + product:
+// every input is >= +0, so the product is never -0 and both are the same.
+template <typename InT>
+__global__ __launch_bounds__(256) void ssim_kernel(
+    const InT *__restrict__ px, const InT *__restrict__ py, int w, int h,
+    float in_scale, SsimArgs sa, float *__restrict__ map, int pitch) {
+  constexpr int R = kRadius;
+  constexpr int IW = kTileW + 2 * R; // 74 columns
+  constexpr int IH = kTileH + 2 * R; // 26 rows
+  constexpr int P = IW + 1;          // odd pitch
+  constexpr int VB = kTileH / 2;     // rows per thread, vertical pass
+  constexpr int HB = 4;              // pixels per thread, horizontal pass
+  constexpr int kIn = 2 * IH * P;
+  constexpr int kV = 5 * kTileH * P;
+  static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
+  __shared__ float lds[kIn > kV ? kIn : kV];
+
+  const int tid = threadIdx.x;
+  const int x0 = blockIdx.x * kTileW;
+  const int y0 = blockIdx.y * kTileH;
+  for (int i = tid; i < IH * IW; i += 256) {
+    const int r = i / IW;
+    const int c = i - r * IW;
+    const size_t off =
+        static_cast<size_t>(sym_index(y0 - R + r, h)) * static_cast<size_t>(w) +
+        static_cast<size_t>(sym_index(x0 - R + c, w));
+    lds[r * P + c] = norm(px[off], in_scale);
+    lds[IH * P + r * P + c] = norm(py[off], in_scale);
+  }
+  __syncthreads();
+
+  const int vc = tid & 127;
+  const int vb = tid >> 7;
+  const bool vact = vc < IW;
+  float acc[5][VB];
+  if (vact) {
+    const float *sx = lds + (vb * VB) * P + vc;
+    const float *sy = sx + IH * P;
+#pragma unroll
+    for (int j = 0; j < VB + 2 * R; ++j) {
+      const float x = sx[j * P];
+      const float y = sy[j * P];
+      const float xx = x * x;
+      const float yy = y * y;
+      const float xy = x * y;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        const int k = j - i;
+        if (k >= 0 && k < kTaps) {
+          const float tk = wtap(sa, k);
+          if (k == 0) {
+            acc[0][i] = tk * x;
+            acc[1][i] = tk * y;
+            acc[2][i] = tk * xx;
+            acc[3][i] = tk * yy;
+            acc[4][i] = tk * xy;
+          } else {
+            acc[0][i] = acc[0][i] + tk * x;
+            acc[1][i] = acc[1][i] + tk * y;
+            acc[2][i] = acc[2][i] + tk * xx;
+            acc[3][i] = acc[3][i] + tk * yy;
+            acc[4][i] = acc[4][i] + tk * xy;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads(); // the input tile is dead
+  if (vact) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        lds[(q * kTileH + vb * VB + i) * P + vc] = acc[q][i];
+  }
+  __syncthreads();
+
+  const int ty = tid >> 4;
+  const int seg = tid & 15;
+  float fq[5][HB];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const float *row = lds + (q * kTileH + ty) * P + seg * HB;
+    float v[HB + 2 * R];
+#pragma unroll
+    for (int j = 0; j < HB + 2 * R; ++j)
+      v[j] = row[j];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+      float s = wtap(sa, 0) * v[i];
+#pragma unroll
+      for (int k = 1; k < kTaps; ++k)
+        s = s + wtap(sa, k) * v[i + k];
+      fq[q][i] = s;
+    }
+  }
+  const int y = y0 + ty;
+#pragma unroll
+  for (int i = 0; i < HB; ++i) {
+    const int x = x0 + seg * HB + i;
+    if (x < w && y < h)
+      map[static_cast<size_t>(x) * static_cast<size_t>(pitch) +
+          static_cast<size_t>(y)] =
+          ssim_value(fq[0][i], fq[1][i], fq[2][i], fq[3][i], fq[4][i], sa.c1,
+                     sa.c2);
+  }
+}
+
+// Ordered row sums: lane y adds map[x * pitch + y] for x = 0 .. w-1 into an
+// fp64 sum from 0.0, in that order (a serial loop over the row).  Lanes of
+// a wave read 64 consecutive floats per column.  Rows beyond h (up to the
+// pitch, inside the buffer) are computed and dropped.  Two register batches
+// keep one batch of loads in flight while the other is added.
+constexpr int kRowBatch = 16;
+
+__device__ __forceinline__ void load_col_batch(float (&v)[kRowBatch],
+                                               const float *__restrict__ p,
+                                               int x0, int w, int pitch) {
+#pragma unroll
+  for (int k = 0; k < kRowBatch; ++k) {
+    const int x = min(x0 + k, w - 1); // in bounds; extras are not added
+    v[k] = p[static_cast<size_t>(x) * static_cast<size_t>(pitch)];
+  }
+}
+
+__device__ __forceinline__ double add_col_batch(double acc,
+                                                const float (&v)[kRowBatch],
+                                                int x0, int w) {
+  if (x0 + kRowBatch <= w) {
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k)
+      acc = acc + static_cast<double>(v[k]);
+  } else {
+    for (int k = 0; k < kRowBatch && x0 + k < w; ++k)
+      acc = acc + static_cast<double>(v[k]);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(64) void rowsum_kernel(
+    const float *__restrict__ map, int w, int h, int pitch,
+    double *__restrict__ rows) {
+  const int y = blockIdx.x * 64 + threadIdx.x;
+  const float *p = map + y;
+  double acc = 0.0;
+  float va[kRowBatch], vb[kRowBatch];
+  load_col_batch(va, p, 0, w, pitch);
+  for (int x = 0; x < w; x += 2 * kRowBatch) {
+    load_col_batch(vb, p, x + kRowBatch, w, pitch);
+    acc = add_col_batch(acc, va, x, w);
+    if (x + kRowBatch >= w)
+      break;
+    load_col_batch(va, p, x + 2 * kRowBatch, w, pitch);
+    acc = add_col_batch(acc, vb, x + kRowBatch, w);
+  }
+  if (y < h)
+    rows[y] = acc;
+}
+
+// ------------------------------------------------------------------ launch
+
+namespace {
+
+template <typename InT>
+hipError_t launch_decimate_t(const InT *ref, const InT *dist, int w, int h,
+                             int f, float tap, float in_scale, int ow, int oh,
+                             float *dref, float *ddist, hipStream_t stream) {
+  const int xpb = outputs_per_block(f);
+  const dim3 grid(static_cast<unsigned>((ow + xpb - 1) / xpb),
+                  static_cast<unsigned>(oh));
+  const uintptr_t align = 4 * sizeof(InT);
+  const bool vec = w % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(ref) |
+                     reinterpret_cast<uintptr_t>(dist)) % align) == 0;
+  if (vec)
+    decimate_kernel<InT, true><<<grid, dim3(kDecThreads), 0, stream>>>(
+        ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
+  else
+    decimate_kernel<InT, false><<<grid, dim3(kDecThreads), 0, stream>>>(
+        ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
+  return hipGetLastError();
+}
+
+template <typename InT>
+hipError_t launch_ssim_t(const InT *x, const InT *y, int w, int h,
+                         float in_scale, const SsimArgs &sa, float *map,
+                         hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((w + kTileW - 1) / kTileW),
+                  static_cast<unsigned>((h + kTileH - 1) / kTileH));
+  ssim_kernel<InT><<<grid, dim3(256), 0, stream>>>(x, y, w, h, in_scale, sa,
+                                                   map, map_pitch(h));
+  return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_decimate(int bpc, const void *ref, const void *dist, int w,
+                           int h, int f, float tap, float in_scale, int ow,
+                           int oh, float *dref, float *ddist,
+                           hipStream_t stream) {
+  if (f < 2 || outputs_per_block(f) < 1 || ow < 1 || oh < 1)
+    return hipErrorInvalidValue;
+  if (bpc == 8)
+    return launch_decimate_t(static_cast<const uint8_t *>(ref),
+                             static_cast<const uint8_t *>(dist), w, h, f, tap,
+                             in_scale, ow, oh, dref, ddist, stream);
+  return launch_decimate_t(static_cast<const uint16_t *>(ref),
+                           static_cast<const uint16_t *>(dist), w, h, f, tap,
+                           in_scale, ow, oh, dref, ddist, stream);
+}
+
+hipError_t launch_ssim(int bpc, const void *x, const void *y, int w, int h,
+                       float in_scale, const SsimArgs &sa, float *map,
+                       hipStream_t stream) {
+  if (w < 1 || h < 1)
+    return hipErrorInvalidValue;
+  if (bpc == 0)
+    return launch_ssim_t(static_cast<const float *>(x),
+                         static_cast<const float *>(y), w, h, 1.0f, sa, map,
+                         stream);
+  if (bpc == 8)
+    return launch_ssim_t(static_cast<const uint8_t *>(x),
+                         static_cast<const uint8_t *>(y), w, h, in_scale, sa,
+                         map, stream);
+  return launch_ssim_t(static_cast<const uint16_t *>(x),
+                       static_cast<const uint16_t *>(y), w, h, in_scale, sa,
+                       map, stream);
+}
+
+hipError_t launch_ssim_rowsum(const float *map, int w, int h, double *rows,
+                              hipStream_t stream) {
+  if (w < 1 || h < 1)
+    return hipErrorInvalidValue;
+  const int pitch = map_pitch(h);
+  rowsum_kernel<<<dim3(static_cast<unsigned>(pitch / 64)), dim3(64), 0,
+                  stream>>>(map, w, h, pitch, rows);
+  return hipGetLastError();
+}
+
+} // namespace fssimk

@@ -19,6 +19,11 @@ Workloads (name -> list of frames, each ``(ref, dist, bpc)``):
   checker_1080p_10bit      1920x1080 10-bit checkerboard, 1 px shift, seed 3
   bright_1080p_16bit       1920x1080 16-bit bright gradient, seed 4
   pink_4k_8bit             3840x2160 8-bit 1/f noise, seed = frame index
+
+For the float SSIM decimation, whose factor max(1, round(min(w, h) / 256))
+depends only on the frame size, ``noisy_pair`` draws one pair of any size
+and bit depth (uniform reference, noisy distorted frame), so that every
+factor 1..10 and odd sizes can be exercised.
 """
 import numpy as np
 
@@ -159,6 +164,19 @@ def pink_4k_8bit(frames=20, first=0, h=2160, w=3840):
     -> standardised to mean 128, sd 40 -> rint, clipped.  Dist: 2x2 box-mean
     downscale, bilinear 2x upscale, rint, clipped."""
     return [pink_4k_frame(first + i, h, w) for i in range(frames)]
+
+
+def noisy_pair(w, h, bpc, seed, sd_frac=0.05):
+    """Ref: uniform integers on [0, 2^bpc - 1].  Dist: ref + N(0, (sd_frac *
+    2^bpc)^2), rint, clipped to the bit depth's range."""
+    g = _rng(seed)
+    top = (1 << bpc) - 1
+    dt = np.uint8 if bpc == 8 else np.uint16
+    ref = g.integers(0, top + 1, size=(h, w))
+    noisy = ref.astype(np.float64) + g.normal(0.0, sd_frac * (top + 1),
+                                               size=(h, w))
+    dist = np.clip(np.rint(noisy), 0, top)
+    return ref.astype(dt), dist.astype(dt), bpc
 
 
 WORKLOADS = {
