@@ -22,7 +22,12 @@ The line carries, besides the contract fields:
   extra         1920x1080 and 576x324 frames/s, the 4K rate when the frames
                 come from pinned host memory (PCIe copies included, never the
                 headline value), HBM GB/s of the whole frame from counters
-                when available, and the per-kernel split.
+                when available, and the per-kernel split; under "fssim" the
+                float SSIM feature on the same 4K frames and on the 1080p
+                10-bit frames: frames/s, the decimation kernel's HBM
+                roofline (algorithmic bytes: both sample planes read once,
+                both decimated fp32 planes written once) and the CPU
+                oracle's rate.
 """
 import argparse
 import hashlib
@@ -142,6 +147,100 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
     return (t1 - t0), kt
 
 
+def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
+    """The float SSIM queue over resident frames, as time_frames does for
+    VIF.  Returns (seconds, kernel times, geometry)."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    pairs = [(td(r), td(d)) for (r, d, _) in frames]
+    ctx = V.FloatSsim(w, h, bpc)
+
+    def run(n):
+        for i in range(n):
+            if ctx.pending() == V.FSSIM_QUEUE_DEPTH:
+                ctx.collect()
+            ctx.submit(*pairs[i % len(pairs)])
+        while ctx.pending():
+            ctx.collect()
+
+    run(warmup)
+    ctx.set_profiling(prof_kinds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = ctx.kernel_times()
+    geom = ctx.geometry()
+    ctx.close()
+    return (t1 - t0), kt, geom
+
+
+def fssim_kernel_us(V, frames, w, h, bpc, n=300):
+    """Average kernel durations (HIP events on the slot's stream around each
+    launch) with one frame at a time (fssim_score), so that no other frame's
+    kernels share the GPU during a timed launch."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    pairs = [(td(r), td(d)) for (r, d, _) in frames[:4]]
+    ctx = V.FloatSsim(w, h, bpc)
+    for i in range(10):
+        ctx.score(*pairs[i % len(pairs)])
+    ctx.set_profiling(0x7)
+    for i in range(n):
+        ctx.score(*pairs[i % len(pairs)])
+    kt = ctx.kernel_times()
+    ctx.close()
+    return {k: 1000.0 * v[0] / max(v[1], 1) for k, v in kt.items()}
+
+
+def fssim_leg(V, frames, w, h, bpc, steps, cpu_budget_s):
+    """frames/s of the float SSIM queue (no timing events), the kernels'
+    average durations one frame at a time, the decimation kernel against
+    the HBM peak, and the oracle on this host."""
+    dt, _, (f, ow, oh) = time_fssim(V, frames, w, h, bpc, steps, 20)
+    avg = fssim_kernel_us(V, frames, w, h, bpc)
+    bps = 1 if bpc == 8 else 2
+    dec_bytes = 2 * w * h * bps + 2 * ow * oh * 4
+    rec = {"workload": "%dx%d %d-bit, factor %d -> %dx%d" % (w, h, bpc, f,
+                                                             ow, oh),
+           "fps": round(steps / dt, 1),
+           "kernel_avg_us": {k: round(v, 2) for k, v in avg.items()}}
+    if f > 1 and avg["decimate"] > 0:
+        gbs = dec_bytes / (avg["decimate"] * 1e-6) / 1e9
+        rec["decimate_roofline"] = {
+            "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": dec_bytes}
+    if cpu_budget_s > 0:
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            r, d, b = frames[n % len(frames)]
+            oracle.fssim_score(r, d, b)
+            n += 1
+            if time.perf_counter() - t0 >= cpu_budget_s:
+                break
+        rec["cpu_oracle"] = {"fps": round(n / (time.perf_counter() - t0), 2),
+                             "cores": 1, "frames": n}
+    return rec
+
+
 def time_host_frames(V, frames, w, h, bpc, steps, warmup):
     """The queue fed from host memory: pinned host planes, each frame copied
     to the slot's device buffers by the library (vif_submit_host).  The
@@ -251,11 +350,12 @@ def main():
     ap.add_argument("--frames", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-1080p", type=int, default=500)
-    ap.add_argument("--mode", choices=["full", "frames", "copy"],
+    ap.add_argument("--mode", choices=["full", "frames", "copy", "fssim"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
                     "loop (for profiler runs); copy: a plain device copy of "
-                    "known size (counter calibration)")
+                    "known size (counter calibration); fssim: only the 4K "
+                    "float SSIM loop (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the feature on "
@@ -278,6 +378,12 @@ def main():
           file=sys.stderr, flush=True)
     frames4k = synth.pink_4k_8bit(frames=args.frames)
     w, h, bpc = 3840, 2160, 8
+    if args.mode == "fssim":
+        dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps,
+                                 args.warmup)
+        print("4K float SSIM (factor %d): %.1f frames/s"
+              % (geom[0], args.steps / dt), file=sys.stderr, flush=True)
+        return
 
     dt, kt = time_frames(V, frames4k, w, h, bpc, args.steps, args.warmup,
                          prof_kinds=["scale0"])
@@ -312,6 +418,12 @@ def main():
     fps_small = 2000 / dts
     fps_host = time_host_frames(V, frames4k, w, h, bpc, 200, 10)
 
+    # float SSIM with its exact decimation, on the same 4K frames and on the
+    # 1080p 10-bit frames
+    fssim = {"4k_8bit": fssim_leg(V, frames4k, w, h, bpc, 2000,
+                                  0 if args.no_cpu_baseline else 5.0),
+             "1080p_10bit": fssim_leg(V, f1080, 1920, 1080, 10, 2000, 0)}
+
     ops = OPS_PER_PIXEL_SCALE0 * w * h
     achieved = ops / (s0_avg_ms / 1000.0) / 1e12
     peak = VALU_PEAK_OPS / 1e12
@@ -338,7 +450,8 @@ def main():
                                       "collect": round(host_collect_us, 2)},
              "host_us_per_frame_1080p": {
                  "submit": round(kt1080["_host_submit_us"], 2),
-                 "collect": round(kt1080["_host_collect_us"], 2)}}
+                 "collect": round(kt1080["_host_collect_us"], 2)},
+             "fssim": fssim}
     if frame_bytes:
         gbs = frame_bytes * fps / 1e9
         extra["hbm_gbs_per_frame_counters"] = round(gbs, 1)

@@ -101,7 +101,8 @@ def test_4k_parity(V, orc):
         _compare(V, orc, ref, dist, bpc, "pink_4k_8bit[%d]" % i)
 
 
-# (w, h, bpc): factors 2..10, power-of-two and rounding box taps, odd sizes
+# (w, h, bpc): factors 2..10, 16 and 32, power-of-two (the kernel's integer
+# path up to 16) and rounding box taps, odd sizes
 # (n & 1 adds a decimated sample), a width that is an odd multiple of its
 # odd factor (the last window's mirror reaches furthest back), every depth
 FACTOR_CASES = [
@@ -116,6 +117,9 @@ FACTOR_CASES = [
     (2048, 2049, 10),  # f = 8, odd height
     (2305, 2304, 8),   # f = 9, odd width, 2305 = 256 * 9 + 1
     (2560, 2600, 16),  # f = 10
+    (4096, 4000, 8),   # f = 16, the largest factor of the integer path
+    (4000, 4100, 12),  # f = 16
+    (8192, 8064, 8),   # f = 32, a power of two on the fp64 path
 ]
 
 

@@ -21,9 +21,10 @@ constexpr int kDecSpan = 4 * kDecThreads;
 // the start is rounded down to a multiple of 4.
 inline int outputs_per_block(int f) { return (kDecSpan - 3 - 2 * f) / f; }
 
-// SSIM stage: tiles of 64 x 16 pixels.
+// SSIM stage: tiles of 64 x 8 pixels (small tiles: the decimated planes are
+// small, and more blocks keep more waves busy).
 constexpr int kTileW = 64;
-constexpr int kTileH = 16;
+constexpr int kTileH = 8;
 
 // Map layout: column-major, pitch rounded up to whole 64-row groups, so the
 // row-sum waves (one lane per row) read 64 consecutive floats per column.

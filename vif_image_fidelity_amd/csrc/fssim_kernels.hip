@@ -6,12 +6,14 @@
 //                    product an fp32 value, summed exactly in fp64 and
 //                    rounded to fp32 once (Research-2130 "float_ssim
 //                    decimation on the SYCL device", Sources and Findings);
+//                    decimate_pow2_kernel for factors 2, 4, 8, 16, where
+//                    the same value is an integer sum times a power of two;
 //   ssim_kernel      the 11-tap Gaussian window of x, y, x*x, y*y, x*y
 //                    (vertical pass, then horizontal) and the per-pixel
 //                    SSIM value, stored column-major;
 //   rowsum_kernel    each row's values added left to right in fp64, one
-//                    lane per row, straight into the context's pinned host
-//                    buffer.
+//                    lane per row (the map staged through LDS), straight
+//                    into the context's pinned host buffer.
 // Every border index goes through the symmetric mirror of period 2n
 // (Research-2130, Sources), so planes of any size >= 1 stay in bounds.
 //
@@ -92,9 +94,12 @@ __device__ __forceinline__ void load4(const uint16_t *p, int c, int w,
 // rounded down to a multiple of 4.
 //   1. every thread adds, for each of its 4 columns, the products of the f
 //      window rows (mirrored row indices are uniform in the block) into an
-//      fp64 column sum, for both planes; the sums go to LDS;
+//      fp64 column sum, for both planes; the loads of up to kRowGroup rows
+//      are all issued before the first of them is used; the sums go to LDS;
 //   2. decimated pixel x adds the column sums of its f window columns
 //      (mirrored) and rounds the sum to fp32 once.
+constexpr int kRowGroup = 8;
+
 template <typename InT, bool kVec>
 __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
     const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
@@ -116,20 +121,30 @@ __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
   double sd[4] = {0.0, 0.0, 0.0, 0.0};
   if (c <= hi) {
     const int ry = y * f - half;
-#pragma unroll 2
-    for (int dy = 0; dy < f; ++dy) {
-      const size_t off =
-          static_cast<size_t>(sym_index(ry + dy, h)) * static_cast<size_t>(w) +
-          static_cast<size_t>(c);
-      float vr[4], vd[4];
-      load4<kVec>(ref + off, c, w, in_scale, vr);
-      load4<kVec>(dist + off, c, w, in_scale, vd);
+    for (int g = 0; g < f; g += kRowGroup) {
+      // rows past the window load the last row again (in bounds, no
+      // branch, so every load of the group is in flight at once) and add
+      // +0.0, which leaves the non-negative sum as it is
+      float vr[kRowGroup][4], vd[kRowGroup][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pr = vr[j] * tap;
-        const float pd = vd[j] * tap;
-        sr[j] = sr[j] + static_cast<double>(pr);
-        sd[j] = sd[j] + static_cast<double>(pd);
+      for (int k = 0; k < kRowGroup; ++k) {
+        const int dy = min(g + k, f - 1);
+        const size_t off = static_cast<size_t>(sym_index(ry + dy, h)) *
+                               static_cast<size_t>(w) +
+                           static_cast<size_t>(c);
+        load4<kVec>(ref + off, c, w, in_scale, vr[k]);
+        load4<kVec>(dist + off, c, w, in_scale, vd[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kRowGroup; ++k) {
+        const bool in = g + k < f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pr = in ? vr[k][j] * tap : 0.0f;
+          const float pd = in ? vd[k][j] * tap : 0.0f;
+          sr[j] = sr[j] + static_cast<double>(pr);
+          sd[j] = sd[j] + static_cast<double>(pd);
+        }
       }
     }
   }
@@ -151,6 +166,115 @@ __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
                      static_cast<size_t>(xo);
     dref[o] = static_cast<float>(u);
     ddist[o] = static_cast<float>(v);
+  }
+}
+
+// Power-of-two factors up to 16: the tap 2^-2k is exact and so is every
+// product (a sample of at most 16 bits times a power of two), so the window
+// sum is 2^-(bpc-8) * tap times the integer sum S of the raw samples.
+// S <= 16^2 * 65535 < 2^24 is exact in fp32, and the scaling by a power of
+// two is exact too: the decimated value is (float)S * iscale with no
+// rounding at all, the same value the exact fp64 sum rounds to.  The block
+// and LDS layout are those of decimate_kernel; the column sums are integers
+// (8-bit samples: two columns per 32-bit add, in 16-bit halves that cannot
+// carry, 16 * 255 < 2^16).
+template <bool kVec>
+__device__ __forceinline__ void add4(const uint8_t *p, int c, int w,
+                                     uint32_t (&s)[4]) {
+  if constexpr (kVec) {
+    const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+    s[0] += u & 0x00ff00ffu;        // columns 0 and 2
+    s[1] += (u >> 8) & 0x00ff00ffu; // columns 1 and 3
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s[j] += c + j < w ? static_cast<uint32_t>(p[j]) : 0u;
+  }
+}
+
+template <bool kVec>
+__device__ __forceinline__ void add4(const uint16_t *p, int c, int w,
+                                     uint32_t (&s)[4]) {
+  if constexpr (kVec) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    s[0] += u.x & 0xffffu;
+    s[1] += u.x >> 16;
+    s[2] += u.y & 0xffffu;
+    s[3] += u.y >> 16;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s[j] += c + j < w ? static_cast<uint32_t>(p[j]) : 0u;
+  }
+}
+
+// Column sums of the 4 columns in natural order.
+template <typename InT, bool kVec>
+__device__ __forceinline__ void unpack4(const uint32_t (&s)[4],
+                                        uint32_t (&o)[4]) {
+  if constexpr (kVec && sizeof(InT) == 1) {
+    o[0] = s[0] & 0xffffu;
+    o[1] = s[1] & 0xffffu;
+    o[2] = s[0] >> 16;
+    o[3] = s[1] >> 16;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = s[j];
+  }
+}
+
+template <typename InT, bool kVec, int F>
+__global__ __launch_bounds__(kDecThreads) void decimate_pow2_kernel(
+    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
+    float iscale, int ow, int xpb, float *__restrict__ dref,
+    float *__restrict__ ddist) {
+  constexpr int f = F;
+  __shared__ uint32_t cs[2][kDecSpan];
+  const int t = threadIdx.x;
+  const int y = blockIdx.y;
+  const int half = f / 2;
+  const int x0 = blockIdx.x * xpb;
+  const int x1 = min(ow, x0 + xpb);
+  const int lo = max(0, x0 * f - half - f);
+  const int a = lo & ~3;
+  const int hi = min(w - 1, (x1 - 1) * f - half + f - 1);
+  const int c = a + 4 * t;
+  uint32_t sr[4] = {0u, 0u, 0u, 0u};
+  uint32_t sd[4] = {0u, 0u, 0u, 0u};
+  if (c <= hi) {
+    const int ry = y * f - half;
+#pragma unroll
+    for (int k = 0; k < F; ++k) {
+      const size_t off = static_cast<size_t>(sym_index(ry + k, h)) *
+                             static_cast<size_t>(w) +
+                         static_cast<size_t>(c);
+      add4<kVec>(ref + off, c, w, sr);
+      add4<kVec>(dist + off, c, w, sd);
+    }
+  }
+  uint32_t ur[4], ud[4];
+  unpack4<InT, kVec>(sr, ur);
+  unpack4<InT, kVec>(sd, ud);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cs[0][4 * t + j] = ur[j];
+    cs[1][4 * t + j] = ud[j];
+  }
+  __syncthreads();
+  for (int xo = x0 + t; xo < x1; xo += kDecThreads) {
+    const int cx = xo * f - half;
+    uint32_t u = 0u, v = 0u;
+#pragma unroll
+    for (int dx = 0; dx < f; ++dx) {
+      const int k = sym_index(cx + dx, w) - a;
+      u += cs[0][k];
+      v += cs[1][k];
+    }
+    const size_t o = static_cast<size_t>(y) * static_cast<size_t>(ow) +
+                     static_cast<size_t>(xo);
+    dref[o] = static_cast<float>(u) * iscale;
+    ddist[o] = static_cast<float>(v) * iscale;
   }
 }
 
@@ -179,14 +303,14 @@ __device__ __forceinline__ float wtap(const SsimArgs &sa, int k) {
   return sa.t[k < kTaps - 1 - k ? k : kTaps - 1 - k];
 }
 
-// One block: a 64 x 16 tile of SSIM values.
-//   1. the (16+10) x (64+10) input tile of both planes to LDS as fp32,
-//      mirrored;
-//   2. vertical passes of x, y, x*x, y*y, x*y: thread (column, half) owns 8
-//      rows; the five products of a sample are formed once per read;
+// One block: a kTileW x kTileH tile of SSIM values.
+//   1. the (kTileH+10) x (kTileW+10) input tile of both planes to LDS as
+//      fp32, mirrored;
+//   2. vertical passes of x, y, x*x, y*y, x*y: thread (column, half) owns
+//      kTileH/2 rows; the five products of a sample are formed once per read;
 //   3. the vertical results to LDS (the input tile's region);
-//   4. horizontal passes, 4 pixels per thread, and the SSIM value, stored at
-//      map[x * pitch + y].
+//   4. horizontal passes, kTileW * kTileH / 256 pixels per thread, and the
+//      SSIM value, stored at map[x * pitch + y].
 // A window accumulator starts at its first product instead of 0 + product:
 // every input is >= +0, so the product is never -0 and both are the same.
 template <typename InT>
@@ -198,23 +322,43 @@ __global__ __launch_bounds__(256) void ssim_kernel(
   constexpr int IH = kTileH + 2 * R; // 26 rows
   constexpr int P = IW + 1;          // odd pitch
   constexpr int VB = kTileH / 2;     // rows per thread, vertical pass
-  constexpr int HB = 4;              // pixels per thread, horizontal pass
+  constexpr int HB = kTileW * kTileH / 256; // pixels per thread, horizontal
+  constexpr int SEGS = kTileW / HB;  // threads per tile row
   constexpr int kIn = 2 * IH * P;
   constexpr int kV = 5 * kTileH * P;
-  static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
+  static_assert(SEGS * kTileH == 256, "one horizontal segment per thread");
   __shared__ float lds[kIn > kV ? kIn : kV];
 
   const int tid = threadIdx.x;
   const int x0 = blockIdx.x * kTileW;
   const int y0 = blockIdx.y * kTileH;
-  for (int i = tid; i < IH * IW; i += 256) {
-    const int r = i / IW;
-    const int c = i - r * IW;
-    const size_t off =
-        static_cast<size_t>(sym_index(y0 - R + r, h)) * static_cast<size_t>(w) +
-        static_cast<size_t>(sym_index(x0 - R + c, w));
-    lds[r * P + c] = norm(px[off], in_scale);
-    lds[IH * P + r * P + c] = norm(py[off], in_scale);
+  // all of a thread's loads are issued before the first LDS store
+  {
+    constexpr int kPer = (IH * IW + 255) / 256;
+    InT vx[kPer], vy[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + 256 * k;
+      if (i < IH * IW) {
+        const int r = i / IW;
+        const int c = i - r * IW;
+        const size_t off = static_cast<size_t>(sym_index(y0 - R + r, h)) *
+                               static_cast<size_t>(w) +
+                           static_cast<size_t>(sym_index(x0 - R + c, w));
+        vx[k] = px[off];
+        vy[k] = py[off];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + 256 * k;
+      if (i < IH * IW) {
+        const int r = i / IW;
+        const int c = i - r * IW;
+        lds[r * P + c] = norm(vx[k], in_scale);
+        lds[IH * P + r * P + c] = norm(vy[k], in_scale);
+      }
+    }
   }
   __syncthreads();
 
@@ -264,8 +408,8 @@ __global__ __launch_bounds__(256) void ssim_kernel(
   }
   __syncthreads();
 
-  const int ty = tid >> 4;
-  const int seg = tid & 15;
+  const int ty = tid / SEGS;
+  const int seg = tid % SEGS;
   float fq[5][HB];
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
@@ -295,55 +439,85 @@ __global__ __launch_bounds__(256) void ssim_kernel(
   }
 }
 
-// Ordered row sums: lane y adds map[x * pitch + y] for x = 0 .. w-1 into an
-// fp64 sum from 0.0, in that order (a serial loop over the row).  Lanes of
-// a wave read 64 consecutive floats per column.  Rows beyond h (up to the
-// pitch, inside the buffer) are computed and dropped.  Two register batches
-// keep one batch of loads in flight while the other is added.
-constexpr int kRowBatch = 16;
+// Ordered row sums.  A block owns 64 rows; wave 0's lane r adds
+// map[x * pitch + y0 + r] for x = 0 .. w-1 into an fp64 sum from 0.0, in
+// that order (a serial loop over the row).  The block stages the map in
+// chunks of kSumCols columns x 64 rows through LDS: all four waves issue
+// every load of a chunk at once (float4, 64 consecutive rows of a column are
+// one 256-byte run), then wave 0 adds the chunk from LDS while the other
+// waves load the next chunk into the second buffer.  Rows beyond h (up to
+// the pitch, inside the buffer) are computed and dropped.
+constexpr int kSumCols = 96;
+constexpr int kSumF4 = kSumCols * 16;  // 4-float vectors per chunk
+constexpr int kSumPer = kSumF4 / 192;  // per loading thread
+static_assert(kSumF4 % 192 == 0, "three waves load a chunk evenly");
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void load_col_batch(float (&v)[kRowBatch],
-                                               const float *__restrict__ p,
-                                               int x0, int w, int pitch) {
+__device__ __forceinline__ void load_chunk(f32x4 (&v)[kSumPer],
+                                           const float *__restrict__ map,
+                                           int pitch, int y0, int x0, int w,
+                                           int lt) {
 #pragma unroll
-  for (int k = 0; k < kRowBatch; ++k) {
-    const int x = min(x0 + k, w - 1); // in bounds; extras are not added
-    v[k] = p[static_cast<size_t>(x) * static_cast<size_t>(pitch)];
+  for (int k = 0; k < kSumPer; ++k) {
+    const int i = lt + 192 * k;
+    const int col = min(x0 + i / 16, w - 1); // in bounds; extras unused
+    v[k] = *reinterpret_cast<const f32x4 *>(
+        map + static_cast<size_t>(col) * static_cast<size_t>(pitch) + y0 +
+        4 * (i % 16));
   }
 }
 
-__device__ __forceinline__ double add_col_batch(double acc,
-                                                const float (&v)[kRowBatch],
-                                                int x0, int w) {
-  if (x0 + kRowBatch <= w) {
+__device__ __forceinline__ void store_chunk(float *buf,
+                                            const f32x4 (&v)[kSumPer],
+                                            int lt) {
 #pragma unroll
-    for (int k = 0; k < kRowBatch; ++k)
-      acc = acc + static_cast<double>(v[k]);
-  } else {
-    for (int k = 0; k < kRowBatch && x0 + k < w; ++k)
-      acc = acc + static_cast<double>(v[k]);
-  }
-  return acc;
+  for (int k = 0; k < kSumPer; ++k)
+    *reinterpret_cast<f32x4 *>(buf + 4 * (lt + 192 * k)) = v[k];
 }
 
-__global__ __launch_bounds__(64) void rowsum_kernel(
+__global__ __launch_bounds__(256) void rowsum_kernel(
     const float *__restrict__ map, int w, int h, int pitch,
     double *__restrict__ rows) {
-  const int y = blockIdx.x * 64 + threadIdx.x;
-  const float *p = map + y;
-  double acc = 0.0;
-  float va[kRowBatch], vb[kRowBatch];
-  load_col_batch(va, p, 0, w, pitch);
-  for (int x = 0; x < w; x += 2 * kRowBatch) {
-    load_col_batch(vb, p, x + kRowBatch, w, pitch);
-    acc = add_col_batch(acc, va, x, w);
-    if (x + kRowBatch >= w)
-      break;
-    load_col_batch(va, p, x + 2 * kRowBatch, w, pitch);
-    acc = add_col_batch(acc, vb, x + kRowBatch, w);
+  __shared__ float buf[2][kSumCols * 64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int y0 = blockIdx.x * 64;
+  const int chunks = (w + kSumCols - 1) / kSumCols;
+  const int lt = tid - 64; // loading thread index of waves 1..3
+  if (wave > 0) {
+    f32x4 v[kSumPer];
+    load_chunk(v, map, pitch, y0, 0, w, lt);
+    store_chunk(buf[0], v, lt);
   }
-  if (y < h)
-    rows[y] = acc;
+  __syncthreads();
+  double acc = 0.0;
+  for (int ch = 0; ch < chunks; ++ch) {
+    const int x0 = ch * kSumCols;
+    if (wave == 0) {
+      const float *b = buf[ch & 1] + lane;
+      const int n = min(kSumCols, w - x0);
+      int x = 0;
+      for (; x + 16 <= n; x += 16) {
+        float t[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          t[k] = b[(x + k) * 64];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          acc = acc + static_cast<double>(t[k]);
+      }
+      for (; x < n; ++x)
+        acc = acc + static_cast<double>(b[x * 64]);
+    } else if (ch + 1 < chunks) {
+      f32x4 v[kSumPer];
+      load_chunk(v, map, pitch, y0, x0 + kSumCols, w, lt);
+      store_chunk(buf[(ch + 1) & 1], v, lt);
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && y0 + lane < h)
+    rows[y0 + lane] = acc;
 }
 
 // ------------------------------------------------------------------ launch
@@ -361,12 +535,33 @@ hipError_t launch_decimate_t(const InT *ref, const InT *dist, int w, int h,
   const bool vec = w % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(ref) |
                      reinterpret_cast<uintptr_t>(dist)) % align) == 0;
-  if (vec)
+  // in_scale and tap are powers of two for these factors, so is their
+  // product
+  const float iscale = in_scale * tap;
+  const dim3 blk(kDecThreads);
+#define FSSIM_POW2(F)                                                          \
+  if (vec)                                                                     \
+    decimate_pow2_kernel<InT, true, F><<<grid, blk, 0, stream>>>(              \
+        ref, dist, w, h, iscale, ow, xpb, dref, ddist);                        \
+  else                                                                         \
+    decimate_pow2_kernel<InT, false, F><<<grid, blk, 0, stream>>>(             \
+        ref, dist, w, h, iscale, ow, xpb, dref, ddist)
+  if (f == 2) {
+    FSSIM_POW2(2);
+  } else if (f == 4) {
+    FSSIM_POW2(4);
+  } else if (f == 8) {
+    FSSIM_POW2(8);
+  } else if (f == 16) {
+    FSSIM_POW2(16);
+  } else if (vec) {
     decimate_kernel<InT, true><<<grid, dim3(kDecThreads), 0, stream>>>(
         ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
-  else
+  } else {
     decimate_kernel<InT, false><<<grid, dim3(kDecThreads), 0, stream>>>(
         ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
+  }
+#undef FSSIM_POW2
   return hipGetLastError();
 }
 
@@ -421,7 +616,7 @@ hipError_t launch_ssim_rowsum(const float *map, int w, int h, double *rows,
   if (w < 1 || h < 1)
     return hipErrorInvalidValue;
   const int pitch = map_pitch(h);
-  rowsum_kernel<<<dim3(static_cast<unsigned>(pitch / 64)), dim3(64), 0,
+  rowsum_kernel<<<dim3(static_cast<unsigned>(pitch / 64)), dim3(256), 0,
                   stream>>>(map, w, h, pitch, rows);
   return hipGetLastError();
 }
