@@ -19,7 +19,9 @@ The line carries, besides the contract fields:
                 kernel source has not changed since they were taken, else null.
   cpu_baseline  the CPU oracle on this host, one core, on a bounded sample of
                 the same workload.
-  extra         1920x1080 and 576x324 frames/s, the 4K rate when the frames
+  extra         1920x1080 and 576x324 frames/s, the rates with batched
+                submissions (vif_submit_batch: one launch per kernel for 4, 8
+                or 16 frames), the 4K rate when the frames
                 come from pinned host memory (PCIe copies included, never the
                 headline value), HBM GB/s of the whole frame from counters
                 when available, and the per-kernel split; under "fssim" the
@@ -100,7 +102,11 @@ def ensure_lib():
     _lib.load()
 
 
-def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
+def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0,
+                batch=1):
+    """Scores `steps` frames (cycling over the resident pairs) through the
+    context's queue, `batch` frames per submission (one launch per kernel
+    for the whole batch).  Returns (seconds, kernel times)."""
     import torch
     dev = torch.device("cuda:0")
 
@@ -112,23 +118,36 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
         return torch.from_numpy(a).to(dev)
 
     pairs = [(td(r), td(d)) for (r, d, _) in frames]
-    ctx = V.Vif(w, h, bpc)
+    ctx = V.Vif(w, h, bpc, max_batch=batch)
+    from vif_image_fidelity_amd import _lib
+    ptrs = [(r.data_ptr(), d.data_ptr()) for r, d in pairs]
 
     host = {"submit": 0.0, "collect": 0.0}
 
     def run(n):
-        # keep the context's queue full: frame i+depth is submitted as soon
-        # as frame i has been collected
+        # keep the context's queue full: a submission goes in as soon as the
+        # oldest one's frames have been collected
         clock = time.perf_counter
-        for i in range(n):
-            if ctx.pending() == V.QUEUE_DEPTH:
+        i = 0
+        while i < n:
+            k = min(batch, n - i)
+            if ctx.pending() + k > V.QUEUE_DEPTH * batch:
                 c0 = clock()
-                ctx.collect()
+                for _ in range(batch):
+                    ctx.collect()
                 host["collect"] += clock() - c0
-            r, d = pairs[i % len(pairs)]
             c0 = clock()
-            ctx.submit(r, d)
+            if batch == 1:
+                r, d = pairs[i % len(pairs)]
+                ctx.submit(r, d)
+            else:
+                sel = [ptrs[(i + j) % len(ptrs)] for j in range(k)]
+                rc = _lib.vif_submit_batch(ctx._ctx, [a for a, _ in sel],
+                                           [b for _, b in sel])
+                if rc != 0:
+                    raise V.VifError(rc, "vif_submit_batch")
             host["submit"] += clock() - c0
+            i += k
         while ctx.pending():
             ctx.collect()
 
@@ -416,6 +435,15 @@ def main():
     fsmall = synth.netflix_576x324_8bit()
     dts, kts = time_frames(V, fsmall, 576, 324, 8, 2000, 50)
     fps_small = 2000 / dts
+
+    # batched submissions: each kernel launched once for several frames
+    batched = {}
+    for key, fr, bw, bh, bb, nb, steps in (
+            ("4k_8bit_batch4", frames4k, w, h, bpc, 4, 1000),
+            ("1080p_10bit_batch8", f1080, 1920, 1080, 10, 8, 3000),
+            ("576x324_8bit_batch16", fsmall, 576, 324, 8, 16, 8000)):
+        dtb, _ = time_frames(V, fr, bw, bh, bb, steps, 4 * nb, batch=nb)
+        batched[key] = round(steps / dtb, 1)
     fps_host = time_host_frames(V, frames4k, w, h, bpc, 200, 10)
 
     # float SSIM with its exact decimation, on the same 4K frames and on the
@@ -436,6 +464,7 @@ def main():
     extra = {"fps_1080p_10bit": round(fps1080, 1),
              "fps_576x324_8bit": round(fps_small, 1),
              "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
+             "fps_batched": batched,
              "host_us_per_frame_576x324": {
                  "submit": round(kts["_host_submit_us"], 2),
                  "collect": round(kts["_host_collect_us"], 2)},

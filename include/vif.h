@@ -166,6 +166,28 @@ int vif_submit_host(vif_ctx *ctx, const void *ref, const void *dist);
 int vif_score_host(vif_ctx *ctx, const void *ref, const void *dist,
                    double out[8]);
 
+/*
+ * Batched submission (an extension of the queue above for many frames of one
+ * geometry).  vif_create_batch is vif_create_ex for a context whose
+ * submissions may carry up to max_batch frame pairs (1 <= max_batch <=
+ * VIF_MAX_BATCH); each queue slot's device and pinned buffers are sized for
+ * max_batch frames, so memory grows with it.  vif_submit_batch enqueues n
+ * pairs (1 <= n <= max_batch; refs[z], dists[z] as for vif_submit) as ONE
+ * slot: every kernel of the path runs once for all n frames, which amortises
+ * the launches and fills the device with small frames.  The frames count as
+ * n pending frames; vif_collect returns them one by one in order, and the
+ * slot is free again once all n are collected.  Results are the same bits as
+ * n single submissions.  VIF_EINVAL for a bad n, NULL arrays or frames, or
+ * when all VIF_QUEUE_DEPTH slots are in use.  vif_submit is a batch of one;
+ * vif_create and vif_create_ex make contexts with max_batch = 1.  The frames
+ * stay valid until their vif_collect returns.  Allocates nothing.
+ */
+#define VIF_MAX_BATCH 16
+vif_ctx *vif_create_batch(int w, int h, int bpc, const vif_options *opt,
+                          int max_batch);
+int vif_submit_batch(vif_ctx *ctx, int n, const void *const *refs,
+                     const void *const *dists);
+
 /* vif_pending -- frames submitted and not yet collected (or VIF_EINVAL). */
 int vif_pending(const vif_ctx *ctx);
 

@@ -217,3 +217,17 @@ def test_fssim_null_context_calls(lib):
     assert _lib.fssim_pending(None) == _lib.VIF_EINVAL
     assert _lib.fssim_geometry(None, np.zeros(3, np.int32)) == _lib.VIF_EINVAL
     _lib.fssim_destroy(None)
+
+
+@pytest.mark.parametrize("mb", [0, -1, 17, 1000])
+def test_create_batch_rejects_bad_capacity(lib, mb):
+    """A batch capacity outside 1..VIF_MAX_BATCH is refused at create time,
+    before any device call."""
+    from vif_image_fidelity_amd import _lib
+    assert not _lib.vif_create_batch(64, 64, 8, None, mb)
+    assert _lib.vif_errno() == _lib.VIF_EINVAL
+
+
+def test_submit_batch_null_context(lib):
+    from vif_image_fidelity_amd import _lib
+    assert _lib.vif_submit_batch(None, [0], [0]) == _lib.VIF_EINVAL

@@ -328,3 +328,137 @@ def test_host_frames_match_device_frames(V, orc):
         ctx.score_host(frames[0][0][:, :-1], frames[0][1][:, :-1])
     with pytest.raises(ValueError):
         ctx.score_host(frames[0][0].astype(np.uint16), frames[0][1])
+
+
+def _check_outputs(got, exp, label):
+    maxdiff = float(np.max(np.abs(got - exp)))
+    assert maxdiff <= GATE, (label, maxdiff)
+    assert got.view(np.uint64).tolist() == exp.view(np.uint64).tolist(), \
+        (label, got, exp)
+
+
+@pytest.mark.parametrize("name,n", [("netflix_576x324_8bit", 16),
+                                    ("checker_1080p_10bit", 3),
+                                    ("bright_1080p_16bit", 5)])
+def test_batch_matches_oracle(V, orc, name, n):
+    """One submission of n frames (each kernel launched once for all of
+    them): every frame's outputs, sums and row sums equal the oracle's."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.WORKLOADS[name]()
+    h, w = frames[0][0].shape
+    bpc = frames[0][2]
+    print("batch case %s n=%d" % (name, n), flush=True)
+    exps = {}
+    for k, (r, d, b) in enumerate(frames):
+        exps[k] = orc.score(r, d, b, want_rows=True)
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.Vif(w, h, bpc, max_batch=n)
+    idx = [(3 * i + 1) % len(frames) for i in range(n)]
+    ctx.submit_batch([dev[k][0] for k in idx], [dev[k][1] for k in idx])
+    assert ctx.pending() == n
+    for i, k in enumerate(idx):
+        got = ctx.collect()
+        exp, esums, erows = exps[k]
+        _check_outputs(got, exp, "%s[%d]" % (name, i))
+        assert ctx.sums().view(np.uint32).tolist() == \
+            esums.view(np.uint32).tolist()
+        assert (ctx.row_sums().view(np.uint32) ==
+                erows.view(np.uint32)).all()
+    assert ctx.pending() == 0
+    ctx.close()
+
+
+def test_batch_4k_two_frames(V, orc):
+    """The 3840x2160 workload's first two frames in one submission."""
+    from vif_image_fidelity_amd import synth
+    frames = [synth.pink_4k_frame(i) for i in range(2)]
+    ctx = V.Vif(3840, 2160, 8, max_batch=2)
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+    for i, (r, d, b) in enumerate(frames):
+        got = ctx.collect()
+        _check_outputs(got, orc.score(r, d, b)[0], "pink_4k_8bit[%d]" % i)
+    ctx.close()
+
+
+def test_batch_tiny_frames(V, orc):
+    """Every tiny geometry in batches of two and of one."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.tiny_frames_8bit()
+    by_size = {}
+    for r, d, b in frames:
+        by_size.setdefault(r.shape, []).append((r, d, b))
+    for shape, fr in by_size.items():
+        h, w = shape
+        ctx = V.Vif(w, h, 8, max_batch=2)
+        dev = [(to_device(r), to_device(d)) for r, d, _ in fr]
+        ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+        ctx.submit(*dev[1])
+        for i, (r, d, b) in enumerate(fr + [fr[1]]):
+            got = ctx.collect()
+            _check_outputs(got, orc.score(r, d, b)[0],
+                           "tiny %dx%d[%d]" % (w, h, i))
+        ctx.close()
+
+
+def test_batch_mixed_queue_and_limits(V, orc):
+    """Batches and single frames share the three slots: a fourth submission
+    is refused until a slot's frames are all collected; order is kept."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit()
+    exps = [orc.score(r, d, b)[0] for r, d, b in frames]
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.Vif(576, 324, 8, max_batch=4)
+    order = []
+    ctx.submit_batch([dev[0][0], dev[1][0], dev[2][0]],
+                     [dev[0][1], dev[1][1], dev[2][1]])
+    order += [0, 1, 2]
+    ctx.submit(*dev[2])
+    order += [2]
+    ctx.submit_batch([dev[1][0]] * 4, [dev[1][1]] * 4)
+    order += [1] * 4
+    assert ctx.pending() == 8
+    with pytest.raises(V.VifError):
+        ctx.submit(*dev[0])          # all three slots in use
+    with pytest.raises(V.VifError):
+        ctx.submit_batch([dev[0][0]] * 5, [dev[0][1]] * 5)  # above capacity
+    for i in range(3):
+        assert ctx.collect().tobytes() == exps[order[i]].tobytes()
+    # the first slot is free again
+    ctx.submit_batch([dev[0][0]], [dev[0][1]])
+    order += [0]
+    for i in range(3, len(order)):
+        assert ctx.collect().tobytes() == exps[order[i]].tobytes(), i
+    assert ctx.pending() == 0
+    ctx.close()
+
+
+def test_batch_with_options(V, orc):
+    """Non-default noise variance and gain limit through a batched
+    submission."""
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit()
+    opt = {"sigma_nsq": 1.5, "enhn_gain_limit": 1.0}
+    ctx = V.Vif(576, 324, 8, options=opt, max_batch=3)
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+    for i, (r, d, b) in enumerate(frames):
+        got = ctx.collect()
+        _check_outputs(got, orc.score(r, d, b, options=opt)[0],
+                       "options[%d]" % i)
+    ctx.close()
+
+
+def test_batch_profiling_counts_one_launch_per_kind(V):
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit()
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.Vif(576, 324, 8, max_batch=3)
+    ctx.set_profiling(0x1F)
+    for _ in range(2):
+        ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+        for _ in dev:
+            ctx.collect()
+    t = ctx.kernel_times()
+    assert [t[k][1] for k in V.KERNEL_KINDS] == [2] * 5
+    ctx.close()

@@ -16,13 +16,13 @@ import numpy as np
 
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
-                   DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH,
+                   DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH, MAX_BATCH,
                    FSSIM_KERNEL_KINDS, FSSIM_QUEUE_DEPTH)
 
 __all__ = ["Vif", "VifError", "FloatSsim", "fssim_taps", "taps",
            "make_options", "DEFAULT_OPTIONS",
            "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
-           "KERNEL_KINDS", "QUEUE_DEPTH", "FSSIM_KERNEL_KINDS",
+           "KERNEL_KINDS", "QUEUE_DEPTH", "MAX_BATCH", "FSSIM_KERNEL_KINDS",
            "FSSIM_QUEUE_DEPTH"]
 
 # Defaults of struct vif_options (include/vif.h states each option's
@@ -78,9 +78,15 @@ class Vif:
     """One scoring context for w x h frames of bpc bits (8, 10, 12, 16).
     options: None or a dict of overrides of DEFAULT_OPTIONS."""
 
-    def __init__(self, w, h, bpc, stream=None, options=None):
+    def __init__(self, w, h, bpc, stream=None, options=None, max_batch=1):
         self.w, self.h, self.bpc = int(w), int(h), int(bpc)
-        if options is None:
+        self.max_batch = int(max_batch)
+        if self.max_batch != 1:
+            ctx = _lib.vif_create_batch(
+                self.w, self.h, self.bpc,
+                None if options is None else make_options(options),
+                self.max_batch)
+        elif options is None:
             ctx = _lib.vif_create(self.w, self.h, self.bpc)
         else:
             ctx = _lib.vif_create_ex(self.w, self.h, self.bpc,
@@ -168,6 +174,17 @@ class Vif:
         rc = _lib.vif_submit(self._ctx, _ptr(ref), _ptr(dist))
         if rc != VIF_OK:
             raise VifError(rc, "vif_submit")
+
+    def submit_batch(self, refs, dists):
+        """Enqueue len(refs) pairs (at most max_batch) as one submission:
+        each kernel runs once for all of them.  collect() returns them one
+        by one, in order."""
+        for t in list(refs) + list(dists):
+            self._check_frame(t)
+        rc = _lib.vif_submit_batch(self._ctx, [_ptr(r) for r in refs],
+                                   [_ptr(d) for d in dists])
+        if rc != VIF_OK:
+            raise VifError(rc, "vif_submit_batch")
 
     def collect(self):
         """Outputs of the oldest submitted pair (float64[8])."""

@@ -18,10 +18,12 @@ VIF_EHIP = -3
 NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
+MAX_BATCH = 16
 NDEBUG = 15
 KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
 FSSIM_TAPS = 11
 FSSIM_QUEUE_DEPTH = 3
+MAX_BATCH = 16
 FSSIM_KERNEL_KINDS = ("decimate", "ssim", "rowsum")
 DEBUG_NAMES = ("vif_scale0", "vif_scale1", "vif_scale2", "vif_scale3",
                "vif", "vif_num", "vif_den",
@@ -65,6 +67,10 @@ def load():
     sig = {
         "vif_create": ([ip, ip, ip], vp),
         "vif_create_ex": ([ip, ip, ip, ctypes.POINTER(VifOptions)], vp),
+        "vif_create_batch": ([ip, ip, ip, ctypes.POINTER(VifOptions), ip],
+                             vp),
+        "vif_submit_batch": ([vp, ip, ctypes.POINTER(vp),
+                              ctypes.POINTER(vp)], ip),
         "vif_default_options": ([ctypes.POINTER(VifOptions)], None),
         "vif_get_options": ([vp, ctypes.POINTER(VifOptions)], ip),
         "vif_get_debug": ([vp, dp], ip),
@@ -118,6 +124,7 @@ def load():
 def exported_symbols():
     """Names of every C function this binding declares."""
     return ["vif_default_options", "vif_create", "vif_create_ex",
+            "vif_create_batch", "vif_submit_batch",
             "vif_get_options", "vif_score", "vif_submit", "vif_collect",
             "vif_submit_host", "vif_score_host",
             "vif_pending", "vif_get_debug",
@@ -151,6 +158,22 @@ def vif_create_ex(w, h, bpc, options):
     return load().vif_create_ex(int(w), int(h), int(bpc),
                                 None if options is None
                                 else ctypes.byref(options))
+
+
+def vif_create_batch(w, h, bpc, options, max_batch):
+    """options: a VifOptions or None (the defaults)."""
+    return load().vif_create_batch(int(w), int(h), int(bpc),
+                                   None if options is None
+                                   else ctypes.byref(options), int(max_batch))
+
+
+def vif_submit_batch(ctx, ref_ptrs, dist_ptrs):
+    """ref_ptrs, dist_ptrs: equal-length sequences of device pointers."""
+    n = len(ref_ptrs)
+    if len(dist_ptrs) != n:
+        raise ValueError("as many distorted as reference frames")
+    arr = ctypes.c_void_p * max(n, 1)
+    return load().vif_submit_batch(ctx, n, arr(*ref_ptrs), arr(*dist_ptrs))
 
 
 def vif_get_options(ctx, options):

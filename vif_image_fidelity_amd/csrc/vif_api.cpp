@@ -1,9 +1,11 @@
 // vif_api.cpp -- the C ABI of include/vif.h: context, launch sequence, one
 // read-back per frame and the host sums.
 //
-// Every frame has a slot of a three-slot ring, and every slot its own stream
-// and buffers (pyramid planes, term buffers, and its row sums in pinned
-// host memory).  The slot's stream runs the four per-scale kernels (filter,
+// Every submission (one frame, or a batch of up to max_batch frames that
+// each kernel processes in one launch, blockIdx.z being the frame) has a slot
+// of a three-slot ring, and every slot its own stream and buffers (pyramid
+// planes, term buffers, and its row sums in pinned host memory, each sized
+// for max_batch frames).  The slot's stream runs the four per-scale kernels (filter,
 // statistic, terms, next scale's planes) and the ordered row sums of all
 // scales (one launch), which write two floats per row per scale straight
 // into the host buffer: one read-back per frame with no copy call
@@ -46,8 +48,8 @@ constexpr int kDepth = VIF_QUEUE_DEPTH;
 constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
 
 struct Slot {
-  float *pyr_ref[kScales] = {};   // [0] unused: scale 0 reads the frames
-  float *pyr_dist[kScales] = {};
+  float *pyr_ref[kScales] = {};   // [0] unused: scale 0 reads the frames;
+  float *pyr_dist[kScales] = {};  // max_batch planes each, plane_elems apart
   void *frame_ref = nullptr;      // device copies of host frames
   void *frame_dist = nullptr;
   float *terms[kScales] = {};     // term buffers of the four scales
@@ -58,6 +60,8 @@ struct Slot {
   hipEvent_t s0_end = nullptr;    // on the slot's stream, after scale 0
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
+  int n = 0;         // frames of the submission in this slot
+  int taken = 0;     // of those, frames already collected
 };
 
 } // namespace
@@ -71,12 +75,16 @@ struct vif_ctx {
   vifk::ScaleGeom geom[kScales] = {};
   vifk::TapArgs taps[kScales] = {};
   Slot slots[kDepth];
+  int max_batch = 1;                   // frames one submission may carry
+  size_t plane_elems[kScales] = {};    // floats per frame, pyramid plane
+  size_t terms_elems[kScales] = {};    // floats per frame, term buffer
   int total_rows = 0;
   int row_base[kScales] = {};
   int rowsum_waves = 0;
   bool order_scale0 = false; // consecutive frames' scale-0 kernels ordered
   vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
-  long head = 0, tail = 0;      // submitted / collected frame counts
+  long head = 0, tail = 0;   // submitted / collected frame counts
+  long shead = 0, stail = 0; // submitted / released slot counts
   float sums[8] = {};
   double last_out[8] = {};
   float *last_rows = nullptr; // host copy of the last collected row sums
@@ -177,38 +185,48 @@ template <typename T> hipError_t dev_alloc(T **p, size_t elems) {
   return hipMalloc(reinterpret_cast<void **>(p), elems * sizeof(T));
 }
 
-// Enqueues one frame into the slot at ctx->head.
-int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
-  Slot &sl = ctx->slots[ctx->head % kDepth];
+// Enqueues n frames (1 <= n <= max_batch) into the next slot: each kernel
+// runs once for all n frames.
+int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
+                  const void *const *dists) {
+  Slot &sl = ctx->slots[ctx->shead % kDepth];
   hipStream_t st = sl.stream;
   hipError_t e = hipSuccess;
-  // the slot's previous frame is ordered before this one on its stream;
-  // work on the default stream is ordered before it by the blocking stream
+  // the slot's previous frames are ordered before these on its stream;
+  // work on the default stream is ordered before them by the blocking stream
   if (ctx->stream != nullptr) {
     e = hipEventRecord(sl.submitted, ctx->stream);
     if (e == hipSuccess)
       e = hipStreamWaitEvent(st, sl.submitted, 0);
   }
-  // consecutive frames' scale-0 kernels run one after the other when each
-  // fills the GPU (the small scales and row sums of one frame still overlap
-  // the next frame's scale 0)
-  if (e == hipSuccess && ctx->order_scale0 && ctx->head > 0)
-    e = hipStreamWaitEvent(st, ctx->slots[(ctx->head - 1) % kDepth].s0_end,
+  // consecutive submissions' scale-0 kernels run one after the other when
+  // each fills the GPU (the small scales and row sums of one submission
+  // still overlap the next one's scale 0)
+  if (e == hipSuccess && ctx->order_scale0 && ctx->shead > 0)
+    e = hipStreamWaitEvent(st, ctx->slots[(ctx->shead - 1) % kDepth].s0_end,
                            0);
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
-    const void *in_ref = s == 0 ? ref : sl.pyr_ref[s];
-    const void *in_dist = s == 0 ? dist : sl.pyr_dist[s];
-    float *nref = s + 1 < kScales ? sl.pyr_ref[s + 1] : nullptr;
-    float *ndist = s + 1 < kScales ? sl.pyr_dist[s + 1] : nullptr;
+    vifk::ScaleIO io = {};
+    for (int z = 0; z < n; ++z) {
+      io.in_ref[z] = s == 0 ? refs[z] : sl.pyr_ref[s] + z * ctx->plane_elems[s];
+      io.in_dist[z] =
+          s == 0 ? dists[z] : sl.pyr_dist[s] + z * ctx->plane_elems[s];
+    }
+    if (s + 1 < kScales) {
+      io.next_ref = sl.pyr_ref[s + 1];
+      io.next_dist = sl.pyr_dist[s + 1];
+      io.next_stride = ctx->plane_elems[s + 1];
+    }
+    io.terms = sl.terms[s];
+    io.terms_stride = ctx->terms_elems[s];
     const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
     const bool timed = (sl.prof_mask >> s) & 1;
     if (timed)
       e = hipEventRecord(sl.prof[s][0], st);
     if (e == hipSuccess)
-      e = vifk::launch_scale(s, ctx->bpc, in_ref, in_dist, ctx->geom[s],
-                             ctx->taps[s], nt, ctx->stat, nref, ndist,
-                             sl.terms[s], st);
+      e = vifk::launch_scale(s, ctx->bpc, io, n, ctx->geom[s], ctx->taps[s],
+                             nt, ctx->stat, st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
     if (e == hipSuccess && s == 0 && ctx->order_scale0)
@@ -217,28 +235,37 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   vifk::RowSumArgs ra = ctx->rowsum;
   for (int s = 0; s < kScales; ++s) {
     ra.terms[s] = sl.terms[s];
+    ra.terms_stride[s] = ctx->terms_elems[s];
     ra.rows[s] = sl.rows_host + 2 * ctx->row_base[s];
   }
+  ra.rows_stride = static_cast<size_t>(2) * ctx->total_rows;
   const bool timed = (sl.prof_mask >> kScales) & 1;
   if (e == hipSuccess && timed)
     e = hipEventRecord(sl.prof[kScales][0], st);
   if (e == hipSuccess)
-    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, st);
+    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, n, st);
   if (e == hipSuccess && timed)
     e = hipEventRecord(sl.prof[kScales][1], st);
   if (e == hipSuccess)
     e = hipEventRecord(sl.done, st);
   if (e != hipSuccess)
     return vifk::status_from_hip(e);
-  ctx->head += 1;
+  sl.n = n;
+  sl.taken = 0;
+  ctx->shead += 1;
+  ctx->head += n;
   return vifk::set_status(VIF_OK);
+}
+
+int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
+  return submit_frames(ctx, 1, &ref, &dist);
 }
 
 // Enqueues one frame whose planes are in host memory: two copies into the
 // slot's frame buffers on the slot's stream, then the frame itself.  The
 // slot's previous frame read those buffers earlier on the same stream.
 int submit_host_frame(vif_ctx *ctx, const void *ref, const void *dist) {
-  Slot &sl = ctx->slots[ctx->head % kDepth];
+  Slot &sl = ctx->slots[ctx->shead % kDepth];
   const size_t bytes = static_cast<size_t>(ctx->w) * ctx->h *
                        (ctx->bpc == 8 ? 1 : 2);
   hipError_t e = hipMemcpyAsync(sl.frame_ref, ref, bytes,
@@ -251,28 +278,36 @@ int submit_host_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   return submit_frame(ctx, sl.frame_ref, sl.frame_dist);
 }
 
-// Waits for the oldest pending frame and writes its outputs.
+// Waits for the oldest pending frame and writes its outputs.  A slot is
+// released once every frame of its submission has been collected.
 int collect_frame(vif_ctx *ctx, double out[8]) {
-  Slot &sl = ctx->slots[ctx->tail % kDepth];
+  Slot &sl = ctx->slots[ctx->stail % kDepth];
+  const int z = sl.taken;
   hipError_t e = hipEventSynchronize(sl.done);
   if (e != hipSuccess) {
-    ctx->tail += 1; // the frame is lost; keep the ring consistent
+    // the submission is lost; keep the ring consistent
+    ctx->tail += sl.n - z;
+    sl.taken = sl.n;
+    ctx->stail += 1;
     return vifk::status_from_hip(e);
   }
-  for (int k = 0; k < kKinds; ++k) {
-    if (!((sl.prof_mask >> k) & 1))
-      continue;
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, sl.prof[k][0], sl.prof[k][1]) ==
-        hipSuccess) {
-      ctx->kernel_ms[k] += ms;
-      ctx->kernel_launches[k] += 1;
+  if (z == 0) {
+    for (int k = 0; k < kKinds; ++k) {
+      if (!((sl.prof_mask >> k) & 1))
+        continue;
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, sl.prof[k][0], sl.prof[k][1]) ==
+          hipSuccess) {
+        ctx->kernel_ms[k] += ms;
+        ctx->kernel_launches[k] += 1;
+      }
     }
   }
   // a skipped scale 0 contributes nothing: its rows read 0 (the kernels
   // still build the pyramid from it)
   const bool skip0 = ctx->opt.skip_scale0 != 0;
-  std::memcpy(ctx->last_rows, sl.rows_host,
+  std::memcpy(ctx->last_rows,
+              sl.rows_host + static_cast<size_t>(z) * 2 * ctx->total_rows,
               sizeof(float) * 2 * ctx->total_rows);
   if (skip0)
     std::memset(ctx->last_rows, 0, sizeof(float) * 2 * ctx->geom[0].h);
@@ -291,6 +326,9 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
   }
   ctx->have_sums = true;
   ctx->tail += 1;
+  sl.taken = z + 1;
+  if (sl.taken == sl.n)
+    ctx->stail += 1;
   for (int s = 0; s < kScales; ++s)
     out[s] = static_cast<double>(N[s]) / static_cast<double>(D[s]);
   if (skip0)
@@ -352,13 +390,20 @@ __attribute__((visibility("default"))) vif_ctx *vif_create(int w, int h,
 
 __attribute__((visibility("default"))) vif_ctx *
 vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
+  return vif_create_batch(w, h, bpc, opt, 1);
+}
+
+__attribute__((visibility("default"))) vif_ctx *
+vif_create_batch(int w, int h, int bpc, const vif_options *opt,
+                 int max_batch) {
   vif_options o;
   vif_default_options(&o);
   if (opt != nullptr)
     o = *opt;
   if (w < VIF_MIN_SIDE || h < VIF_MIN_SIDE ||
       static_cast<long>(w) * h > VIF_MAX_PIXELS ||
-      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) || !options_ok(o)) {
+      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) || !options_ok(o) ||
+      max_batch < 1 || max_batch > VIF_MAX_BATCH) {
     vifk::set_status(VIF_EINVAL);
     return nullptr;
   }
@@ -375,6 +420,7 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
   c->h = h;
   c->bpc = bpc;
   c->opt = o;
+  c->max_batch = max_batch;
   c->stat = vifk::make_stat_args(o.sigma_nsq, o.enhn_gain_limit);
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) {
@@ -395,6 +441,9 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
     g.ntx = (ws + vifk::kTileW - 1) / vifk::kTileW;
     c->row_base[s] = rows;
     rows += hs;
+    c->plane_elems[s] = static_cast<size_t>(ws) * hs;
+    c->terms_elems[s] = static_cast<size_t>(g.strips) *
+                        vifk::term_groups(ws) * vifk::kSeq * 4;
     const int nt = vifk::gaussian_taps(s, c->taps[s].t);
     // the kernels rely on bitwise symmetric taps (see tap() there)
     for (int k = 0; k < nt; ++k)
@@ -424,12 +473,12 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
   if (c->last_rows == nullptr)
     e = hipErrorOutOfMemory;
 
+  const size_t nb = static_cast<size_t>(max_batch);
   for (Slot &sl : c->slots) {
     for (int s = 1; s < kScales && e == hipSuccess; ++s) {
-      const size_t n = static_cast<size_t>(c->geom[s].w) * c->geom[s].h;
-      e = dev_alloc(&sl.pyr_ref[s], n);
+      e = dev_alloc(&sl.pyr_ref[s], nb * c->plane_elems[s]);
       if (e == hipSuccess)
-        e = dev_alloc(&sl.pyr_dist[s], n);
+        e = dev_alloc(&sl.pyr_dist[s], nb * c->plane_elems[s]);
     }
     const size_t frame_bytes = static_cast<size_t>(w) * h * (bpc == 8 ? 1 : 2);
     if (e == hipSuccess)
@@ -437,14 +486,12 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
     if (e == hipSuccess)
       e = hipMalloc(&sl.frame_dist, frame_bytes);
     for (int s = 0; s < kScales && e == hipSuccess; ++s)
-      e = dev_alloc(&sl.terms[s], static_cast<size_t>(c->geom[s].strips) *
-                                      vifk::term_groups(c->geom[s].w) *
-                                      vifk::kSeq * 4);
+      e = dev_alloc(&sl.terms[s], nb * c->terms_elems[s]);
     // coherent pinned memory: the row-sum kernel's stores reach the host
     // without a copy, visible once the slot's event has completed
     if (e == hipSuccess)
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
-                        sizeof(float) * 2 * rows, hipHostMallocCoherent);
+                        nb * sizeof(float) * 2 * rows, hipHostMallocCoherent);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.submitted, hipEventDisableTiming);
     if (e == hipSuccess)
@@ -494,7 +541,7 @@ __attribute__((visibility("default"))) int vif_set_stream(vif_ctx *ctx,
 __attribute__((visibility("default"))) int
 vif_submit(vif_ctx *ctx, const void *ref, const void *dist) {
   if (ctx == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
-      ctx->head - ctx->tail >= kDepth)
+      ctx->shead - ctx->stail >= kDepth)
     return vifk::set_status(VIF_EINVAL);
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
@@ -505,7 +552,7 @@ vif_submit(vif_ctx *ctx, const void *ref, const void *dist) {
 __attribute__((visibility("default"))) int
 vif_submit_host(vif_ctx *ctx, const void *ref, const void *dist) {
   if (ctx == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
-      ctx->head - ctx->tail >= kDepth)
+      ctx->shead - ctx->stail >= kDepth)
     return vifk::set_status(VIF_EINVAL);
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
@@ -526,6 +573,21 @@ vif_score_host(vif_ctx *ctx, const void *ref, const void *dist,
   if (rc != VIF_OK)
     return rc;
   return collect_frame(ctx, out);
+}
+
+__attribute__((visibility("default"))) int
+vif_submit_batch(vif_ctx *ctx, int n, const void *const *refs,
+                 const void *const *dists) {
+  if (ctx == nullptr || refs == nullptr || dists == nullptr || n < 1 ||
+      n > ctx->max_batch || ctx->shead - ctx->stail >= kDepth)
+    return vifk::set_status(VIF_EINVAL);
+  for (int z = 0; z < n; ++z)
+    if (bad_frame_ptrs(ctx, refs[z], dists[z]))
+      return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  return submit_frames(ctx, n, refs, dists);
 }
 
 __attribute__((visibility("default"))) int vif_collect(vif_ctx *ctx,

@@ -57,11 +57,34 @@ constexpr int kTermPitch = kTileW + 4;
 
 __host__ __device__ inline int term_groups(int w) { return (w + 3) / 4; }
 
+// Frames one launch may carry: blockIdx.z of the scale kernels, blockIdx.y
+// of the row sums.
+constexpr int kMaxBatch = 16;
+
+// Inputs and outputs of one launch of a scale kernel for n frames: frame z
+// reads in_ref[z] / in_dist[z] (the caller's frames at scale 0, the
+// context's planes above) and writes the next scale's planes at
+// next_* + z * next_stride and its terms at terms + z * terms_stride
+// (strides in floats).
+struct ScaleIO {
+  const void *in_ref[kMaxBatch];
+  const void *in_dist[kMaxBatch];
+  float *next_ref;
+  float *next_dist;
+  float *terms;
+  size_t next_stride;
+  size_t terms_stride;
+};
+
 // Arguments of the row-sum kernel (all four scales in one launch): scale s
-// owns the waves [pair_base[s], pair_base[s+1]), one wave per two strips.
+// owns the waves [pair_base[s], pair_base[s+1]), one wave per two strips;
+// frame z (blockIdx.y) reads terms[s] + z * terms_stride[s] and writes
+// rows[s] + z * rows_stride.
 struct RowSumArgs {
   const float *terms[kScales];
   float *rows[kScales]; // rows[s][2*y + c], in pinned host memory
+  size_t terms_stride[kScales];
+  size_t rows_stride;
   int w[kScales], h[kScales], strips[kScales];
   int pair_base[kScales + 1];
 };
@@ -77,22 +100,23 @@ struct ScaleGeom {
   size_t tiles() const { return static_cast<size_t>(strips) * ntx; }
 };
 
-// Per-scale kernel: filter, statistic, terms and the next scale's planes.
-// in_* are the scale's planes (native samples at scale 0, fp32 planes
-// above); next_* receive the next scale's planes (unused at scale 3); terms
-// is the scale's term buffer (strips * term_groups(w) * 128 floats).
-hipError_t launch_scale(int scale, int bpc, const void *in_ref,
-                        const void *in_dist, const ScaleGeom &g,
-                        const TapArgs &taps, const TapArgs &next_taps,
-                        const StatArgs &stat, float *next_ref,
-                        float *next_dist, float *terms, hipStream_t stream);
+// Per-scale kernel for n frames (1 <= n <= kMaxBatch): filter, statistic,
+// terms and the next scale's planes.  io.in_* are the scale's planes (native
+// samples at scale 0, fp32 planes above); io.next_* receive the next scale's
+// planes (unused at scale 3); io.terms is the scale's term buffer (strips *
+// term_groups(w) * 128 floats per frame).
+hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
+                        const ScaleGeom &g, const TapArgs &taps,
+                        const TapArgs &next_taps, const StatArgs &stat,
+                        hipStream_t stream);
 
 // Blocks of the scale-0 kernel the current device keeps resident at once
 // (blocks per CU times CUs).
 hipError_t scale0_resident_blocks(int bpc, int *blocks);
 
-// Ordered row sums of all scales of one frame (`waves` = pair_base[4]).
-hipError_t launch_rowsum(const RowSumArgs &args, int waves,
+// Ordered row sums of all scales of n frames (`waves` = pair_base[4] per
+// frame).
+hipError_t launch_rowsum(const RowSumArgs &args, int waves, int n,
                          hipStream_t stream);
 
 }  // namespace vifk

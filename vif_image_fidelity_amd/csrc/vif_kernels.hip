@@ -122,12 +122,19 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
 // The horizontal pass therefore runs in two rounds (x, y and the next
 // scale's planes, then the three second moments); the second round's
 // vertical results wait in registers until its write.
+//
+// Frame z = blockIdx.z of a batched launch reads io.in_ref[z], io.in_dist[z]
+// and writes at its own offsets of the next scale's planes and the terms.
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
-    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
-    float in_scale, TapArgs taps, TapArgs dtaps, StatArgs stat,
-    float *__restrict__ next_ref, float *__restrict__ next_dist,
-    float *__restrict__ terms) {
+    ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
+    StatArgs stat) {
+  const int z = blockIdx.z;
+  const InT *__restrict__ ref = static_cast<const InT *>(io.in_ref[z]);
+  const InT *__restrict__ dist = static_cast<const InT *>(io.in_dist[z]);
+  float *__restrict__ next_ref = io.next_ref + z * io.next_stride;
+  float *__restrict__ next_dist = io.next_dist + z * io.next_stride;
+  float *__restrict__ terms = io.terms + z * io.terms_stride;
   constexpr int N = 2 * R + 1;
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
@@ -396,6 +403,7 @@ __device__ __forceinline__ float add_batch(float acc, const float4 (&v)[kRowBatc
 
 __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
   const int wave = blockIdx.x;
+  const int z = blockIdx.y; // frame of a batched launch
   int s = 0;
   while (s + 1 < kScales && wave >= a.pair_base[s + 1])
     ++s;
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
   const int w = a.w[s];
   const int groups = term_groups(w);
   const float4 *src = reinterpret_cast<const float4 *>(
-                          a.terms[s] +
+                          a.terms[s] + z * a.terms_stride[s] +
                           static_cast<size_t>(strip) * groups * (kSeq * 4)) +
                       seq;
   float acc = 0.0f;
@@ -424,47 +432,42 @@ __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
   }
   const int y = strip * kTileH + (seq >> 1);
   if (live && y < a.h[s])
-    a.rows[s][2 * y + (seq & 1)] = acc;
+    a.rows[s][z * a.rows_stride + 2 * y + (seq & 1)] = acc;
 }
 
 // ------------------------------------------------------------------ launch
 
-hipError_t launch_scale(int scale, int bpc, const void *in_ref,
-                        const void *in_dist, const ScaleGeom &g,
-                        const TapArgs &taps, const TapArgs &next_taps,
-                        const StatArgs &stat, float *next_ref,
-                        float *next_dist, float *terms, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(g.ntx), static_cast<unsigned>(g.strips));
+hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
+                        const ScaleGeom &g, const TapArgs &taps,
+                        const TapArgs &next_taps, const StatArgs &stat,
+                        hipStream_t stream) {
+  if (n < 1 || n > kMaxBatch)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(g.ntx), static_cast<unsigned>(g.strips),
+                  static_cast<unsigned>(n));
   const dim3 block(kThreads);
   switch (scale) {
   case 0:
     if (bpc == 8) {
       scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
-          static_cast<const uint8_t *>(in_ref),
-          static_cast<const uint8_t *>(in_dist), g.w, g.h, 1.0f, taps,
-          next_taps, stat, next_ref, next_dist, terms);
+          io, g.w, g.h, 1.0f, taps, next_taps, stat);
     } else {
       const float sc = bpc == 10 ? 0.25f : bpc == 12 ? 0.0625f : 0.00390625f;
       scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
-          static_cast<const uint16_t *>(in_ref),
-          static_cast<const uint16_t *>(in_dist), g.w, g.h, sc, taps,
-          next_taps, stat, next_ref, next_dist, terms);
+          io, g.w, g.h, sc, taps, next_taps, stat);
     }
     break;
   case 1:
-    scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
-        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, stat, next_ref, next_dist, terms);
+    scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
+                                                          taps, next_taps, stat);
     break;
   case 2:
-    scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
-        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, stat, next_ref, next_dist, terms);
+    scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
+                                                          taps, next_taps, stat);
     break;
   case 3:
-    scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
-        static_cast<const float *>(in_ref), static_cast<const float *>(in_dist),
-        g.w, g.h, 1.0f, taps, next_taps, stat, nullptr, nullptr, terms);
+    scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
+                                                          taps, next_taps, stat);
     break;
   default:
     return hipErrorInvalidValue;
@@ -489,9 +492,11 @@ hipError_t scale0_resident_blocks(int bpc, int *blocks) {
   return e;
 }
 
-hipError_t launch_rowsum(const RowSumArgs &args, int waves,
+hipError_t launch_rowsum(const RowSumArgs &args, int waves, int n,
                          hipStream_t stream) {
-  rowsum_kernel<<<dim3(waves), dim3(64), 0, stream>>>(args);
+  if (n < 1 || n > kMaxBatch)
+    return hipErrorInvalidValue;
+  rowsum_kernel<<<dim3(waves, n), dim3(64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
