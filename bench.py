@@ -166,9 +166,10 @@ def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0,
     return (t1 - t0), kt
 
 
-def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
+def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0, batch=1):
     """The float SSIM queue over resident frames, as time_frames does for
-    VIF.  Returns (seconds, kernel times, geometry)."""
+    VIF, `batch` frames per submission.  Returns (seconds, kernel times,
+    geometry)."""
     import torch
     dev = torch.device("cuda:0")
 
@@ -179,13 +180,21 @@ def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
         return torch.from_numpy(a).to(dev)
 
     pairs = [(td(r), td(d)) for (r, d, _) in frames]
-    ctx = V.FloatSsim(w, h, bpc)
+    ctx = V.FloatSsim(w, h, bpc, max_batch=batch)
 
     def run(n):
-        for i in range(n):
-            if ctx.pending() == V.FSSIM_QUEUE_DEPTH:
-                ctx.collect()
-            ctx.submit(*pairs[i % len(pairs)])
+        i = 0
+        while i < n:
+            k = min(batch, n - i)
+            if ctx.pending() + k > V.FSSIM_QUEUE_DEPTH * batch:
+                for _ in range(batch):
+                    ctx.collect()
+            sel = [pairs[(i + j) % len(pairs)] for j in range(k)]
+            if batch == 1:
+                ctx.submit(*sel[0])
+            else:
+                ctx.submit_batch([a for a, _ in sel], [b for _, b in sel])
+            i += k
         while ctx.pending():
             ctx.collect()
 
@@ -202,10 +211,10 @@ def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0):
     return (t1 - t0), kt, geom
 
 
-def fssim_kernel_us(V, frames, w, h, bpc, n=300):
+def fssim_kernel_us(V, frames, w, h, bpc, n=300, batch=1):
     """Average kernel durations (HIP events on the slot's stream around each
-    launch) with one frame at a time (fssim_score), so that no other frame's
-    kernels share the GPU during a timed launch."""
+    launch) with one submission of `batch` frames at a time, so that no other
+    submission's kernels share the GPU during a timed launch."""
     import torch
     dev = torch.device("cuda:0")
 
@@ -216,36 +225,52 @@ def fssim_kernel_us(V, frames, w, h, bpc, n=300):
         return torch.from_numpy(a).to(dev)
 
     pairs = [(td(r), td(d)) for (r, d, _) in frames[:4]]
-    ctx = V.FloatSsim(w, h, bpc)
+    ctx = V.FloatSsim(w, h, bpc, max_batch=batch)
+
+    def one(i):
+        sel = [pairs[(i + j) % len(pairs)] for j in range(batch)]
+        ctx.submit_batch([a for a, _ in sel], [b for _, b in sel])
+        for _ in range(batch):
+            ctx.collect()
+
     for i in range(10):
-        ctx.score(*pairs[i % len(pairs)])
+        one(i)
     ctx.set_profiling(0x7)
     for i in range(n):
-        ctx.score(*pairs[i % len(pairs)])
+        one(i)
     kt = ctx.kernel_times()
     ctx.close()
     return {k: 1000.0 * v[0] / max(v[1], 1) for k, v in kt.items()}
 
 
-def fssim_leg(V, frames, w, h, bpc, steps, cpu_budget_s):
-    """frames/s of the float SSIM queue (no timing events), the kernels'
-    average durations one frame at a time, the decimation kernel against
-    the HBM peak, and the oracle on this host."""
+def fssim_leg(V, frames, w, h, bpc, steps, cpu_budget_s, batch=8):
+    """frames/s of the float SSIM queue (no timing events), one frame and
+    `batch` frames per submission; the kernels' average durations with one
+    submission at a time; the decimation kernel against the HBM peak (per
+    launch of one frame and of a batch); and the oracle on this host."""
     dt, _, (f, ow, oh) = time_fssim(V, frames, w, h, bpc, steps, 20)
+    dtb, _, _ = time_fssim(V, frames, w, h, bpc, steps, 4 * batch,
+                           batch=batch)
     avg = fssim_kernel_us(V, frames, w, h, bpc)
+    avgb = fssim_kernel_us(V, frames, w, h, bpc, n=100, batch=batch)
     bps = 1 if bpc == 8 else 2
     dec_bytes = 2 * w * h * bps + 2 * ow * oh * 4
     rec = {"workload": "%dx%d %d-bit, factor %d -> %dx%d" % (w, h, bpc, f,
                                                              ow, oh),
            "fps": round(steps / dt, 1),
-           "kernel_avg_us": {k: round(v, 2) for k, v in avg.items()}}
+           "fps_batch%d" % batch: round(steps / dtb, 1),
+           "kernel_avg_us": {k: round(v, 2) for k, v in avg.items()},
+           "kernel_avg_us_batch%d" % batch: {k: round(v, 2)
+                                             for k, v in avgb.items()}}
     if f > 1 and avg["decimate"] > 0:
-        gbs = dec_bytes / (avg["decimate"] * 1e-6) / 1e9
-        rec["decimate_roofline"] = {
-            "bound": "hbm", "achieved": round(gbs, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": dec_bytes}
+        for key, us, nb in (("decimate_roofline", avg["decimate"], 1),
+                            ("decimate_roofline_batch%d" % batch,
+                             avgb["decimate"], batch)):
+            gbs = nb * dec_bytes / (us * 1e-6) / 1e9
+            rec[key] = {"bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": nb * dec_bytes}
     if cpu_budget_s > 0:
         import oracle
         n, t0 = 0, time.perf_counter()
@@ -369,6 +394,9 @@ def main():
     ap.add_argument("--frames", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-1080p", type=int, default=500)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="frames per submission in the frames and fssim "
+                    "modes")
     ap.add_argument("--mode", choices=["full", "frames", "copy", "fssim"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
@@ -399,13 +427,15 @@ def main():
     w, h, bpc = 3840, 2160, 8
     if args.mode == "fssim":
         dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps,
-                                 args.warmup)
-        print("4K float SSIM (factor %d): %.1f frames/s"
-              % (geom[0], args.steps / dt), file=sys.stderr, flush=True)
+                                 args.warmup, batch=args.batch)
+        print("4K float SSIM (factor %d, %d per submission): %.1f frames/s"
+              % (geom[0], args.batch, args.steps / dt), file=sys.stderr,
+              flush=True)
         return
 
     dt, kt = time_frames(V, frames4k, w, h, bpc, args.steps, args.warmup,
-                         prof_kinds=["scale0"])
+                         prof_kinds=["scale0"],
+                         batch=args.batch if args.mode == "frames" else 1)
     fps = args.steps / dt
     ms_step = 1000.0 * dt / args.steps
     s0_ms, s0_n = kt["scale0"]

@@ -97,6 +97,20 @@ int fssim_collect(fssim_ctx *ctx, double out[2]);
 int fssim_pending(const fssim_ctx *ctx);
 
 /*
+ * Batched submission, as vif_create_batch / vif_submit_batch: a context from
+ * fssim_create_batch (1 <= max_batch <= FSSIM_MAX_BATCH; buffers sized for
+ * max_batch frames per queue slot) accepts fssim_submit_batch of n <=
+ * max_batch pairs as one slot, each kernel running once for all n frames;
+ * fssim_collect returns them one by one in order.  The same bits as n single
+ * submissions.  VIF_EINVAL for a bad n, NULL arrays or frames, or a full
+ * queue.  fssim_create makes max_batch = 1.  Allocates nothing.
+ */
+#define FSSIM_MAX_BATCH 16
+fssim_ctx *fssim_create_batch(int w, int h, int bpc, int max_batch);
+int fssim_submit_batch(fssim_ctx *ctx, int n, const void *const *refs,
+                       const void *const *dists);
+
+/*
  * fssim_set_stream -- the caller's HIP stream (hipStream_t as void*; NULL =
  * the default stream): work queued on it before a submit is ordered before
  * the frame's kernels.  VIF_EINVAL while frames are pending.

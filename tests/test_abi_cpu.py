@@ -231,3 +231,10 @@ def test_create_batch_rejects_bad_capacity(lib, mb):
 def test_submit_batch_null_context(lib):
     from vif_image_fidelity_amd import _lib
     assert _lib.vif_submit_batch(None, [0], [0]) == _lib.VIF_EINVAL
+
+
+@pytest.mark.parametrize("mb", [0, 17])
+def test_fssim_create_batch_rejects_bad_capacity(lib, mb):
+    from vif_image_fidelity_amd import _lib
+    assert not _lib.fssim_create_batch(64, 64, 8, mb)
+    assert _lib.vif_errno() == _lib.VIF_EINVAL

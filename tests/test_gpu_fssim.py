@@ -222,3 +222,52 @@ def test_bad_calls(V):
     assert _lib.fssim_score(w16._ctx, buf.data_ptr() + 1,
                             buf.data_ptr() + 1, out) == _lib.VIF_EINVAL
     w16.close()
+
+
+@pytest.mark.parametrize("w,h,bpc,n", [(3840, 2160, 8, 4), (1920, 1080, 10, 8),
+                                       (1280, 720, 8, 3), (576, 324, 8, 16),
+                                       (40, 40, 8, 5)])
+def test_batch_matches_oracle(V, orc, w, h, bpc, n):
+    """n pairs in one submission (each kernel launched once for all of
+    them): every frame's score, map, planes and row sums equal the oracle's;
+    factors 8, 4, 3 (the fp64 path) and 1."""
+    from vif_image_fidelity_amd import synth
+    print("fssim batch case %dx%d bpc %d n=%d" % (w, h, bpc, n), flush=True)
+    frames = [synth.noisy_pair(w, h, bpc, seed=300 + k) for k in range(3)]
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    idx = [(2 * i + 1) % 3 for i in range(n)]
+    ctx = V.FloatSsim(w, h, bpc, max_batch=n)
+    ctx.submit_batch([dev[k][0] for k in idx], [dev[k][1] for k in idx])
+    assert ctx.pending() == n
+    for i, k in enumerate(idx):
+        got = ctx.collect()
+        r, d, b = frames[k]
+        if i == n - 1:
+            # nothing pending now: the debug getters see this frame
+            _check(V, orc, ctx, got, r, d, b, "batch[%d]" % i)
+        else:
+            exp = orc.fssim_score(r, d, b)
+            assert _bits(got).tolist() == _bits(exp).tolist(), (i, got, exp)
+    ctx.close()
+
+
+def test_batch_mixed_with_single_and_limits(V, orc):
+    from vif_image_fidelity_amd import synth
+    frames = [synth.noisy_pair(800, 450, 8, seed=400 + k) for k in range(3)]
+    exps = [orc.fssim_score(r, d, b) for r, d, b in frames]
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.FloatSsim(800, 450, 8, max_batch=4)
+    order = [0, 1, 2]
+    ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+    ctx.submit(*dev[1])
+    order.append(1)
+    ctx.submit_batch([dev[2][0]] * 4, [dev[2][1]] * 4)
+    order += [2] * 4
+    with pytest.raises(V.VifError):
+        ctx.submit(*dev[0])
+    with pytest.raises(V.VifError):
+        ctx.submit_batch([dev[0][0]] * 5, [dev[0][1]] * 5)
+    for k in order:
+        assert _bits(ctx.collect()).tolist() == _bits(exps[k]).tolist()
+    assert ctx.pending() == 0
+    ctx.close()

@@ -288,9 +288,14 @@ class FloatSsim:
     12, 16).  The frame is decimated by factor() first when that is above
     1; geometry() gives (factor, w', h')."""
 
-    def __init__(self, w, h, bpc, stream=None):
+    def __init__(self, w, h, bpc, stream=None, max_batch=1):
         self.w, self.h, self.bpc = int(w), int(h), int(bpc)
-        ctx = _lib.fssim_create(self.w, self.h, self.bpc)
+        self.max_batch = int(max_batch)
+        if self.max_batch != 1:
+            ctx = _lib.fssim_create_batch(self.w, self.h, self.bpc,
+                                          self.max_batch)
+        else:
+            ctx = _lib.fssim_create(self.w, self.h, self.bpc)
         if not ctx:
             raise VifError(_lib.vif_errno(), "fssim_create")
         self._ctx = ctx
@@ -337,6 +342,15 @@ class FloatSsim:
         rc = _lib.fssim_submit(self._ctx, _ptr(ref), _ptr(dist))
         if rc != VIF_OK:
             raise VifError(rc, "fssim_submit")
+
+    def submit_batch(self, refs, dists):
+        """Enqueue len(refs) pairs (at most max_batch) as one submission."""
+        for t in list(refs) + list(dists):
+            self._check_frame(t)
+        rc = _lib.fssim_submit_batch(self._ctx, [_ptr(r) for r in refs],
+                                     [_ptr(d) for d in dists])
+        if rc != VIF_OK:
+            raise VifError(rc, "fssim_submit_batch")
 
     def collect(self):
         out = np.zeros(2, dtype=np.float64)

@@ -99,6 +99,9 @@ def load():
                                     ctypes.c_double, ctypes.c_double, vp, vp,
                                     vp], ip),
         "fssim_create": ([ip, ip, ip], vp),
+        "fssim_create_batch": ([ip, ip, ip, ip], vp),
+        "fssim_submit_batch": ([vp, ip, ctypes.POINTER(vp),
+                                ctypes.POINTER(vp)], ip),
         "fssim_destroy": ([vp], None),
         "fssim_geometry": ([vp, ctypes.POINTER(ctypes.c_int)], ip),
         "fssim_score": ([vp, vp, vp, dp], ip),
@@ -134,7 +137,8 @@ def exported_symbols():
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
             "vif_selftest_log2", "vif_selftest_ratios",
             "vif_selftest_statistic",
-            "fssim_create", "fssim_destroy", "fssim_geometry", "fssim_score",
+            "fssim_create", "fssim_create_batch", "fssim_submit_batch",
+            "fssim_destroy", "fssim_geometry", "fssim_score",
             "fssim_submit", "fssim_collect", "fssim_pending",
             "fssim_set_stream", "fssim_get_row_sums", "fssim_get_map",
             "fssim_get_planes", "fssim_taps", "fssim_set_profiling",
@@ -250,6 +254,19 @@ def vif_strerror(code):
 
 def fssim_create(w, h, bpc):
     return load().fssim_create(int(w), int(h), int(bpc))
+
+
+def fssim_create_batch(w, h, bpc, max_batch):
+    return load().fssim_create_batch(int(w), int(h), int(bpc),
+                                     int(max_batch))
+
+
+def fssim_submit_batch(ctx, ref_ptrs, dist_ptrs):
+    n = len(ref_ptrs)
+    if len(dist_ptrs) != n:
+        raise ValueError("as many distorted as reference frames")
+    arr = ctypes.c_void_p * max(n, 1)
+    return load().fssim_submit_batch(ctx, n, arr(*ref_ptrs), arr(*dist_ptrs))
 
 
 def fssim_destroy(ctx):

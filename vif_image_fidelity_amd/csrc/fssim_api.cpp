@@ -1,12 +1,14 @@
 // fssim_api.cpp -- the C ABI of include/fssim.h: context, launch sequence
 // and the host mean.
 //
-// Each frame takes a slot of a three-slot ring; each slot has its own
-// stream, decimated planes, SSIM map and pinned row sums, so consecutive
-// frames overlap on the device.  A frame is three launches on its slot's
-// stream (decimation when the factor is above 1, the SSIM stage, the
-// ordered row sums, which store straight into the slot's pinned host
-// buffer) and one event.  Collect waits for the event and adds the rows top
+// Each submission (one frame, or a batch of up to max_batch frames that
+// every kernel processes in one launch) takes a slot of a three-slot ring;
+// each slot has its own stream, decimated planes, SSIM maps and pinned row
+// sums, sized for max_batch frames, so consecutive submissions overlap on
+// the device.  A submission is three launches on its slot's stream
+// (decimation when the factor is above 1, the SSIM stage, the ordered row
+// sums, which store straight into the slot's pinned host buffer) and one
+// event.  Collect waits for the event and adds the rows top
 // to bottom in fp64; the mean is that sum divided by the pixel count in
 // fp64, rounded to fp32 (Research-2130 "float_ssim decimation on the SYCL
 // device", Sources and Findings: iqa_ssim() returns the frame mean as an
@@ -38,6 +40,8 @@ struct FSlot {
   hipEvent_t done = nullptr;
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0;
+  int n = 0;     // frames of the submission in this slot
+  int taken = 0; // of those, frames already collected
 };
 
 } // namespace
@@ -51,9 +55,14 @@ struct fssim_ctx {
   fssimk::SsimArgs sa = {};
   hipStream_t stream = nullptr;
   FSlot slots[kDepth];
-  long head = 0, tail = 0;
+  int max_batch = 1;
+  size_t plane = 0;          // floats of one decimated plane
+  size_t map_elems = 0;      // floats of one frame's map
+  long head = 0, tail = 0;   // submitted / collected frames
+  long shead = 0, stail = 0; // submitted / released slots
   double *last_rows = nullptr;
   bool have = false;
+  int last_slot = 0, last_z = 0; // where the last collected frame lives
   int prof_mask = 0;
   double kernel_ms[kKinds] = {};
   long kernel_launches[kKinds] = {};
@@ -117,8 +126,9 @@ bool bad_frame_ptrs(const fssim_ctx *ctx, const void *ref, const void *dist) {
                             reinterpret_cast<uintptr_t>(dist)) & 1u);
 }
 
-int submit_frame(fssim_ctx *ctx, const void *ref, const void *dist) {
-  FSlot &sl = ctx->slots[ctx->head % kDepth];
+int submit_frames(fssim_ctx *ctx, int n, const void *const *refs,
+                  const void *const *dists) {
+  FSlot &sl = ctx->slots[ctx->shead % kDepth];
   hipStream_t st = sl.stream;
   hipError_t e = hipSuccess;
   if (ctx->stream != nullptr) {
@@ -136,68 +146,95 @@ int submit_frame(fssim_ctx *ctx, const void *ref, const void *dist) {
     if (e == hipSuccess && on)
       e = hipEventRecord(sl.prof[k][1], st);
   };
+  fssimk::FramePair in = {};
+  for (int z = 0; z < n; ++z) {
+    in.a[z] = refs[z];
+    in.b[z] = dists[z];
+  }
   if (ctx->f > 1) {
     timed(0, [&] {
-      return fssimk::launch_decimate(ctx->bpc, ref, dist, ctx->w, ctx->h,
-                                     ctx->f, ctx->tap, ctx->in_scale, ctx->ow,
+      return fssimk::launch_decimate(ctx->bpc, in, n, ctx->w, ctx->h, ctx->f,
+                                     ctx->tap, ctx->in_scale, ctx->ow,
                                      ctx->oh, sl.dref, sl.ddist, st);
     });
+    fssimk::FramePair dec = {};
+    for (int z = 0; z < n; ++z) {
+      dec.a[z] = sl.dref + z * ctx->plane;
+      dec.b[z] = sl.ddist + z * ctx->plane;
+    }
     timed(1, [&] {
-      return fssimk::launch_ssim(0, sl.dref, sl.ddist, ctx->ow, ctx->oh,
-                                 1.0f, ctx->sa, sl.map, st);
+      return fssimk::launch_ssim(0, dec, n, ctx->ow, ctx->oh, 1.0f, ctx->sa,
+                                 sl.map, st);
     });
   } else {
     timed(1, [&] {
-      return fssimk::launch_ssim(ctx->bpc, ref, dist, ctx->w, ctx->h,
+      return fssimk::launch_ssim(ctx->bpc, in, n, ctx->w, ctx->h,
                                  ctx->in_scale, ctx->sa, sl.map, st);
     });
   }
   timed(2, [&] {
-    return fssimk::launch_ssim_rowsum(sl.map, ctx->ow, ctx->oh, sl.rows_host,
-                                      st);
+    return fssimk::launch_ssim_rowsum(sl.map, n, ctx->ow, ctx->oh,
+                                      sl.rows_host, st);
   });
   if (e == hipSuccess)
     e = hipEventRecord(sl.done, st);
   if (e != hipSuccess)
     return vifk::status_from_hip(e);
-  ctx->head += 1;
+  sl.n = n;
+  sl.taken = 0;
+  ctx->shead += 1;
+  ctx->head += n;
   return vifk::set_status(VIF_OK);
 }
 
 int collect_frame(fssim_ctx *ctx, double out[2]) {
-  FSlot &sl = ctx->slots[ctx->tail % kDepth];
+  const int si = static_cast<int>(ctx->stail % kDepth);
+  FSlot &sl = ctx->slots[si];
+  const int z = sl.taken;
   hipError_t e = hipEventSynchronize(sl.done);
   if (e != hipSuccess) {
-    ctx->tail += 1;
+    ctx->tail += sl.n - z;
+    sl.taken = sl.n;
+    ctx->stail += 1;
     return vifk::status_from_hip(e);
   }
-  for (int k = 0; k < kKinds; ++k) {
-    if (!((sl.prof_mask >> k) & 1) || (k == 0 && ctx->f == 1))
-      continue;
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, sl.prof[k][0], sl.prof[k][1]) ==
-        hipSuccess) {
-      ctx->kernel_ms[k] += ms;
-      ctx->kernel_launches[k] += 1;
+  if (z == 0) {
+    for (int k = 0; k < kKinds; ++k) {
+      if (!((sl.prof_mask >> k) & 1) || (k == 0 && ctx->f == 1))
+        continue;
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, sl.prof[k][0], sl.prof[k][1]) ==
+          hipSuccess) {
+        ctx->kernel_ms[k] += ms;
+        ctx->kernel_launches[k] += 1;
+      }
     }
   }
-  std::memcpy(ctx->last_rows, sl.rows_host, sizeof(double) * ctx->oh);
+  std::memcpy(ctx->last_rows,
+              sl.rows_host + static_cast<size_t>(z) * ctx->pitch,
+              sizeof(double) * ctx->oh);
   double total = 0.0;
   for (int y = 0; y < ctx->oh; ++y)
     total = total + ctx->last_rows[y];
   const double n = static_cast<double>(ctx->ow) * static_cast<double>(ctx->oh);
   ctx->have = true;
+  ctx->last_slot = si;
+  ctx->last_z = z;
   ctx->tail += 1;
+  sl.taken = z + 1;
+  if (sl.taken == sl.n)
+    ctx->stail += 1;
   out[0] = static_cast<double>(static_cast<float>(total / n));
   out[1] = static_cast<double>(ctx->f);
   return vifk::set_status(VIF_OK);
 }
 
-// The slot of the last returned frame, when its buffers are still its own.
+// The slot of the last returned frame, when its buffers are still its own
+// (nothing submitted since).
 const FSlot *last_slot(const fssim_ctx *ctx) {
   if (ctx == nullptr || !ctx->have || ctx->head != ctx->tail)
     return nullptr;
-  return &ctx->slots[(ctx->tail - 1) % kDepth];
+  return &ctx->slots[ctx->last_slot];
 }
 
 } // namespace
@@ -206,9 +243,15 @@ extern "C" {
 
 __attribute__((visibility("default"))) fssim_ctx *fssim_create(int w, int h,
                                                                int bpc) {
+  return fssim_create_batch(w, h, bpc, 1);
+}
+
+__attribute__((visibility("default"))) fssim_ctx *
+fssim_create_batch(int w, int h, int bpc, int max_batch) {
   if (w < 1 || h < 1 || static_cast<long>(w) * h > FSSIM_MAX_PIXELS ||
       (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) ||
-      fssimk::factor(w, h) > FSSIM_MAX_FACTOR) {
+      fssimk::factor(w, h) > FSSIM_MAX_FACTOR || max_batch < 1 ||
+      max_batch > FSSIM_MAX_BATCH) {
     vifk::set_status(VIF_EINVAL);
     return nullptr;
   }
@@ -220,6 +263,7 @@ __attribute__((visibility("default"))) fssim_ctx *fssim_create(int w, int h,
   c->w = w;
   c->h = h;
   c->bpc = bpc;
+  c->max_batch = max_batch;
   c->f = fssimk::factor(w, h);
   c->ow = c->f > 1 ? fssimk::decimated_size(w, c->f) : w;
   c->oh = c->f > 1 ? fssimk::decimated_size(h, c->f) : h;
@@ -239,23 +283,24 @@ __attribute__((visibility("default"))) fssim_ctx *fssim_create(int w, int h,
   c->last_rows = static_cast<double *>(std::calloc(c->oh, sizeof(double)));
   if (c->last_rows == nullptr && e == hipSuccess)
     e = hipErrorOutOfMemory;
-  const size_t plane = static_cast<size_t>(c->ow) * c->oh;
-  const size_t map = static_cast<size_t>(c->ow) * c->pitch;
+  c->plane = static_cast<size_t>(c->ow) * c->oh;
+  c->map_elems = static_cast<size_t>(c->ow) * c->pitch;
+  const size_t nb = static_cast<size_t>(max_batch);
   for (FSlot &sl : c->slots) {
     if (c->f > 1) {
       if (e == hipSuccess)
-        e = hipMalloc(reinterpret_cast<void **>(&sl.dref), plane * 4);
+        e = hipMalloc(reinterpret_cast<void **>(&sl.dref), nb * c->plane * 4);
       if (e == hipSuccess)
-        e = hipMalloc(reinterpret_cast<void **>(&sl.ddist), plane * 4);
+        e = hipMalloc(reinterpret_cast<void **>(&sl.ddist), nb * c->plane * 4);
     }
     if (e == hipSuccess)
-      e = hipMalloc(reinterpret_cast<void **>(&sl.map), map * 4);
+      e = hipMalloc(reinterpret_cast<void **>(&sl.map), nb * c->map_elems * 4);
     // the row sums also read the map's padding rows (and drop them)
     if (e == hipSuccess)
-      e = hipMemset(sl.map, 0, map * 4);
+      e = hipMemset(sl.map, 0, nb * c->map_elems * 4);
     if (e == hipSuccess)
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
-                        sizeof(double) * c->pitch, hipHostMallocCoherent);
+                        nb * sizeof(double) * c->pitch, hipHostMallocCoherent);
     if (e == hipSuccess)
       e = hipEventCreateWithFlags(&sl.submitted, hipEventDisableTiming);
     if (e == hipSuccess)
@@ -317,12 +362,27 @@ __attribute__((visibility("default"))) int fssim_set_stream(fssim_ctx *ctx,
 __attribute__((visibility("default"))) int
 fssim_submit(fssim_ctx *ctx, const void *ref, const void *dist) {
   if (ctx == nullptr || bad_frame_ptrs(ctx, ref, dist) ||
-      ctx->head - ctx->tail >= kDepth)
+      ctx->shead - ctx->stail >= kDepth)
     return vifk::set_status(VIF_EINVAL);
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
     return vifk::status_from_hip(scope.error());
-  return submit_frame(ctx, ref, dist);
+  return submit_frames(ctx, 1, &ref, &dist);
+}
+
+__attribute__((visibility("default"))) int
+fssim_submit_batch(fssim_ctx *ctx, int n, const void *const *refs,
+                   const void *const *dists) {
+  if (ctx == nullptr || refs == nullptr || dists == nullptr || n < 1 ||
+      n > ctx->max_batch || ctx->shead - ctx->stail >= kDepth)
+    return vifk::set_status(VIF_EINVAL);
+  for (int z = 0; z < n; ++z)
+    if (bad_frame_ptrs(ctx, refs[z], dists[z]))
+      return vifk::set_status(VIF_EINVAL);
+  DeviceScope scope(ctx->device);
+  if (scope.error() != hipSuccess)
+    return vifk::status_from_hip(scope.error());
+  return submit_frames(ctx, n, refs, dists);
 }
 
 __attribute__((visibility("default"))) int fssim_collect(fssim_ctx *ctx,
@@ -350,7 +410,7 @@ fssim_score(fssim_ctx *ctx, const void *ref, const void *dist, double out[2]) {
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
     return vifk::status_from_hip(scope.error());
-  const int rc = submit_frame(ctx, ref, dist);
+  const int rc = submit_frames(ctx, 1, &ref, &dist);
   if (rc != VIF_OK)
     return rc;
   return collect_frame(ctx, out);
@@ -380,8 +440,9 @@ fssim_get_map(fssim_ctx *ctx, float *map, long capacity) {
   } catch (...) {
     return vifk::set_status(VIF_ENOMEM);
   }
-  const hipError_t e = hipMemcpy(cm.data(), sl->map, cm.size() * 4,
-                                 hipMemcpyDeviceToHost);
+  const hipError_t e =
+      hipMemcpy(cm.data(), sl->map + ctx->last_z * ctx->map_elems,
+                cm.size() * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess)
     return vifk::status_from_hip(e);
   for (int y = 0; y < ctx->oh; ++y)
@@ -401,11 +462,11 @@ fssim_get_planes(fssim_ctx *ctx, float *planes, long capacity) {
   DeviceScope scope(ctx->device);
   if (scope.error() != hipSuccess)
     return vifk::status_from_hip(scope.error());
-  hipError_t e = hipMemcpy(planes, sl->dref, static_cast<size_t>(n) * 4,
-                           hipMemcpyDeviceToHost);
+  hipError_t e = hipMemcpy(planes, sl->dref + ctx->last_z * ctx->plane,
+                           static_cast<size_t>(n) * 4, hipMemcpyDeviceToHost);
   if (e == hipSuccess)
-    e = hipMemcpy(planes + n, sl->ddist, static_cast<size_t>(n) * 4,
-                  hipMemcpyDeviceToHost);
+    e = hipMemcpy(planes + n, sl->ddist + ctx->last_z * ctx->plane,
+                  static_cast<size_t>(n) * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess)
     return vifk::status_from_hip(e);
   vifk::set_status(VIF_OK);

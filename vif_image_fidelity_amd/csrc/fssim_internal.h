@@ -44,21 +44,31 @@ SsimArgs make_ssim_args();
 int factor(int w, int h);
 int decimated_size(int n, int f);
 
-// Decimates both planes (samples of bpc bits, 1 or 2 bytes) by f into
-// dref / ddist (ow x oh fp32, row-major, pitch ow).
-hipError_t launch_decimate(int bpc, const void *ref, const void *dist, int w,
-                           int h, int f, float tap, float in_scale, int ow,
-                           int oh, float *dref, float *ddist,
-                           hipStream_t stream);
+// Frames one launch may carry (blockIdx.z of the decimation and SSIM
+// kernels, blockIdx.y of the row sums).
+constexpr int kMaxBatch = 16;
 
-// SSIM stage of a w x h pair into map (column-major, pitch map_pitch(h)).
-// bpc 0 means fp32 planes (the decimated ones); 8..16 the samples.
-hipError_t launch_ssim(int bpc, const void *x, const void *y, int w, int h,
+// Per-frame planes of a launch: frame z reads a[z] and b[z].
+struct FramePair {
+  const void *a[kMaxBatch];
+  const void *b[kMaxBatch];
+};
+
+// Decimates both planes of n frames (samples of bpc bits, 1 or 2 bytes) by
+// f into dref / ddist + z * ow * oh (ow x oh fp32, row-major, pitch ow).
+hipError_t launch_decimate(int bpc, const FramePair &in, int n, int w, int h,
+                           int f, float tap, float in_scale, int ow, int oh,
+                           float *dref, float *ddist, hipStream_t stream);
+
+// SSIM stage of n w x h pairs into map + z * w * map_pitch(h) (column-major,
+// pitch map_pitch(h)).  bpc 0 means fp32 planes (the decimated ones); 8..16
+// the samples.
+hipError_t launch_ssim(int bpc, const FramePair &in, int n, int w, int h,
                        float in_scale, const SsimArgs &sa, float *map,
                        hipStream_t stream);
 
-// Ordered fp64 sums of the map's rows into rows[0..h).
-hipError_t launch_ssim_rowsum(const float *map, int w, int h, double *rows,
-                              hipStream_t stream);
+// Ordered fp64 sums of the rows of n maps into rows + z * map_pitch(h).
+hipError_t launch_ssim_rowsum(const float *map, int n, int w, int h,
+                              double *rows, hipStream_t stream);
 
 } // namespace fssimk

@@ -102,9 +102,15 @@ constexpr int kRowGroup = 8;
 
 template <typename InT, bool kVec>
 __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
-    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
-    int f, float tap, float in_scale, int ow, int xpb,
-    float *__restrict__ dref, float *__restrict__ ddist) {
+    FramePair in, int w, int h, int f, float tap, float in_scale, int ow,
+    int oh, int xpb, float *__restrict__ dref_all,
+    float *__restrict__ ddist_all) {
+  const int z = blockIdx.z; // frame of a batched launch
+  const InT *__restrict__ ref = static_cast<const InT *>(in.a[z]);
+  const InT *__restrict__ dist = static_cast<const InT *>(in.b[z]);
+  const size_t plane = static_cast<size_t>(ow) * static_cast<size_t>(oh);
+  float *__restrict__ dref = dref_all + z * plane;
+  float *__restrict__ ddist = ddist_all + z * plane;
   __shared__ double cs[2][kDecSpan];
   const int t = threadIdx.x;
   const int y = blockIdx.y;
@@ -226,10 +232,15 @@ __device__ __forceinline__ void unpack4(const uint32_t (&s)[4],
 
 template <typename InT, bool kVec, int F>
 __global__ __launch_bounds__(kDecThreads) void decimate_pow2_kernel(
-    const InT *__restrict__ ref, const InT *__restrict__ dist, int w, int h,
-    float iscale, int ow, int xpb, float *__restrict__ dref,
-    float *__restrict__ ddist) {
+    FramePair in, int w, int h, float iscale, int ow, int oh, int xpb,
+    float *__restrict__ dref_all, float *__restrict__ ddist_all) {
   constexpr int f = F;
+  const int z = blockIdx.z; // frame of a batched launch
+  const InT *__restrict__ ref = static_cast<const InT *>(in.a[z]);
+  const InT *__restrict__ dist = static_cast<const InT *>(in.b[z]);
+  const size_t plane = static_cast<size_t>(ow) * static_cast<size_t>(oh);
+  float *__restrict__ dref = dref_all + z * plane;
+  float *__restrict__ ddist = ddist_all + z * plane;
   __shared__ uint32_t cs[2][kDecSpan];
   const int t = threadIdx.x;
   const int y = blockIdx.y;
@@ -315,8 +326,13 @@ __device__ __forceinline__ float wtap(const SsimArgs &sa, int k) {
 // every input is >= +0, so the product is never -0 and both are the same.
 template <typename InT>
 __global__ __launch_bounds__(256) void ssim_kernel(
-    const InT *__restrict__ px, const InT *__restrict__ py, int w, int h,
-    float in_scale, SsimArgs sa, float *__restrict__ map, int pitch) {
+    FramePair in, int w, int h, float in_scale, SsimArgs sa,
+    float *__restrict__ map_all, int pitch) {
+  const int zf = blockIdx.z; // frame of a batched launch
+  const InT *__restrict__ px = static_cast<const InT *>(in.a[zf]);
+  const InT *__restrict__ py = static_cast<const InT *>(in.b[zf]);
+  float *__restrict__ map =
+      map_all + zf * static_cast<size_t>(w) * static_cast<size_t>(pitch);
   constexpr int R = kRadius;
   constexpr int IW = kTileW + 2 * R; // 74 columns
   constexpr int IH = kTileH + 2 * R; // 26 rows
@@ -476,9 +492,13 @@ __device__ __forceinline__ void store_chunk(float *buf,
 }
 
 __global__ __launch_bounds__(256) void rowsum_kernel(
-    const float *__restrict__ map, int w, int h, int pitch,
-    double *__restrict__ rows) {
+    const float *__restrict__ map_all, int w, int h, int pitch,
+    double *__restrict__ rows_all) {
   __shared__ float buf[2][kSumCols * 64];
+  const int zf = blockIdx.y; // frame of a batched launch
+  const float *__restrict__ map =
+      map_all + zf * static_cast<size_t>(w) * static_cast<size_t>(pitch);
+  double *__restrict__ rows = rows_all + zf * static_cast<size_t>(pitch);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -525,16 +545,17 @@ __global__ __launch_bounds__(256) void rowsum_kernel(
 namespace {
 
 template <typename InT>
-hipError_t launch_decimate_t(const InT *ref, const InT *dist, int w, int h,
-                             int f, float tap, float in_scale, int ow, int oh,
+hipError_t launch_decimate_t(const FramePair &in, int n, int w, int h, int f,
+                             float tap, float in_scale, int ow, int oh,
                              float *dref, float *ddist, hipStream_t stream) {
   const int xpb = outputs_per_block(f);
   const dim3 grid(static_cast<unsigned>((ow + xpb - 1) / xpb),
-                  static_cast<unsigned>(oh));
+                  static_cast<unsigned>(oh), static_cast<unsigned>(n));
   const uintptr_t align = 4 * sizeof(InT);
-  const bool vec = w % 4 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(ref) |
-                     reinterpret_cast<uintptr_t>(dist)) % align) == 0;
+  bool vec = w % 4 == 0;
+  for (int z = 0; z < n; ++z)
+    vec = vec && ((reinterpret_cast<uintptr_t>(in.a[z]) |
+                   reinterpret_cast<uintptr_t>(in.b[z])) % align) == 0;
   // in_scale and tap are powers of two for these factors, so is their
   // product
   const float iscale = in_scale * tap;
@@ -542,10 +563,10 @@ hipError_t launch_decimate_t(const InT *ref, const InT *dist, int w, int h,
 #define FSSIM_POW2(F)                                                          \
   if (vec)                                                                     \
     decimate_pow2_kernel<InT, true, F><<<grid, blk, 0, stream>>>(              \
-        ref, dist, w, h, iscale, ow, xpb, dref, ddist);                        \
+        in, w, h, iscale, ow, oh, xpb, dref, ddist);                           \
   else                                                                         \
     decimate_pow2_kernel<InT, false, F><<<grid, blk, 0, stream>>>(             \
-        ref, dist, w, h, iscale, ow, xpb, dref, ddist)
+        in, w, h, iscale, ow, oh, xpb, dref, ddist)
   if (f == 2) {
     FSSIM_POW2(2);
   } else if (f == 4) {
@@ -555,69 +576,63 @@ hipError_t launch_decimate_t(const InT *ref, const InT *dist, int w, int h,
   } else if (f == 16) {
     FSSIM_POW2(16);
   } else if (vec) {
-    decimate_kernel<InT, true><<<grid, dim3(kDecThreads), 0, stream>>>(
-        ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
+    decimate_kernel<InT, true><<<grid, blk, 0, stream>>>(
+        in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist);
   } else {
-    decimate_kernel<InT, false><<<grid, dim3(kDecThreads), 0, stream>>>(
-        ref, dist, w, h, f, tap, in_scale, ow, xpb, dref, ddist);
+    decimate_kernel<InT, false><<<grid, blk, 0, stream>>>(
+        in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist);
   }
 #undef FSSIM_POW2
   return hipGetLastError();
 }
 
 template <typename InT>
-hipError_t launch_ssim_t(const InT *x, const InT *y, int w, int h,
+hipError_t launch_ssim_t(const FramePair &in, int n, int w, int h,
                          float in_scale, const SsimArgs &sa, float *map,
                          hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((w + kTileW - 1) / kTileW),
-                  static_cast<unsigned>((h + kTileH - 1) / kTileH));
-  ssim_kernel<InT><<<grid, dim3(256), 0, stream>>>(x, y, w, h, in_scale, sa,
+                  static_cast<unsigned>((h + kTileH - 1) / kTileH),
+                  static_cast<unsigned>(n));
+  ssim_kernel<InT><<<grid, dim3(256), 0, stream>>>(in, w, h, in_scale, sa,
                                                    map, map_pitch(h));
   return hipGetLastError();
 }
 
 } // namespace
 
-hipError_t launch_decimate(int bpc, const void *ref, const void *dist, int w,
-                           int h, int f, float tap, float in_scale, int ow,
-                           int oh, float *dref, float *ddist,
-                           hipStream_t stream) {
-  if (f < 2 || outputs_per_block(f) < 1 || ow < 1 || oh < 1)
+hipError_t launch_decimate(int bpc, const FramePair &in, int n, int w, int h,
+                           int f, float tap, float in_scale, int ow, int oh,
+                           float *dref, float *ddist, hipStream_t stream) {
+  if (f < 2 || outputs_per_block(f) < 1 || ow < 1 || oh < 1 || n < 1 ||
+      n > kMaxBatch)
     return hipErrorInvalidValue;
   if (bpc == 8)
-    return launch_decimate_t(static_cast<const uint8_t *>(ref),
-                             static_cast<const uint8_t *>(dist), w, h, f, tap,
-                             in_scale, ow, oh, dref, ddist, stream);
-  return launch_decimate_t(static_cast<const uint16_t *>(ref),
-                           static_cast<const uint16_t *>(dist), w, h, f, tap,
-                           in_scale, ow, oh, dref, ddist, stream);
+    return launch_decimate_t<uint8_t>(in, n, w, h, f, tap, in_scale, ow, oh,
+                                      dref, ddist, stream);
+  return launch_decimate_t<uint16_t>(in, n, w, h, f, tap, in_scale, ow, oh,
+                                     dref, ddist, stream);
 }
 
-hipError_t launch_ssim(int bpc, const void *x, const void *y, int w, int h,
+hipError_t launch_ssim(int bpc, const FramePair &in, int n, int w, int h,
                        float in_scale, const SsimArgs &sa, float *map,
                        hipStream_t stream) {
-  if (w < 1 || h < 1)
+  if (w < 1 || h < 1 || n < 1 || n > kMaxBatch)
     return hipErrorInvalidValue;
   if (bpc == 0)
-    return launch_ssim_t(static_cast<const float *>(x),
-                         static_cast<const float *>(y), w, h, 1.0f, sa, map,
-                         stream);
+    return launch_ssim_t<float>(in, n, w, h, 1.0f, sa, map, stream);
   if (bpc == 8)
-    return launch_ssim_t(static_cast<const uint8_t *>(x),
-                         static_cast<const uint8_t *>(y), w, h, in_scale, sa,
-                         map, stream);
-  return launch_ssim_t(static_cast<const uint16_t *>(x),
-                       static_cast<const uint16_t *>(y), w, h, in_scale, sa,
-                       map, stream);
+    return launch_ssim_t<uint8_t>(in, n, w, h, in_scale, sa, map, stream);
+  return launch_ssim_t<uint16_t>(in, n, w, h, in_scale, sa, map, stream);
 }
 
-hipError_t launch_ssim_rowsum(const float *map, int w, int h, double *rows,
-                              hipStream_t stream) {
-  if (w < 1 || h < 1)
+hipError_t launch_ssim_rowsum(const float *map, int n, int w, int h,
+                              double *rows, hipStream_t stream) {
+  if (w < 1 || h < 1 || n < 1 || n > kMaxBatch)
     return hipErrorInvalidValue;
   const int pitch = map_pitch(h);
-  rowsum_kernel<<<dim3(static_cast<unsigned>(pitch / 64)), dim3(256), 0,
-                  stream>>>(map, w, h, pitch, rows);
+  rowsum_kernel<<<dim3(static_cast<unsigned>(pitch / 64),
+                       static_cast<unsigned>(n)),
+                  dim3(256), 0, stream>>>(map, w, h, pitch, rows);
   return hipGetLastError();
 }
 
