@@ -73,13 +73,16 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
 
 
 def kernel_source_hash():
+    """SHA-256 of what the VIF kernels' machine code depends on: their
+    sources and the compiler flags of the build."""
+    from vif_image_fidelity_amd import build
     h = hashlib.sha256()
     for rel in ("vif_image_fidelity_amd/csrc/vif_kernels.hip",
                 "vif_image_fidelity_amd/csrc/vif_device_math.h",
-                "vif_image_fidelity_amd/csrc/vif_internal.h",
-                "vif_image_fidelity_amd/build.py"):
+                "vif_image_fidelity_amd/csrc/vif_internal.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()
 
 
