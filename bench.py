@@ -2,21 +2,23 @@
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step scores one 3840x2160 8-bit luma frame pair (the whole path: four
-scales of filtering, statistic, decimation and ordered row sums, one
-read-back and the host sums).  The 20 synthetic 1/f-noise frame pairs are
-resident in HBM before the timed region; steps cycle through them and go
-through the context's asynchronous queue (submit / collect, up to three
-frames in flight), so consecutive frames overlap their read-back and host
-work with the next frame's kernels.  Prints one JSON line.
+One step scores one batch of --batch (default 4) 3840x2160 8-bit luma frame
+pairs: the whole path (four scales of filtering, statistic, decimation and
+ordered row sums, the read-back and the host sums) with each kernel launched
+once for the batch (vif_submit_batch).  The 20 synthetic 1/f-noise frame
+pairs are resident in HBM before the timed region; steps cycle through them
+and go through the context's asynchronous queue (up to three batches in
+flight), so consecutive batches overlap their read-back and host work with
+the next batch's kernels.  `value` is frames/s.  Prints one JSON line.
 
 The line carries, besides the contract fields:
-  roofline      the dominant kernel (the scale-0 filter/statistic kernel):
-                algorithmic fp32 operations per launch / its average duration,
-                timed with HIP events on the context's stream during the timed
-                region, against the VALU peak; `traffic` is the kernel's HBM
-                bytes per launch from committed rocprofv3 counters when the
-                kernel source has not changed since they were taken, else null.
+  roofline      the dominant kernel (the scale-0 filter/statistic kernel, one
+                launch per batch): algorithmic fp32 operations per launch /
+                its average duration, timed with HIP events on the slot's
+                stream during the timed region, against the VALU peak;
+                `traffic` is the kernel's HBM bytes per launch from committed
+                rocprofv3 counters taken at the same batch size, when the
+                kernel source and flags have not changed since, else null.
   cpu_baseline  the CPU oracle on this host, one core, on a bounded sample of
                 the same workload.
   extra         1920x1080 and 576x324 frames/s, the rates with batched
@@ -86,14 +88,16 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def load_traffic():
-    """Counter-derived HBM bytes per launch of the scale-0 kernel, if taken
-    on the current kernel source."""
+def load_traffic(batch):
+    """Counter-derived HBM bytes per launch of the scale-0 kernel (a launch
+    of `batch` frames) and per frame of the whole path, if taken on the
+    current kernel source at that batch size."""
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None, None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if (rec.get("kernel_source_sha256") != kernel_source_hash() or
+            rec.get("batch") != batch):
         return None, None
     return rec.get("scale0_bytes_per_launch"), rec.get("frame_bytes")
 
@@ -392,14 +396,15 @@ def cpu_baseline(frames, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=150,
+                    help="timed steps; a step is one batch of --batch frames")
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--frames", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-1080p", type=int, default=500)
-    ap.add_argument("--batch", type=int, default=1,
-                    help="frames per submission in the frames and fssim "
-                    "modes")
+    ap.add_argument("--batch", type=int, default=4,
+                    help="frames per step (one submission, each kernel "
+                    "launched once for them); the fssim mode defaults to 1")
     ap.add_argument("--mode", choices=["full", "frames", "copy", "fssim"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
@@ -428,28 +433,41 @@ def main():
           file=sys.stderr, flush=True)
     frames4k = synth.pink_4k_8bit(frames=args.frames)
     w, h, bpc = 3840, 2160, 8
+    batch = args.batch
+    if not 1 <= batch <= V.MAX_BATCH:
+        print("--batch must be 1..%d" % V.MAX_BATCH, file=sys.stderr)
+        sys.exit(2)
     if args.mode == "fssim":
-        dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps,
-                                 args.warmup, batch=args.batch)
+        fb = batch if "--batch" in sys.argv else 1
+        dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps * fb,
+                                 args.warmup * fb, batch=fb)
         print("4K float SSIM (factor %d, %d per submission): %.1f frames/s"
-              % (geom[0], args.batch, args.steps / dt), file=sys.stderr,
+              % (geom[0], fb, args.steps * fb / dt), file=sys.stderr,
               flush=True)
         return
 
-    dt, kt = time_frames(V, frames4k, w, h, bpc, args.steps, args.warmup,
-                         prof_kinds=["scale0"],
-                         batch=args.batch if args.mode == "frames" else 1)
-    fps = args.steps / dt
+    nframes = args.steps * batch
+    dt, kt = time_frames(V, frames4k, w, h, bpc, nframes,
+                         args.warmup * batch, prof_kinds=["scale0"],
+                         batch=batch)
+    fps = nframes / dt
     ms_step = 1000.0 * dt / args.steps
     s0_ms, s0_n = kt["scale0"]
     s0_avg_ms = s0_ms / max(s0_n, 1)
-    print("4K: %.1f frames/s, %.3f ms/step; scale-0 kernel %.1f us avg"
-          % (fps, ms_step, 1000 * s0_avg_ms), file=sys.stderr, flush=True)
+    print("4K: %.1f frames/s, %.3f ms/step of %d frames; scale-0 kernel "
+          "%.1f us per launch" % (fps, ms_step, batch, 1000 * s0_avg_ms),
+          file=sys.stderr, flush=True)
     if args.mode == "frames":
         return
 
-    host_submit_us = kt["_host_submit_us"]
-    host_collect_us = kt["_host_collect_us"]
+    # one frame per submission (the pages' per-frame call), same frames
+    dt1, kt1 = time_frames(V, frames4k, w, h, bpc, 500, 20,
+                           prof_kinds=["scale0"])
+    fps_one = 500 / dt1
+    s0_one_ms = kt1["scale0"][0] / max(kt1["scale0"][1], 1)
+
+    host_submit_us = kt1["_host_submit_us"]
+    host_collect_us = kt1["_host_collect_us"]
     iso_s0_us = isolated_scale0_us(V, frames4k, w, h, bpc)
 
     # per-kernel split (all kinds timed; separate run, not the headline)
@@ -472,7 +490,6 @@ def main():
     # batched submissions: each kernel launched once for several frames
     batched = {}
     for key, fr, bw, bh, bb, nb, steps in (
-            ("4k_8bit_batch4", frames4k, w, h, bpc, 4, 1000),
             ("1080p_10bit_batch8", f1080, 1920, 1080, 10, 8, 3000),
             ("576x324_8bit_batch16", fsmall, 576, 324, 8, 16, 8000)):
         dtb, _ = time_frames(V, fr, bw, bh, bb, steps, 4 * nb, batch=nb)
@@ -485,16 +502,19 @@ def main():
                                   0 if args.no_cpu_baseline else 5.0),
              "1080p_10bit": fssim_leg(V, f1080, 1920, 1080, 10, 2000, 0)}
 
-    ops = OPS_PER_PIXEL_SCALE0 * w * h
-    achieved = ops / (s0_avg_ms / 1000.0) / 1e12
+    ops = OPS_PER_PIXEL_SCALE0 * w * h  # per frame
+    achieved = batch * ops / (s0_avg_ms / 1000.0) / 1e12
     peak = VALU_PEAK_OPS / 1e12
-    traffic, frame_bytes = load_traffic()
+    traffic, frame_bytes = load_traffic(batch)
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
                 "peak": round(peak, 2), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
     pops = path_ops(w, h)
-    extra = {"fps_1080p_10bit": round(fps1080, 1),
+    extra = {"fps_4k_one_frame_per_submission": round(fps_one, 1),
+             "scale0_frac_one_frame_per_submission": round(
+                 ops / (s0_one_ms / 1000.0) / VALU_PEAK_OPS, 4),
+             "fps_1080p_10bit": round(fps1080, 1),
              "fps_576x324_8bit": round(fps_small, 1),
              "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
              "fps_batched": batched,
@@ -502,7 +522,8 @@ def main():
                  "submit": round(kts["_host_submit_us"], 2),
                  "collect": round(kts["_host_collect_us"], 2)},
              "kernel_avg_us_4k": split,
-             "scale0_kernel_avg_us": round(1000 * s0_avg_ms, 2),
+             "scale0_launch_avg_us": round(1000 * s0_avg_ms, 2),
+             "scale0_frames_per_launch": batch,
              "scale0_kernel_isolated_us": round(iso_s0_us, 2),
              "scale0_isolated_frac_of_valu_peak": round(
                  ops / (iso_s0_us * 1e-6) / VALU_PEAK_OPS, 4),
@@ -542,8 +563,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "pink_4k_8bit: 3840x2160 8-bit luma pairs, "
                                "1/f-noise ref, 2x down/up-scaled dist, %d "
-                               "frames resident in HBM" % args.frames,
-                   "w": w, "h": h, "bpc": bpc, "scales": 4},
+                               "frames resident in HBM, %d frames per step "
+                               "(one batched submission)" % (args.frames,
+                                                              batch),
+                   "w": w, "h": h, "bpc": bpc, "scales": 4,
+                   "frames_per_step": batch},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
