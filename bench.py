@@ -379,6 +379,34 @@ def copy_calibration(launches):
           file=sys.stderr, flush=True)
 
 
+def _oracle_frames(args):
+    """Worker of the all-cores oracle figure: generates two frames of the
+    1/f workload, then scores them in turn for budget_s seconds; returns
+    (frames scored, seconds)."""
+    first, step, budget_s = args
+    import oracle
+    from vif_image_fidelity_amd import synth
+    frames = [synth.pink_4k_frame((first + j * step) % 20) for j in range(2)]
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        r, d, b = frames[n % 2]
+        oracle.score(r, d, b)
+        n += 1
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(budget_s=12.0, procs=None):
+    """The oracle on several host cores at once: one process per core (at
+    most 16), each scoring whole frames of the same workload.  Returns
+    (frames/s summed over the processes, processes)."""
+    import multiprocessing as mp
+    procs = procs or min(16, os.cpu_count() or 1)
+    with mp.get_context("spawn").Pool(procs) as pool:
+        res = pool.map(_oracle_frames,
+                       [(k, procs, budget_s) for k in range(procs)])
+    return sum(n / t for n, t in res), procs
+
+
 def cpu_baseline(frames, budget_s=12.0):
     import oracle
     n = 0
@@ -417,6 +445,17 @@ def main():
               "a single MI355X (frames shard across GPUs with no exchange; "
               "see the design notes).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    cpu_all = None
+    if args.mode == "full" and not args.no_cpu_baseline:
+        # before this process touches the GPU: the oracle on every core at
+        # once, one process per core
+        afps, aprocs = cpu_baseline_all_cores()
+        cpu_all = {"value": round(afps, 3), "unit": "frames/s",
+                   "processes": aprocs, "host_cpus": os.cpu_count(),
+                   "kind": "oracle"}
+        print("oracle on %d processes: %.2f frames/s" % (aprocs, afps),
+              file=sys.stderr, flush=True)
 
     import torch
     if not torch.cuda.is_available():
@@ -547,6 +586,7 @@ def main():
                "kind": "oracle",
                "sample": "%d of the 3840x2160 8-bit frame pairs, single "
                          "thread, %.1f s" % (cn, cdt)}
+        extra["cpu_oracle_all_cores"] = cpu_all
 
     line = {
         "metric": METRIC,

@@ -368,11 +368,12 @@ def test_batch_matches_oracle(V, orc, name, n):
     ctx.close()
 
 
-def test_batch_4k_two_frames(V, orc):
-    """The 3840x2160 workload's first two frames in one submission."""
+def test_batch_4k_bench_configuration(V, orc):
+    """The benchmark's launch configuration: four 3840x2160 frames of the 1/f
+    workload in one submission (every kernel launched once for them)."""
     from vif_image_fidelity_amd import synth
-    frames = [synth.pink_4k_frame(i) for i in range(2)]
-    ctx = V.Vif(3840, 2160, 8, max_batch=2)
+    frames = [synth.pink_4k_frame(i) for i in range(4)]
+    ctx = V.Vif(3840, 2160, 8, max_batch=4)
     dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
     ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
     for i, (r, d, b) in enumerate(frames):
