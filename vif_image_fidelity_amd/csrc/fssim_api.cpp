@@ -23,9 +23,13 @@
 #include "../../include/fssim.h"
 #include "../../include/vif.h"
 #include "fssim_internal.h"
+#include "hip_util.h"
 #include "vif_status.h"
 
 namespace {
+
+using vifk::DeviceScope;
+using vifk::destroy_event;
 
 constexpr int kDepth = FSSIM_QUEUE_DEPTH;
 constexpr int kKinds = 3; // decimation, SSIM stage, row sums
@@ -70,13 +74,6 @@ struct fssim_ctx {
 
 namespace {
 
-void destroy_event(hipEvent_t &e) {
-  if (e) {
-    (void)hipEventDestroy(e);
-    e = nullptr;
-  }
-}
-
 void free_all(fssim_ctx *c) {
   for (FSlot &sl : c->slots) {
     if (sl.dref)
@@ -98,26 +95,6 @@ void free_all(fssim_ctx *c) {
   }
   std::free(c->last_rows);
 }
-
-class DeviceScope {
-public:
-  explicit DeviceScope(int dev) {
-    if (hipGetDevice(&prev_) != hipSuccess)
-      prev_ = -1;
-    if (prev_ != dev)
-      err_ = hipSetDevice(dev);
-  }
-  ~DeviceScope() {
-    int cur = -1;
-    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_)
-      (void)hipSetDevice(prev_);
-  }
-  hipError_t error() const { return err_; }
-
-private:
-  int prev_ = -1;
-  hipError_t err_ = hipSuccess;
-};
 
 bool bad_frame_ptrs(const fssim_ctx *ctx, const void *ref, const void *dist) {
   if (ref == nullptr || dist == nullptr)

@@ -37,11 +37,15 @@
 
 #include "../../include/vif.h"
 #include "vif_internal.h"
+#include "hip_util.h"
 #include "vif_status.h"
 
 using vifk::kScales;
 
 namespace {
+
+using vifk::DeviceScope;
+using vifk::destroy_event;
 
 constexpr int kDepth = VIF_QUEUE_DEPTH;
 
@@ -119,37 +123,9 @@ int status_from_hip(hipError_t e) {
 
 namespace {
 
-// Makes the context's device current for the scope of one call.
-class DeviceScope {
-public:
-  explicit DeviceScope(int dev) {
-    if (hipGetDevice(&prev_) != hipSuccess)
-      prev_ = -1;
-    if (prev_ != dev)
-      err_ = hipSetDevice(dev);
-  }
-  ~DeviceScope() {
-    int cur = -1;
-    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_)
-      (void)hipSetDevice(prev_);
-  }
-  hipError_t error() const { return err_; }
-
-private:
-  int prev_ = -1;
-  hipError_t err_ = hipSuccess;
-};
-
 bool fault_injected_alloc() {
   const char *v = std::getenv("VIF_FAULT_INJECT");
   return v != nullptr && std::strcmp(v, "alloc") == 0;
-}
-
-void destroy_event(hipEvent_t &e) {
-  if (e) {
-    (void)hipEventDestroy(e);
-    e = nullptr;
-  }
 }
 
 void free_all(vif_ctx *c) {
