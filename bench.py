@@ -48,15 +48,30 @@ sys.path.insert(0, ROOT)
 METRIC = ("VIF frames/sec at 1080p and 4K on 1 MI355X; achieved HBM GB/s vs "
           "peak")
 
-# Plain fp32 VALU operations per launch of the scale-0 kernel, counted from
-# the definition (no fused multiply-add, no packed math): per scale-0 pixel
-# 3 products + 5 quantities x 2 passes x (17 mul + 16 add) + 8 for the
-# variances = 341, plus the next scale's 9-tap low-pass of both planes at
-# even rows (two columns per decimated pixel) and even columns: 2 planes x 3
-# x (9 mul + 8 add) = 102 per scale-1 pixel = 25.5 per scale-0 pixel.  The
-# statistic's own operations are left out (they depend on the content), so
-# the figure is a lower bound of the work done.
-OPS_PER_PIXEL_SCALE0 = 341.0 + 102.0 / 4.0
+# Algorithmic operations of the scale-0 kernel per scale-0 pixel, counted
+# from the definition: every IEEE operation once (separate multiply and add,
+# no fused multiply-add, no packing; fp64 operations and conversions count
+# as one like fp32 ones).
+#   filter: 3 products + 5 quantities x 2 passes x (17 mul + 16 add) + 8 for
+#     the variances (3 mul, 3 sub, 2 clamps) = 341;
+#   the next scale's 9-tap low-pass of both planes at even rows (two columns
+#     per decimated pixel) and even columns: 2 planes x 3 x (9 mul + 8 add)
+#     = 102 per scale-1 pixel = 25.5 per scale-0 pixel;
+#   the statistic of a pixel in the high-variance branch = 78: fp64
+#     conversion and comparison of sigma1_sq (2); g = sigma12 / sigma1_sq,
+#     g * sigma12, sv_sq (3); the comparisons with eps and 0, the floor at
+#     eps and the gain limit (4) with their four selects (4); g * g and
+#     a = g*g * sigma1_sq (2); the numerator ratio: two conversions, the sum
+#     with nsq, the quotient, the sum with 1, the conversion to fp32 (6); the
+#     denominator ratio: quotient, sum, conversion (3); two log2
+#     polynomials of 27 each (exponent field, bias, mantissa bits, t = m - 1,
+#     9 Horner steps of multiply and add, the last product, the exponent's
+#     conversion and the final sum).
+# On the benchmark's frames every scale-0 pixel takes that branch
+# (tests/test_bench_workload.py), so the statistic counts for every pixel.
+FILTER_OPS_PER_PIXEL_SCALE0 = 341.0 + 102.0 / 4.0
+STAT_OPS_PER_PIXEL = 78.0
+OPS_PER_PIXEL_SCALE0 = FILTER_OPS_PER_PIXEL_SCALE0 + STAT_OPS_PER_PIXEL
 
 # VALU peak for plain (unfused, unpacked) fp32 operations.  MI355X's fp32
 # vector figure, 157.3 TFLOP/s, is 256 CUs x 4 SIMDs x 32 lanes x 2 flops (an
@@ -345,16 +360,18 @@ def isolated_scale0_us(V, frames, w, h, bpc, n=50):
 
 
 def path_ops(w, h):
-    """Plain fp32 operations the definition needs per frame, statistic
-    excluded: per scale the 3 products, 5 quantities x 2 passes x
-    (N mul + N-1 add) and 8 for the variances per pixel, the next scale's
-    low-pass (2 planes x 3 x (2N'-1) per decimated pixel) and 2 row-sum adds
-    per pixel."""
+    """Algorithmic operations the definition needs per frame: per scale the
+    3 products, 5 quantities x 2 passes x (N mul + N-1 add) and 8 for the
+    variances per pixel, the statistic (STAT_OPS_PER_PIXEL, every pixel
+    counted in the high-variance branch, which at least 99.9% of the
+    benchmark's pixels take at every scale), the next scale's low-pass
+    (2 planes x 3 x (2N'-1) per decimated pixel) and 2 row-sum adds per
+    pixel."""
     widths = (17, 9, 5, 3)
     ops, ws, hs = 0.0, w, h
     for s in range(4):
         n = widths[s]
-        ops += (3 + 10 * (2 * n - 1) + 8 + 2) * ws * hs
+        ops += (3 + 10 * (2 * n - 1) + 8 + STAT_OPS_PER_PIXEL + 2) * ws * hs
         if s < 3:
             ops += 6 * (2 * widths[s + 1] - 1) * (ws // 2) * (hs // 2)
         ws, hs = ws // 2, hs // 2
@@ -542,6 +559,7 @@ def main():
              "1080p_10bit": fssim_leg(V, f1080, 1920, 1080, 10, 2000, 0)}
 
     ops = OPS_PER_PIXEL_SCALE0 * w * h  # per frame
+    fops = FILTER_OPS_PER_PIXEL_SCALE0 * w * h
     achieved = batch * ops / (s0_avg_ms / 1000.0) / 1e12
     peak = VALU_PEAK_OPS / 1e12
     traffic, frame_bytes = load_traffic(batch)
@@ -550,7 +568,12 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
     pops = path_ops(w, h)
-    extra = {"fps_4k_one_frame_per_submission": round(fps_one, 1),
+    extra = {"scale0_ops_per_pixel": {
+                 "filter_and_decimation": FILTER_OPS_PER_PIXEL_SCALE0,
+                 "statistic": STAT_OPS_PER_PIXEL},
+             "scale0_frac_filter_ops_only": round(
+                 batch * fops / (s0_avg_ms / 1000.0) / VALU_PEAK_OPS, 4),
+             "fps_4k_one_frame_per_submission": round(fps_one, 1),
              "scale0_frac_one_frame_per_submission": round(
                  ops / (s0_one_ms / 1000.0) / VALU_PEAK_OPS, 4),
              "fps_1080p_10bit": round(fps1080, 1),
