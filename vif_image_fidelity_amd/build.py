@@ -41,8 +41,34 @@ FLAGS = [
 ]
 
 
+EXAMPLE_SRC = os.path.join(CSRC, "score_raw.c")
+EXAMPLE = os.path.join(HERE, "score_raw")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_example(verbose=False):
+    """Compile score_raw.c, a plain C caller of the library's C ABI (gcc,
+    C11), against the freshly built library."""
+    tmp = EXAMPLE + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROCM, "include"), "-o", tmp, EXAMPLE_SRC,
+           "-L", HERE, "-lvif_amd", "-L", os.path.join(ROCM, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("gcc failed building %s" % EXAMPLE)
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
+
+
 def build(verbose=False):
-    """Compile every source into vif_image_fidelity_amd/libvif_amd.so."""
+    """Compile every source into vif_image_fidelity_amd/libvif_amd.so, then
+    the C example that calls it."""
     tmp = LIB + ".tmp%d" % os.getpid()
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = (["hipcc"] + FLAGS + ["-shared", "-o", tmp] + srcs +
@@ -54,6 +80,7 @@ def build(verbose=False):
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building %s" % LIB)
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
 
 
