@@ -182,6 +182,25 @@ def test_package_import_needs_no_gpu():
     assert len(V.DEBUG_NAMES) == 15 and V.DEBUG_NAMES[4] == "vif"
 
 
+def test_one_hip_runtime_in_the_process():
+    """Loading the library before anything imports torch still leaves one
+    HIP runtime mapped: torch bundles its own copy under the same soname,
+    and two copies in one process make torch's device pointers and streams
+    invalid in the library's calls."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from vif_image_fidelity_amd import _lib\n"
+            "_lib.load()\n"
+            "import torch\n"
+            "p = {l.split()[-1] for l in open('/proc/self/maps')"
+            " if 'libamdhip64' in l}\n"
+            "print(len(p), sorted(p))\n" % ROOT)
+    ensure_built()
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("1 "), r.stdout
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     from vif_image_fidelity_amd import _lib
     monkeypatch.setattr(_lib, "_lib", None)

@@ -60,6 +60,12 @@ def load():
         raise RuntimeError(
             "libvif_amd.so is not built (%s); run "
             "`python -m vif_image_fidelity_amd.build` first" % LIB_PATH)
+    # PyTorch ships its own copy of the HIP runtime under the soname the
+    # library links against.  Importing torch first makes the dynamic loader
+    # bind the library to that copy: loaded the other way round, the process
+    # holds two runtimes, and device pointers and streams of one are invalid
+    # in the other.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, ip, fp = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)
     dp = ctypes.POINTER(ctypes.c_double)
