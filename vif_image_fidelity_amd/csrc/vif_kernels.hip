@@ -34,6 +34,10 @@ namespace vifk {
 
 constexpr int kThreads = 256;
 
+// Four floats as the compiler's native vector type, for the non-temporal
+// load and store builtins.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Planes hold at most 2^27 samples, so a 32-bit offset addresses them.
 // The input tile stays in LDS in the plane's own sample type (one byte per
 // 8-bit sample); to_float normalises a sample where the vertical pass reads
@@ -340,16 +344,20 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
 
   // 8. terms to the strip's term buffer: groups of 4 columns, each group
   //    holding the 32 sequences' 4 values ([g][seq][4] floats); this tile's
-  //    28 groups are one contiguous 14 KiB block.
+  //    28 groups are one contiguous 14 KiB block.  The stores are
+  //    non-temporal: the row sums read the terms only after the frame's
+  //    last scale, so they should not displace the input tiles in L2.
   {
-    float4 *dst = reinterpret_cast<float4 *>(
+    f32x4 *dst = reinterpret_cast<f32x4 *>(
         terms + (static_cast<size_t>(strip) * term_groups(w) + x0 / 4) *
                     (kSeq * 4));
     const int groups = min(kTileW, w - x0 + 3) / 4;
     for (int i = tid; i < groups * kSeq; i += kThreads) {
       const int g = i / kSeq;
       const int q = i - g * kSeq;
-      dst[i] = *reinterpret_cast<const float4 *>(sT + q * kTermPitch + 4 * g);
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const f32x4 *>(sT + q * kTermPitch + 4 * g),
+          dst + i);
     }
   }
 }
@@ -362,20 +370,21 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
 // Decision: one fp32 sum per row, in order, no group or atomic reduction).
 // Each float4 load brings four consecutive columns of a lane's sequence;
 // two register batches keep one batch of loads in flight while the other is
-// added.  No LDS, so these waves fit beside a running scale kernel.
+// added.  No LDS, so these waves fit beside a running scale kernel.  The
+// loads are non-temporal: each term is read once.
 constexpr int kRowBatch = 12; // float4 loads per batch and lane
 
-__device__ __forceinline__ void load_batch(float4 (&v)[kRowBatch],
-                                           const float4 *__restrict__ src,
+__device__ __forceinline__ void load_batch(f32x4 (&v)[kRowBatch],
+                                           const f32x4 *__restrict__ src,
                                            int g0, int groups) {
 #pragma unroll
   for (int k = 0; k < kRowBatch; ++k) {
     const int g = min(g0 + k, groups - 1); // in-bounds; extras are not added
-    v[k] = src[static_cast<size_t>(g) * kSeq];
+    v[k] = __builtin_nontemporal_load(src + static_cast<size_t>(g) * kSeq);
   }
 }
 
-__device__ __forceinline__ float add_batch(float acc, const float4 (&v)[kRowBatch],
+__device__ __forceinline__ float add_batch(float acc, const f32x4 (&v)[kRowBatch],
                                            int x0, int w) {
   if (x0 + 4 * kRowBatch <= w) {
 #pragma unroll
@@ -415,12 +424,12 @@ __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
   const int seq = lane & 31;
   const int w = a.w[s];
   const int groups = term_groups(w);
-  const float4 *src = reinterpret_cast<const float4 *>(
-                          a.terms[s] + z * a.terms_stride[s] +
-                          static_cast<size_t>(strip) * groups * (kSeq * 4)) +
-                      seq;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(
+                         a.terms[s] + z * a.terms_stride[s] +
+                         static_cast<size_t>(strip) * groups * (kSeq * 4)) +
+                     seq;
   float acc = 0.0f;
-  float4 va[kRowBatch], vb[kRowBatch];
+  f32x4 va[kRowBatch], vb[kRowBatch];
   load_batch(va, src, 0, groups);
   for (int g = 0; g < groups; g += 2 * kRowBatch) {
     load_batch(vb, src, g + kRowBatch, groups);
