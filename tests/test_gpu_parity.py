@@ -382,6 +382,75 @@ def test_batch_4k_bench_configuration(V, orc):
     ctx.close()
 
 
+def test_4k_ordered_stream_paths(V, orc):
+    """At 3840x2160 consecutive scale-0 kernels run on the context's own
+    scale-0 stream and the other kernels wait for them across streams.
+    Every way in is checked on that path: a full queue of device frames with
+    every kernel timed, a queue of pinned host frames (copies on the slot's
+    stream, scale 0 on the other), and frames written on the caller's stream
+    just before the submit, behind other work on that stream."""
+    import torch
+    from vif_image_fidelity_amd import synth
+    frames = [synth.pink_4k_frame(i) for i in range(2)]
+    want = [orc.score(r, d, b)[0] for r, d, b in frames]
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.Vif(3840, 2160, 8)
+    print("ordered paths: device queue, profiling on", flush=True)
+    ctx.set_profiling(True)
+    order = [0, 1, 0, 1, 1, 0]
+    outs = []
+    for i in order:
+        if ctx.pending() == V.QUEUE_DEPTH:
+            outs.append(ctx.collect())
+        ctx.submit(*dev[i])
+    while ctx.pending():
+        outs.append(ctx.collect())
+    for i, got in zip(order, outs):
+        assert got.tobytes() == want[i].tobytes(), i
+    kt = ctx.kernel_times()
+    for kind in V.KERNEL_KINDS:
+        ms, n = kt[kind]
+        assert n == len(order) and ms > 0, kind
+    ctx.set_profiling(False)
+    print("ordered paths: pinned host queue", flush=True)
+    pinned = []
+    for r, d, _ in frames:
+        pr = torch.empty(r.shape, dtype=torch.uint8, pin_memory=True)
+        pd = torch.empty(d.shape, dtype=torch.uint8, pin_memory=True)
+        pr.numpy()[:] = r
+        pd.numpy()[:] = d
+        pinned.append((pr, pd))
+    outs = []
+    for i in order:
+        if ctx.pending() == V.QUEUE_DEPTH:
+            outs.append(ctx.collect())
+        ctx.submit_host(*pinned[i])
+    while ctx.pending():
+        outs.append(ctx.collect())
+    for i, got in zip(order, outs):
+        assert got.tobytes() == want[i].tobytes(), i
+    print("ordered paths: frames written on the caller's stream", flush=True)
+    s = torch.cuda.Stream()
+    a = torch.ones(2048, 2048, device="cuda:0")
+    for k in range(2):
+        src = dev[k]
+        dr = dev[1 - k][0].clone()
+        dd = dev[1 - k][1].clone()
+        torch.cuda.synchronize()
+        ctx.set_stream(s)
+        with torch.cuda.stream(s):
+            for _ in range(8):
+                a = torch.mm(a, a) * (1.0 / 2048)
+            dr.copy_(src[0])
+            dd.copy_(src[1])
+        ctx.submit(dr, dd)
+        got = ctx.collect()
+        ctx.set_stream(None)
+        assert got.tobytes() == want[k].tobytes(), k
+    torch.cuda.synchronize()
+    ctx.close()
+
+
 def test_batch_tiny_frames(V, orc):
     """Every tiny geometry in batches of two and of one."""
     from vif_image_fidelity_amd import synth
