@@ -458,9 +458,9 @@ def main():
                     "float SSIM loop (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the feature on "
-              "a single MI355X (frames shard across GPUs with no exchange; "
-              "see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library scores frames on "
+              "a single MI355X (frames shard across GPUs with no exchange, "
+              "one context per GPU).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     cpu_all = None
