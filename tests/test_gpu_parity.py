@@ -180,6 +180,48 @@ def test_wide_samples_parity_and_invariance(V, orc, bpc):
     assert a.tobytes() == b.tobytes()
 
 
+def _offset_view(t, k):
+    """The frame t copied into a larger buffer k samples from its start."""
+    import torch
+    flat = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+    flat[k:k + t.numel()] = t.reshape(-1)
+    return flat[k:k + t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("bpc", [8, 16])
+def test_input_load_paths(V, orc, bpc):
+    """Scale 0 loads interior tiles 8 samples at a time when the width is a
+    multiple of 8 and the planes are aligned to 8 samples, and one sample at
+    a time otherwise (edge tiles, other widths, planes at any other offset).
+    Every combination scores bit for bit as the oracle: width 360 (tiles 1
+    and 2 interior) with aligned planes and with planes one sample off, width
+    364, and a batch whose second frame is off."""
+    g = np.random.Generator(np.random.PCG64(360 + bpc))
+    top = (1 << bpc) - 1
+    dt = np.uint8 if bpc == 8 else np.uint16
+    for w in (360, 364):
+        h = 100
+        ref = g.integers(0, top + 1, size=(h, w)).astype(dt)
+        dist = np.clip(ref.astype(np.int64) +
+                       g.integers(-(top // 10), top // 10 + 1, size=(h, w)),
+                       0, top).astype(dt)
+        exp = orc.score(ref, dist, bpc)[0]
+        ctx = V.Vif(w, h, bpc, max_batch=2)
+        dr, dd = to_device(ref), to_device(dist)
+        for k in (0, 1, 3):
+            print("load paths: bpc %d width %d offset %d" % (bpc, w, k),
+                  flush=True)
+            a = dr if k == 0 else _offset_view(dr, k)
+            b = dd if k == 0 else _offset_view(dd, k)
+            got = ctx.score(a, b)
+            assert got.tobytes() == exp.tobytes(), (w, k)
+        ro, do = _offset_view(dr, 1), _offset_view(dd, 1)
+        ctx.submit_batch([dr, ro], [dd, do])
+        assert ctx.collect().tobytes() == exp.tobytes()
+        assert ctx.collect().tobytes() == exp.tobytes()
+        ctx.close()
+
+
 def test_flat_and_identical_frames(V, orc):
     f = np.full((64, 80), 200, np.uint8)
     out = _compare(V, orc, f, f, 8, "flat")

@@ -31,6 +31,7 @@
 // scales in order in fp64.
 #include <hip/hip_runtime_api.h>
 
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -196,6 +197,16 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
     }
     io.terms = sl.terms[s];
     io.terms_stride = ctx->terms_elems[s];
+    if (s == 0) {
+      // 8 samples per load: rows start on 8-sample boundaries and the
+      // planes are aligned to 8 samples' bytes
+      const uintptr_t align = ctx->bpc == 8 ? 8 : 16;
+      bool vec = ctx->w % 8 == 0;
+      for (int z = 0; z < n; ++z)
+        vec = vec && reinterpret_cast<uintptr_t>(refs[z]) % align == 0 &&
+              reinterpret_cast<uintptr_t>(dists[z]) % align == 0;
+      io.vec_in = vec ? 1 : 0;
+    }
     const vifk::TapArgs &nt = ctx->taps[s + 1 < kScales ? s + 1 : s];
     const bool timed = (sl.prof_mask >> s) & 1;
     if (timed)

@@ -74,6 +74,10 @@ struct ScaleIO {
   float *terms;
   size_t next_stride;
   size_t terms_stride;
+  // scale 0: every in_ref/in_dist plane may be read 8 samples per load
+  // (width a multiple of 8, planes 8-byte aligned for 8-bit samples,
+  // 16-byte for 16-bit ones); 0 otherwise and at scales 1-3
+  int vec_in;
 };
 
 // Arguments of the row-sum kernel (all four scales in one launch): scale s

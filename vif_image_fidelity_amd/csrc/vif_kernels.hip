@@ -27,6 +27,8 @@
 // are the same value.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "vif_device_math.h"
 #include "vif_internal.h"
 
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   static_assert(CW <= 128, "one thread per vertical column in two halves");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
   static_assert(kTileH == 2 * VB, "two row blocks");
-  __shared__ float lds[kLds];
+  __shared__ __attribute__((aligned(16))) float lds[kLds];
   InT *sIn = reinterpret_cast<InT *>(lds);
 
   const int tid = threadIdx.x;
@@ -167,22 +169,62 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   const int strip = blockIdx.y;
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
-  // 1. input tile [IR][CW] for ref then dist.  Waves 0-1 load the even
-  //    rows, waves 2-3 the odd ones: the row (and its mirror) is uniform in a
-  //    wave, and all of a thread's loads are issued before the first use.
+  // 1. input tile [IR][CW] for ref then dist.  A tile whose columns all lie
+  //    inside the plane, in a plane that allows it (io.vec_in), loads 8
+  //    samples per thread and load: 16 threads per row, 16 rows per pass,
+  //    two passes per plane (x0 - R is a multiple of 8, so every load is
+  //    aligned).  Other tiles load one sample per thread and row, mirroring
+  //    each column: waves 0-1 the even rows, waves 2-3 the odd ones, so the
+  //    row (and its mirror) is uniform in a wave.  Either way all of a
+  //    thread's loads are issued before the first store.
   {
-    const int c = tid & 127;
-    const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
-    static_assert(IR % 2 == 0, "the two row phases cover the tile");
-    if (c < CW) {
-      const unsigned gx = static_cast<unsigned>(mirror_clamp(x0 - R + c, w));
+    bool vec = false;
+    if constexpr (sizeof(InT) < 4)
+      vec = io.vec_in != 0 && x0 - R >= 0 && x0 - R + CW <= w;
+    if (vec) {
+      if constexpr (sizeof(InT) < 4) {
+        constexpr int kSpl = 8;                 // samples per load
+        constexpr int kTpr = CW / kSpl;         // threads per row
+        constexpr int kRpp = kThreads / kTpr;   // rows per pass
+        using Vec = typename std::conditional<sizeof(InT) == 1, uint2,
+                                              uint4>::type;
+        static_assert(sizeof(Vec) == kSpl * sizeof(InT), "8 samples");
+        static_assert(CW % kSpl == 0 && IR % kRpp == 0, "whole passes");
+        const int q = tid % kTpr;
+        const int r0 = tid / kTpr;
+        Vec a[IR / kRpp], b[IR / kRpp];
 #pragma unroll
-      for (int it = 0; it < IR / 2; ++it) {
-        const int j = half + 2 * it;
-        const unsigned gy = static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
-        const unsigned off = gy * static_cast<unsigned>(w) + gx;
-        sIn[j * CW + c] = ref[off];
-        sIn[IR * CW + j * CW + c] = dist[off];
+        for (int it = 0; it < IR / kRpp; ++it) {
+          const int j = r0 + kRpp * it;
+          const unsigned gy =
+              static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
+          const unsigned base = gy * static_cast<unsigned>(w) + (x0 - R);
+          a[it] = reinterpret_cast<const Vec *>(ref + base)[q];
+          b[it] = reinterpret_cast<const Vec *>(dist + base)[q];
+        }
+#pragma unroll
+        for (int it = 0; it < IR / kRpp; ++it) {
+          const int j = r0 + kRpp * it;
+          *reinterpret_cast<Vec *>(sIn + j * CW + kSpl * q) = a[it];
+          *reinterpret_cast<Vec *>(sIn + IR * CW + j * CW + kSpl * q) = b[it];
+        }
+      }
+    } else {
+      const int c = tid & 127;
+      const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+      static_assert(IR % 2 == 0, "the two row phases cover the tile");
+      if (c < CW) {
+        const unsigned gx =
+            static_cast<unsigned>(mirror_clamp(x0 - R + c, w));
+#pragma unroll
+        for (int it = 0; it < IR / 2; ++it) {
+          const int j = half + 2 * it;
+          const unsigned gy =
+              static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
+          const unsigned off = gy * static_cast<unsigned>(w) + gx;
+          sIn[j * CW + c] = ref[off];
+          sIn[IR * CW + j * CW + c] = dist[off];
+        }
       }
     }
   }
