@@ -450,6 +450,9 @@ def main():
     ap.add_argument("--batch", type=int, default=4,
                     help="frames per step (one submission, each kernel "
                     "launched once for them); the fssim mode defaults to 1")
+    ap.add_argument("--workload", choices=["4k", "1080p10"], default="4k",
+                    help="frames mode only: the 3840x2160 8-bit frames, or "
+                    "the 1920x1080 10-bit checkerboard pairs")
     ap.add_argument("--mode", choices=["full", "frames", "copy", "fssim"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
@@ -485,14 +488,27 @@ def main():
     import vif_image_fidelity_amd as V
     from vif_image_fidelity_amd import synth
 
-    print("generating %d synthetic 3840x2160 frame pairs" % args.frames,
-          file=sys.stderr, flush=True)
-    frames4k = synth.pink_4k_8bit(frames=args.frames)
-    w, h, bpc = 3840, 2160, 8
     batch = args.batch
     if not 1 <= batch <= V.MAX_BATCH:
         print("--batch must be 1..%d" % V.MAX_BATCH, file=sys.stderr)
         sys.exit(2)
+    if args.mode == "frames" and args.workload == "1080p10":
+        frames = synth.checker_1080p_10bit()
+        nframes = args.steps * batch
+        dt, kt = time_frames(V, frames, 1920, 1080, 10, nframes,
+                             args.warmup * batch, prof_kinds=["scale0"],
+                             batch=batch)
+        s0_ms, s0_n = kt["scale0"]
+        print("1080p 10-bit: %.1f frames/s, %.3f ms/step of %d frames; "
+              "scale-0 kernel %.1f us per launch"
+              % (nframes / dt, 1000.0 * dt / args.steps, batch,
+                 1000.0 * s0_ms / max(s0_n, 1)), file=sys.stderr, flush=True)
+        return
+
+    print("generating %d synthetic 3840x2160 frame pairs" % args.frames,
+          file=sys.stderr, flush=True)
+    frames4k = synth.pink_4k_8bit(frames=args.frames)
+    w, h, bpc = 3840, 2160, 8
     if args.mode == "fssim":
         fb = batch if "--batch" in sys.argv else 1
         dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps * fb,
