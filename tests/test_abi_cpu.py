@@ -174,6 +174,32 @@ def test_fault_injection_alloc(lib):
     assert r.stdout.split() == ["False", "-2"]
 
 
+def test_binding_constants_match_headers():
+    """The Python binding's constants are the headers' #defines."""
+    import re
+    from vif_image_fidelity_amd import _lib
+    defs = {}
+    for fn in ("vif.h", "fssim.h"):
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        for m in re.finditer(r"#define\s+(\w+)\s+\(?(\d+)L?(?:\s*<<\s*(\d+))?\)?",
+                             text):
+            v = int(m.group(2))
+            if m.group(3):
+                v <<= int(m.group(3))
+            defs[m.group(1)] = v
+    pairs = {"VIF_QUEUE_DEPTH": _lib.QUEUE_DEPTH,
+             "VIF_MAX_BATCH": _lib.MAX_BATCH,
+             "VIF_MIN_SIDE": _lib.MIN_SIDE,
+             "VIF_MAX_PIXELS": _lib.MAX_PIXELS,
+             "FSSIM_TAPS": _lib.FSSIM_TAPS,
+             "FSSIM_QUEUE_DEPTH": _lib.FSSIM_QUEUE_DEPTH,
+             "FSSIM_MAX_BATCH": _lib.MAX_BATCH,
+             "FSSIM_MAX_PIXELS": _lib.FSSIM_MAX_PIXELS,
+             "FSSIM_MAX_FACTOR": _lib.FSSIM_MAX_FACTOR}
+    for name, value in pairs.items():
+        assert defs[name] == value, name
+
+
 def test_package_import_needs_no_gpu():
     import vif_image_fidelity_amd as V
     assert V.VIF_OK == 0

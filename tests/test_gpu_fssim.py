@@ -163,6 +163,25 @@ def test_misaligned_pointers(V, orc, w, h, bpc):
     _check(V, orc, ctx, got, ref, dist, bpc, "misaligned_%dx%d" % (w, h))
 
 
+@pytest.mark.parametrize("w,h", [(16, 1048704), (384, 349524)])
+def test_tall_planes(V, orc, w, h):
+    """More tile rows than a grid's y dimension allows (65 536 blocks): at
+    16 x 1048704 (factor 1) the SSIM stage has 131 088 rows of tiles; at
+    384 x 349524 (factor 2, close to the largest accepted frame) the
+    decimation has 174 762 output rows.  Both lay their blocks out in one
+    grid dimension."""
+    g = np.random.Generator(np.random.PCG64(w + h))
+    ref = g.integers(0, 256, size=(h, w)).astype(np.uint8)
+    dist = np.clip(ref.astype(np.int16) +
+                   g.integers(-20, 21, size=(h, w), dtype=np.int16),
+                   0, 255).astype(np.uint8)
+    print("fssim parity case tall %dx%d" % (w, h), flush=True)
+    ctx = V.FloatSsim(w, h, 8)
+    got = ctx.score(to_device(ref), to_device(dist))
+    _check(V, orc, ctx, got, ref, dist, 8, "tall %dx%d" % (w, h))
+    ctx.close()
+
+
 def test_queue_matches_single_calls(V, orc):
     """Three frames in flight, collected in order, equal the oracle."""
     from vif_image_fidelity_amd import synth

@@ -45,10 +45,11 @@ def _ctx(V, w, h, bpc):
     return _ctx_cache[key]
 
 
-def _compare(V, orc, ref, dist, bpc, label):
+def _compare(V, orc, ref, dist, bpc, label, ctx=None):
     h, w = ref.shape
     print("parity case %s %dx%d bpc %d" % (label, w, h, bpc), flush=True)
-    ctx = _ctx(V, w, h, bpc)
+    if ctx is None:
+        ctx = _ctx(V, w, h, bpc)
     got = ctx.score(to_device(ref), to_device(dist))
     gsums = ctx.sums()
     grows = ctx.row_sums()
@@ -83,6 +84,37 @@ def test_4k_parity_first_frames(V, orc):
 EDGE_SHAPES = [(16, 16), (17, 16), (16, 17), (112, 16), (113, 17), (224, 32),
                (225, 33), (16, 300), (300, 16), (71, 71), (72, 72), (73, 41),
                (129, 97), (1000, 37), (37, 1000), (3841, 33)]
+
+
+def _noisy8(seed, w, h, spread=20):
+    g = np.random.Generator(np.random.PCG64(seed))
+    ref = g.integers(0, 256, size=(h, w)).astype(np.uint8)
+    dist = np.clip(ref.astype(np.int16) +
+                   g.integers(-spread, spread + 1, size=(h, w), dtype=np.int16),
+                   0, 255).astype(np.uint8)
+    return ref, dist
+
+
+@pytest.mark.parametrize("wh", [(16, 1048704), (1048704, 16)])
+def test_extreme_aspect_frames(V, orc, wh):
+    """A frame 16 pixels wide has 65 544 tile rows at scale 0, more than a
+    grid's y dimension allows (65 536 blocks): the tiles are laid out in one
+    grid dimension.  Its transpose has 9364 tiles in a row."""
+    w, h = wh
+    ref, dist = _noisy8(w + 3 * h, w, h)
+    ctx = V.Vif(w, h, 8)
+    _compare(V, orc, ref, dist, 8, "extreme aspect", ctx=ctx)
+    ctx.close()
+
+
+def test_max_pixels_parity(V, orc):
+    """The largest frame a context accepts: 2^27 pixels (16384 x 8192)."""
+    w, h = 16384, 8192
+    assert w * h == V.MAX_PIXELS
+    ref, dist = _noisy8(27, w, h)
+    ctx = V.Vif(w, h, 8)
+    _compare(V, orc, ref, dist, 8, "max pixels", ctx=ctx)
+    ctx.close()
 
 
 OPTION_SETS = [

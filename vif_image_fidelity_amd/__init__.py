@@ -17,13 +17,15 @@ import numpy as np
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
                    DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH, MAX_BATCH,
-                   FSSIM_KERNEL_KINDS, FSSIM_QUEUE_DEPTH)
+                   MIN_SIDE, MAX_PIXELS, FSSIM_KERNEL_KINDS,
+                   FSSIM_QUEUE_DEPTH, FSSIM_MAX_PIXELS, FSSIM_MAX_FACTOR)
 
 __all__ = ["Vif", "VifError", "FloatSsim", "fssim_taps", "taps",
            "make_options", "DEFAULT_OPTIONS",
            "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
-           "KERNEL_KINDS", "QUEUE_DEPTH", "MAX_BATCH", "FSSIM_KERNEL_KINDS",
-           "FSSIM_QUEUE_DEPTH"]
+           "KERNEL_KINDS", "QUEUE_DEPTH", "MAX_BATCH", "MIN_SIDE",
+           "MAX_PIXELS", "FSSIM_KERNEL_KINDS", "FSSIM_QUEUE_DEPTH",
+           "FSSIM_MAX_PIXELS", "FSSIM_MAX_FACTOR"]
 
 # Defaults of struct vif_options (include/vif.h states each option's
 # meaning and range).

@@ -19,11 +19,14 @@ NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
 MAX_BATCH = 16
+MIN_SIDE = 16
+MAX_PIXELS = 1 << 27
 NDEBUG = 15
 KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
 FSSIM_TAPS = 11
 FSSIM_QUEUE_DEPTH = 3
-MAX_BATCH = 16
+FSSIM_MAX_PIXELS = 1 << 27
+FSSIM_MAX_FACTOR = 128
 FSSIM_KERNEL_KINDS = ("decimate", "ssim", "rowsum")
 DEBUG_NAMES = ("vif_scale0", "vif_scale1", "vif_scale2", "vif_scale3",
                "vif", "vif_num", "vif_den",

@@ -47,6 +47,9 @@ int decimated_size(int n, int f);
 // Frames one launch may carry (blockIdx.z of the decimation and SSIM
 // kernels, blockIdx.y of the row sums).
 constexpr int kMaxBatch = 16;
+// Blocks per launch in grid dimension y (the runtime allows 65536; planes
+// with more rows of blocks take several launches).
+constexpr int kMaxGridY = 65535;
 
 // Per-frame planes of a launch: frame z reads a[z] and b[z].
 struct FramePair {

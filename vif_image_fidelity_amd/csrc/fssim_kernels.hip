@@ -27,6 +27,8 @@
 // then the columns; the result is the CPU's exact sum, and one conversion
 // to fp32 (round to nearest even) gives the CPU's plane bit for bit.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "fssim_internal.h"
@@ -88,7 +90,8 @@ __device__ __forceinline__ void load4(const uint16_t *p, int c, int w,
   }
 }
 
-// One block: decimated row y = blockIdx.y, decimated columns
+// One block: decimated row y = y0 + blockIdx.y (planes with more rows than
+// a grid's y dimension allows take several launches), decimated columns
 // [x0, x1) with x0 = blockIdx.x * xpb.  Their windows (mirrored) read plane
 // columns [lo, hi]; thread t covers columns a + 4t .. a + 4t + 3 with a = lo
 // rounded down to a multiple of 4.
@@ -104,7 +107,7 @@ template <typename InT, bool kVec>
 __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
     FramePair in, int w, int h, int f, float tap, float in_scale, int ow,
     int oh, int xpb, float *__restrict__ dref_all,
-    float *__restrict__ ddist_all) {
+    float *__restrict__ ddist_all, int y0) {
   const int z = blockIdx.z; // frame of a batched launch
   const InT *__restrict__ ref = static_cast<const InT *>(in.a[z]);
   const InT *__restrict__ dist = static_cast<const InT *>(in.b[z]);
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void decimate_kernel(
   float *__restrict__ ddist = ddist_all + z * plane;
   __shared__ double cs[2][kDecSpan];
   const int t = threadIdx.x;
-  const int y = blockIdx.y;
+  const int y = y0 + static_cast<int>(blockIdx.y);
   const int half = f / 2;
   const int x0 = blockIdx.x * xpb;
   const int x1 = min(ow, x0 + xpb);
@@ -233,7 +236,7 @@ __device__ __forceinline__ void unpack4(const uint32_t (&s)[4],
 template <typename InT, bool kVec, int F>
 __global__ __launch_bounds__(kDecThreads) void decimate_pow2_kernel(
     FramePair in, int w, int h, float iscale, int ow, int oh, int xpb,
-    float *__restrict__ dref_all, float *__restrict__ ddist_all) {
+    float *__restrict__ dref_all, float *__restrict__ ddist_all, int y0) {
   constexpr int f = F;
   const int z = blockIdx.z; // frame of a batched launch
   const InT *__restrict__ ref = static_cast<const InT *>(in.a[z]);
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads) void decimate_pow2_kernel(
   float *__restrict__ ddist = ddist_all + z * plane;
   __shared__ uint32_t cs[2][kDecSpan];
   const int t = threadIdx.x;
-  const int y = blockIdx.y;
+  const int y = y0 + static_cast<int>(blockIdx.y);
   const int half = f / 2;
   const int x0 = blockIdx.x * xpb;
   const int x1 = min(ow, x0 + xpb);
@@ -327,7 +330,7 @@ __device__ __forceinline__ float wtap(const SsimArgs &sa, int k) {
 template <typename InT>
 __global__ __launch_bounds__(256) void ssim_kernel(
     FramePair in, int w, int h, float in_scale, SsimArgs sa,
-    float *__restrict__ map_all, int pitch) {
+    float *__restrict__ map_all, int pitch, int ty0) {
   const int zf = blockIdx.z; // frame of a batched launch
   const InT *__restrict__ px = static_cast<const InT *>(in.a[zf]);
   const InT *__restrict__ py = static_cast<const InT *>(in.b[zf]);
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(256) void ssim_kernel(
 
   const int tid = threadIdx.x;
   const int x0 = blockIdx.x * kTileW;
-  const int y0 = blockIdx.y * kTileH;
+  const int y0 = (ty0 + static_cast<int>(blockIdx.y)) * kTileH;
   // all of a thread's loads are issued before the first LDS store
   {
     constexpr int kPer = (IH * IW + 255) / 256;
@@ -549,8 +552,6 @@ hipError_t launch_decimate_t(const FramePair &in, int n, int w, int h, int f,
                              float tap, float in_scale, int ow, int oh,
                              float *dref, float *ddist, hipStream_t stream) {
   const int xpb = outputs_per_block(f);
-  const dim3 grid(static_cast<unsigned>((ow + xpb - 1) / xpb),
-                  static_cast<unsigned>(oh), static_cast<unsigned>(n));
   const uintptr_t align = 4 * sizeof(InT);
   bool vec = w % 4 == 0;
   for (int z = 0; z < n; ++z)
@@ -560,42 +561,58 @@ hipError_t launch_decimate_t(const FramePair &in, int n, int w, int h, int f,
   // product
   const float iscale = in_scale * tap;
   const dim3 blk(kDecThreads);
+  // grid y holds at most kMaxGridY output rows per launch
+  for (int y0 = 0; y0 < oh; y0 += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>((ow + xpb - 1) / xpb),
+                    static_cast<unsigned>(std::min(kMaxGridY, oh - y0)),
+                    static_cast<unsigned>(n));
 #define FSSIM_POW2(F)                                                          \
   if (vec)                                                                     \
     decimate_pow2_kernel<InT, true, F><<<grid, blk, 0, stream>>>(              \
-        in, w, h, iscale, ow, oh, xpb, dref, ddist);                           \
+        in, w, h, iscale, ow, oh, xpb, dref, ddist, y0);                       \
   else                                                                         \
     decimate_pow2_kernel<InT, false, F><<<grid, blk, 0, stream>>>(             \
-        in, w, h, iscale, ow, oh, xpb, dref, ddist)
-  if (f == 2) {
-    FSSIM_POW2(2);
-  } else if (f == 4) {
-    FSSIM_POW2(4);
-  } else if (f == 8) {
-    FSSIM_POW2(8);
-  } else if (f == 16) {
-    FSSIM_POW2(16);
-  } else if (vec) {
-    decimate_kernel<InT, true><<<grid, blk, 0, stream>>>(
-        in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist);
-  } else {
-    decimate_kernel<InT, false><<<grid, blk, 0, stream>>>(
-        in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist);
+        in, w, h, iscale, ow, oh, xpb, dref, ddist, y0)
+    if (f == 2) {
+      FSSIM_POW2(2);
+    } else if (f == 4) {
+      FSSIM_POW2(4);
+    } else if (f == 8) {
+      FSSIM_POW2(8);
+    } else if (f == 16) {
+      FSSIM_POW2(16);
+    } else if (vec) {
+      decimate_kernel<InT, true><<<grid, blk, 0, stream>>>(
+          in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist, y0);
+    } else {
+      decimate_kernel<InT, false><<<grid, blk, 0, stream>>>(
+          in, w, h, f, tap, in_scale, ow, oh, xpb, dref, ddist, y0);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return e;
   }
 #undef FSSIM_POW2
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <typename InT>
 hipError_t launch_ssim_t(const FramePair &in, int n, int w, int h,
                          float in_scale, const SsimArgs &sa, float *map,
                          hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((w + kTileW - 1) / kTileW),
-                  static_cast<unsigned>((h + kTileH - 1) / kTileH),
-                  static_cast<unsigned>(n));
-  ssim_kernel<InT><<<grid, dim3(256), 0, stream>>>(in, w, h, in_scale, sa,
-                                                   map, map_pitch(h));
-  return hipGetLastError();
+  const int tiles_y = (h + kTileH - 1) / kTileH;
+  // grid y holds at most kMaxGridY rows of tiles per launch
+  for (int t0 = 0; t0 < tiles_y; t0 += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>((w + kTileW - 1) / kTileW),
+                    static_cast<unsigned>(std::min(kMaxGridY, tiles_y - t0)),
+                    static_cast<unsigned>(n));
+    ssim_kernel<InT><<<grid, dim3(256), 0, stream>>>(in, w, h, in_scale, sa,
+                                                     map, map_pitch(h), t0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
 }
 
 } // namespace

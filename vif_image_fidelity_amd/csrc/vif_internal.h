@@ -60,6 +60,9 @@ __host__ __device__ inline int term_groups(int w) { return (w + 3) / 4; }
 // Frames one launch may carry: blockIdx.z of the scale kernels, blockIdx.y
 // of the row sums.
 constexpr int kMaxBatch = 16;
+// Blocks per launch in grid dimension y (the runtime allows 65536; a frame
+// with more rows of tiles takes several launches).
+constexpr int kMaxGridY = 65535;
 
 // Inputs and outputs of one launch of a scale kernel for n frames: frame z
 // reads in_ref[z] / in_dist[z] (the caller's frames at scale 0, the

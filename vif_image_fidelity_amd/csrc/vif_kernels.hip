@@ -27,6 +27,8 @@
 // are the same value.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "vif_device_math.h"
@@ -131,10 +133,12 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
 //
 // Frame z = blockIdx.z of a batched launch reads io.in_ref[z], io.in_dist[z]
 // and writes at its own offsets of the next scale's planes and the terms.
+// Tile (blockIdx.x, strip0 + blockIdx.y): a frame with more strips than a
+// grid's y dimension allows is covered by several launches.
 template <int R, int RD, typename InT>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
-    StatArgs stat) {
+    StatArgs stat, int strip0) {
   const int z = blockIdx.z;
   const InT *__restrict__ ref = static_cast<const InT *>(io.in_ref[z]);
   const InT *__restrict__ dist = static_cast<const InT *>(io.in_dist[z]);
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
 
   const int tid = threadIdx.x;
   const int tx = blockIdx.x;
-  const int strip = blockIdx.y;
+  const int strip = strip0 + static_cast<int>(blockIdx.y);
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
   // 1. input tile [IR][CW] for ref then dist.  A tile whose columns all lie
@@ -492,38 +496,45 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
                         const ScaleGeom &g, const TapArgs &taps,
                         const TapArgs &next_taps, const StatArgs &stat,
                         hipStream_t stream) {
-  if (n < 1 || n > kMaxBatch)
+  if (n < 1 || n > kMaxBatch || scale < 0 || scale > 3)
     return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(g.ntx), static_cast<unsigned>(g.strips),
-                  static_cast<unsigned>(n));
   const dim3 block(kThreads);
-  switch (scale) {
-  case 0:
-    if (bpc == 8) {
-      scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, 1.0f, taps, next_taps, stat);
-    } else {
-      const float sc = bpc == 10 ? 0.25f : bpc == 12 ? 0.0625f : 0.00390625f;
-      scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, sc, taps, next_taps, stat);
+  const float sc = bpc == 8    ? 1.0f
+                   : bpc == 10 ? 0.25f
+                   : bpc == 12 ? 0.0625f
+                               : 0.00390625f;
+  // grid y holds at most kMaxGridY strips per launch
+  for (int s0 = 0; s0 < g.strips; s0 += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>(g.ntx),
+                    static_cast<unsigned>(std::min(kMaxGridY, g.strips - s0)),
+                    static_cast<unsigned>(n));
+    switch (scale) {
+    case 0:
+      if (bpc == 8)
+        scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
+            io, g.w, g.h, sc, taps, next_taps, stat, s0);
+      else
+        scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
+            io, g.w, g.h, sc, taps, next_taps, stat, s0);
+      break;
+    case 1:
+      scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+      break;
+    case 2:
+      scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+      break;
+    default:
+      scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+      break;
     }
-    break;
-  case 1:
-    scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
-                                                          taps, next_taps, stat);
-    break;
-  case 2:
-    scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
-                                                          taps, next_taps, stat);
-    break;
-  case 3:
-    scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(io, g.w, g.h, 1.0f,
-                                                          taps, next_taps, stat);
-    break;
-  default:
-    return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t scale0_resident_blocks(int bpc, int *blocks) {
