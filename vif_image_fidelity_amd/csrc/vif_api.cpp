@@ -20,7 +20,8 @@
 // previous frame's scale-0 event): two of them side by side gain nothing,
 // and each launch's duration then is its own.  A submission is six runtime
 // calls (five launches, one event), plus an event and that stream wait when
-// the scale-0 kernels are ordered.
+// the scale-0 kernels are ordered (and a launch more per scale for every
+// 65535 strips beyond the first: see launch_scale).
 //
 // The slot streams are blocking streams, so they are ordered after work on
 // the default stream (where a caller typically fills the frames); a caller

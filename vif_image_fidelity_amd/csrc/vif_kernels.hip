@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
 }
 
-// Ordered row sums of every scale, one launch per frame.  One wave owns two
+// Ordered row sums of every scale, one launch per submission.  One wave owns two
 // 16-row strips of one scale: lane l adds sequence l%32 (row (l%32)/2,
 // component l%2) of strip 2p + l/32 left to right into one fp32
 // accumulator starting at 0.0f, exactly the serial loop over the row
