@@ -37,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -89,16 +90,26 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines, each line's
+    whitespace runs collapsed (comments and layout do not change the
+    machine code)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(ln.split()) for ln in text.split("\n")
+                     if ln.strip())
+
+
 def kernel_source_hash():
     """SHA-256 of what the VIF kernels' machine code depends on: their
-    sources and the compiler flags of the build."""
+    sources (comments removed) and the compiler flags of the build."""
     from vif_image_fidelity_amd import build
     h = hashlib.sha256()
     for rel in ("vif_image_fidelity_amd/csrc/vif_kernels.hip",
                 "vif_image_fidelity_amd/csrc/vif_device_math.h",
                 "vif_image_fidelity_amd/csrc/vif_internal.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_code_only(f.read()).encode())
     h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()
 

@@ -26,3 +26,14 @@ def test_every_pixel_takes_the_high_branch(orc, index):
             assert high == 1.0, (index, s, high)
         else:
             assert high >= 0.999, (index, s, high)
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The traffic record stays valid across comment edits of the kernel
+    sources and becomes invalid with any code edit."""
+    import bench
+    src = "int f(int a) {  // one\n  /* two\n lines */ return a + 1;\n}\n"
+    same = "// header\nint f(int a) {  // changed\n  return a + 1;\n}\n"
+    other = "int f(int a) {\n  return a + 2;\n}\n"
+    assert bench._code_only(src) == bench._code_only(same)
+    assert bench._code_only(src) != bench._code_only(other)
