@@ -64,6 +64,8 @@ struct Slot {
   hipEvent_t submitted = nullptr; // on the caller's stream
   hipEvent_t done = nullptr;      // on the slot's stream, after the row sums
   hipEvent_t s0_end = nullptr;    // on the slot's stream, after scale 0
+  hipEvent_t s0_done = nullptr;   // the event after this submission's scale
+                                  // 0: s0_end, or the timing event there
   hipEvent_t prof[kKinds][2] = {};
   int prof_mask = 0; // kinds timed for the frame in this slot
   int n = 0;         // frames of the submission in this slot
@@ -181,7 +183,7 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
   // each fills the GPU (the small scales and row sums of one submission
   // still overlap the next one's scale 0)
   if (e == hipSuccess && ctx->order_scale0 && ctx->shead > 0)
-    e = hipStreamWaitEvent(st, ctx->slots[(ctx->shead - 1) % kDepth].s0_end,
+    e = hipStreamWaitEvent(st, ctx->slots[(ctx->shead - 1) % kDepth].s0_done,
                            0);
   sl.prof_mask = ctx->prof_mask;
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
@@ -217,8 +219,14 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
                              nt, ctx->stat, st);
     if (e == hipSuccess && timed)
       e = hipEventRecord(sl.prof[s][1], st);
-    if (e == hipSuccess && s == 0 && ctx->order_scale0)
-      e = hipEventRecord(sl.s0_end, st);
+    // one event after scale 0 orders the next submission's: the timing
+    // event when scale 0 is timed (a second record right after it would
+    // delay the slot's next kernel once more)
+    if (e == hipSuccess && s == 0 && ctx->order_scale0) {
+      sl.s0_done = timed ? sl.prof[0][1] : sl.s0_end;
+      if (!timed)
+        e = hipEventRecord(sl.s0_end, st);
+    }
   }
   vifk::RowSumArgs ra = ctx->rowsum;
   for (int s = 0; s < kScales; ++s) {
