@@ -182,6 +182,28 @@ def test_tall_planes(V, orc, w, h):
     ctx.close()
 
 
+def test_queue_holds_temporary_frames(V, orc):
+    """As for VIF: temporaries passed to submit() and submit_batch() are
+    held by the binding until their collect()."""
+    import torch
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit(frames=3)
+    exps = [orc.fssim_score(r, d, b) for (r, d, b) in frames]
+    ctx = V.FloatSsim(576, 324, 8, max_batch=2)
+    ctx.submit(to_device(frames[0][0]), to_device(frames[0][1]))
+    ctx.submit_batch([to_device(frames[1][0]), to_device(frames[2][0])],
+                     [to_device(frames[1][1]), to_device(frames[2][1])])
+    assert len(ctx._inflight) == ctx.pending() == 3
+    junk = [torch.full((324, 576), 7, dtype=torch.uint8, device="cuda:0")
+            for _ in range(8)]
+    del junk
+    for i in range(3):
+        got = ctx.collect()
+        assert _bits(got).tolist() == _bits(exps[i]).tolist(), i
+    assert len(ctx._inflight) == 0
+    ctx.close()
+
+
 def test_queue_matches_single_calls(V, orc):
     """Three frames in flight, collected in order, equal the oracle."""
     from vif_image_fidelity_amd import synth

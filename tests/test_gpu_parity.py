@@ -308,6 +308,35 @@ def test_async_queue_matches_oracle(V, orc):
     ctx.close()
 
 
+def test_queue_holds_temporary_frames(V, orc):
+    """Frames passed to submit() as temporaries (no other reference) stay
+    alive until their collect(): the binding holds them, so the caching
+    allocator cannot hand their memory to the tensors allocated and filled
+    in between while the kernels read it."""
+    import torch
+    from vif_image_fidelity_amd import synth
+    frames = synth.netflix_576x324_8bit(frames=3)
+    exps = [orc.score(r, d, b)[0] for (r, d, b) in frames]
+    ctx = V.Vif(576, 324, 8)
+    order = [0, 1, 2, 2, 1, 0, 1]
+    outs = []
+    for i in order:
+        if ctx.pending() == V.QUEUE_DEPTH:
+            outs.append(ctx.collect())
+        r, d, _ = frames[i]
+        ctx.submit(to_device(r), to_device(d))
+        assert len(ctx._inflight) == ctx.pending()
+        junk = [torch.full(r.shape, 255, dtype=torch.uint8, device="cuda:0")
+                for _ in range(4)]
+        del junk
+    while ctx.pending():
+        outs.append(ctx.collect())
+    assert len(ctx._inflight) == 0
+    for i, got in zip(order, outs):
+        assert got.tobytes() == exps[i].tobytes(), i
+    ctx.close()
+
+
 def test_graph_replays_match_direct_launches(V, orc):
     """Untimed frames replay a per-slot HIP graph whose frame pointers are
     rewritten each time; timed frames launch directly.  Interleave both,

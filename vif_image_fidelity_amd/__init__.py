@@ -12,6 +12,8 @@ raises.
 The synthetic workload generators live in ``vif_image_fidelity_amd.synth``
 and need neither the library nor a GPU.
 """
+import collections
+
 import numpy as np
 
 from . import _lib
@@ -96,6 +98,10 @@ class Vif:
         if not ctx:
             raise VifError(_lib.vif_errno(), "vif_create")
         self._ctx = ctx
+        # the frames of every pending submission, oldest first: held here
+        # until their collect() returns, so the memory of a temporary frame
+        # is not reused while the kernels still read it
+        self._inflight = collections.deque()
         self.total_rows = sum((self.h >> s) for s in range(4))
         if stream is not None:
             self.set_stream(stream)
@@ -161,21 +167,25 @@ class Vif:
         return out
 
     def submit_host(self, ref, dist):
-        """Enqueue one pair held in host memory; the arrays must stay alive
-        and unchanged until the matching collect() returns."""
+        """Enqueue one pair held in host memory; the arrays must stay
+        unchanged until the matching collect() returns (the context holds a
+        reference to them until then)."""
         rc = _lib.vif_submit_host(self._ctx, self._host_ptr(ref),
                                   self._host_ptr(dist))
         if rc != VIF_OK:
             raise VifError(rc, "vif_submit_host")
+        self._inflight.append((ref, dist))
 
     def submit(self, ref, dist):
         """Enqueue one pair (at most QUEUE_DEPTH pending); the frames must
-        stay valid until the matching collect() returns."""
+        stay unchanged until the matching collect() returns (the context
+        holds a reference to them until then)."""
         self._check_frame(ref)
         self._check_frame(dist)
         rc = _lib.vif_submit(self._ctx, _ptr(ref), _ptr(dist))
         if rc != VIF_OK:
             raise VifError(rc, "vif_submit")
+        self._inflight.append((ref, dist))
 
     def submit_batch(self, refs, dists):
         """Enqueue len(refs) pairs (at most max_batch) as one submission:
@@ -187,11 +197,15 @@ class Vif:
                                    [_ptr(d) for d in dists])
         if rc != VIF_OK:
             raise VifError(rc, "vif_submit_batch")
+        self._inflight.extend(zip(refs, dists))
 
     def collect(self):
         """Outputs of the oldest submitted pair (float64[8])."""
         out = np.zeros(8, dtype=np.float64)
         rc = _lib.vif_collect(self._ctx, out)
+        # drop the frames the library no longer holds (after an error too)
+        while len(self._inflight) > _lib.vif_pending(self._ctx):
+            self._inflight.popleft()
         if rc != VIF_OK:
             raise VifError(rc, "vif_collect")
         return out
@@ -260,8 +274,9 @@ class Vif:
 
     def close(self):
         if getattr(self, "_ctx", None):
-            _lib.vif_destroy(self._ctx)
+            _lib.vif_destroy(self._ctx)  # waits for pending work
             self._ctx = None
+        getattr(self, "_inflight", collections.deque()).clear()
 
     def __del__(self):
         try:
@@ -301,6 +316,7 @@ class FloatSsim:
         if not ctx:
             raise VifError(_lib.vif_errno(), "fssim_create")
         self._ctx = ctx
+        self._inflight = collections.deque()  # as in Vif
         g = np.zeros(3, dtype=np.int32)
         rc = _lib.fssim_geometry(ctx, g)
         if rc != VIF_OK:
@@ -344,6 +360,7 @@ class FloatSsim:
         rc = _lib.fssim_submit(self._ctx, _ptr(ref), _ptr(dist))
         if rc != VIF_OK:
             raise VifError(rc, "fssim_submit")
+        self._inflight.append((ref, dist))
 
     def submit_batch(self, refs, dists):
         """Enqueue len(refs) pairs (at most max_batch) as one submission."""
@@ -353,10 +370,13 @@ class FloatSsim:
                                      [_ptr(d) for d in dists])
         if rc != VIF_OK:
             raise VifError(rc, "fssim_submit_batch")
+        self._inflight.extend(zip(refs, dists))
 
     def collect(self):
         out = np.zeros(2, dtype=np.float64)
         rc = _lib.fssim_collect(self._ctx, out)
+        while len(self._inflight) > _lib.fssim_pending(self._ctx):
+            self._inflight.popleft()
         if rc != VIF_OK:
             raise VifError(rc, "fssim_collect")
         return out
@@ -402,8 +422,9 @@ class FloatSsim:
 
     def close(self):
         if getattr(self, "_ctx", None):
-            _lib.fssim_destroy(self._ctx)
+            _lib.fssim_destroy(self._ctx)  # waits for pending work
             self._ctx = None
+        getattr(self, "_inflight", collections.deque()).clear()
 
     def __del__(self):
         try:
