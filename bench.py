@@ -564,6 +564,10 @@ def main():
     dt1080, kt1080 = time_frames(V, f1080, 1920, 1080, 10, args.steps_1080p,
                                  10)
     fps1080 = args.steps_1080p / dt1080
+    # and the bright 16-bit pairs of the same size
+    f1080b = synth.bright_1080p_16bit()
+    dt1080b, _ = time_frames(V, f1080b, 1920, 1080, 16, args.steps_1080p, 10)
+    fps1080b = args.steps_1080p / dt1080b
 
     # 576x324 (the launch-bound small frame) and 4K fed from host memory
     fsmall = synth.netflix_576x324_8bit()
@@ -574,6 +578,7 @@ def main():
     batched = {}
     for key, fr, bw, bh, bb, nb, steps in (
             ("1080p_10bit_batch8", f1080, 1920, 1080, 10, 8, 3000),
+            ("1080p_16bit_batch8", f1080b, 1920, 1080, 16, 8, 3000),
             ("576x324_8bit_batch16", fsmall, 576, 324, 8, 16, 8000)):
         dtb, _ = time_frames(V, fr, bw, bh, bb, steps, 4 * nb, batch=nb)
         batched[key] = round(steps / dtb, 1)
@@ -604,6 +609,7 @@ def main():
              "scale0_frac_one_frame_per_submission": round(
                  ops / (s0_one_ms / 1000.0) / VALU_PEAK_OPS, 4),
              "fps_1080p_10bit": round(fps1080, 1),
+             "fps_1080p_16bit": round(fps1080b, 1),
              "fps_576x324_8bit": round(fps_small, 1),
              "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
              "fps_batched": batched,
