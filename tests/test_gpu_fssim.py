@@ -204,6 +204,35 @@ def test_queue_holds_temporary_frames(V, orc):
     ctx.close()
 
 
+def test_caller_stream_orders_frame_writes(V, orc):
+    """With the caller's stream set, work queued on it before a submit
+    (here a copy that writes the frames, behind other work on that stream)
+    is ordered before the decimation reads them."""
+    import torch
+    from vif_image_fidelity_amd import synth
+    frames = synth.pink_4k_8bit(frames=2)
+    exps = [orc.fssim_score(r, d, b) for (r, d, b) in frames]
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.FloatSsim(3840, 2160, 8)
+    s = torch.cuda.Stream()
+    a = torch.ones(2048, 2048, device="cuda:0")
+    for k in range(2):
+        dr = dev[1 - k][0].clone()
+        dd = dev[1 - k][1].clone()
+        torch.cuda.synchronize()
+        ctx.set_stream(s)
+        with torch.cuda.stream(s):
+            for _ in range(8):
+                a = torch.mm(a, a) * (1.0 / 2048)
+            dr.copy_(dev[k][0])
+            dd.copy_(dev[k][1])
+        got = ctx.score(dr, dd)
+        ctx.set_stream(None)
+        assert _bits(got).tolist() == _bits(exps[k]).tolist(), k
+    torch.cuda.synchronize()
+    ctx.close()
+
+
 def test_queue_matches_single_calls(V, orc):
     """Three frames in flight, collected in order, equal the oracle."""
     from vif_image_fidelity_amd import synth
