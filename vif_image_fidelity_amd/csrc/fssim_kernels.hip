@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void ssim_kernel(
       map_all + zf * static_cast<size_t>(w) * static_cast<size_t>(pitch);
   constexpr int R = kRadius;
   constexpr int IW = kTileW + 2 * R; // 74 columns
-  constexpr int IH = kTileH + 2 * R; // 26 rows
+  constexpr int IH = kTileH + 2 * R; // 18 rows
   constexpr int P = IW + 1;          // odd pitch
   constexpr int VB = kTileH / 2;     // rows per thread, vertical pass
   constexpr int HB = kTileW * kTileH / 256; // pixels per thread, horizontal
