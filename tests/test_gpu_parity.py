@@ -337,6 +337,52 @@ def test_queue_holds_temporary_frames(V, orc):
     ctx.close()
 
 
+def test_contexts_in_two_threads(V, orc):
+    """Separate contexts are independent: two host threads, each with its
+    own context (one 576x324, one 1920x1080 10-bit), score their frames
+    through full queues at the same time (ctypes releases the interpreter
+    lock during library calls), and every output matches the oracle."""
+    import threading
+    from vif_image_fidelity_amd import synth
+    work = {"small": synth.netflix_576x324_8bit(frames=3),
+            "1080p": synth.checker_1080p_10bit(frames=2)}
+    want = {k: [orc.score(r, d, b)[0] for (r, d, b) in fr]
+            for k, fr in work.items()}
+    dev = {k: [(to_device(r), to_device(d)) for (r, d, _) in fr]
+           for k, fr in work.items()}
+    got = {}
+    errors = []
+
+    def run(key):
+        try:
+            r0 = work[key][0][0]
+            ctx = V.Vif(r0.shape[1], r0.shape[0], work[key][0][2])
+            outs = []
+            order = list(range(len(dev[key]))) * 6
+            for i in order:
+                if ctx.pending() == V.QUEUE_DEPTH:
+                    outs.append(ctx.collect())
+                ctx.submit(*dev[key][i])
+            while ctx.pending():
+                outs.append(ctx.collect())
+            ctx.close()
+            got[key] = (order, outs)
+        except Exception as e:  # reported below, in the main thread
+            errors.append((key, repr(e)))
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in work]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(got) == sorted(work), "a thread did not finish"
+    for key, (order, outs) in got.items():
+        assert len(outs) == len(order)
+        for i, out in zip(order, outs):
+            assert out.tobytes() == want[key][i].tobytes(), (key, i)
+
+
 def test_graph_replays_match_direct_launches(V, orc):
     """Untimed frames replay a per-slot HIP graph whose frame pointers are
     rewritten each time; timed frames launch directly.  Interleave both,
