@@ -233,6 +233,24 @@ def test_caller_stream_orders_frame_writes(V, orc):
     ctx.close()
 
 
+def test_random_sweep(V, orc):
+    """A seeded sweep of 30 random frame sizes (1..1499 on each side, so
+    factors 1 to 6, odd and even sizes) and bit depths: decimated planes,
+    map, row sums and score bit for bit as the oracle."""
+    g = np.random.Generator(np.random.PCG64(2027))
+    for case in range(30):
+        w = int(g.integers(1, 1500))
+        h = int(g.integers(1, 1500))
+        bpc = int(g.choice([8, 10, 12, 16]))
+        top = (1 << bpc) - 1
+        dt = np.uint8 if bpc == 8 else np.uint16
+        ref = g.integers(0, top + 1, size=(h, w))
+        dist = np.clip(ref + g.integers(-(top // 8), top // 8 + 1,
+                                        size=(h, w)), 0, top)
+        _compare(V, orc, ref.astype(dt), dist.astype(dt), bpc,
+                 "sweep %d" % case)
+
+
 def test_queue_matches_single_calls(V, orc):
     """Three frames in flight, collected in order, equal the oracle."""
     from vif_image_fidelity_amd import synth

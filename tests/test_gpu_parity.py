@@ -254,6 +254,73 @@ def test_input_load_paths(V, orc, bpc):
         ctx.close()
 
 
+def _random_pair(g, w, h, bpc):
+    """One seeded pair of a randomly chosen kind: noise, smooth, a flat
+    region, or a gradient; the distorted frame noisy or blurred."""
+    top = (1 << bpc) - 1
+    kind = int(g.integers(0, 4))
+    if kind == 0:
+        ref = g.integers(0, top + 1, size=(h, w))
+    elif kind == 1:
+        base = g.integers(0, top + 1, size=(h + 4, w + 4)).astype(np.float64)
+        ref = np.rint(sum(base[i:i + h, j:j + w] for i in range(5)
+                          for j in range(5)) / 25.0)
+    elif kind == 2:
+        ref = g.integers(0, top + 1, size=(h, w))
+        ref[h // 4:3 * h // 4, w // 4:3 * w // 4] = top // 3
+    else:
+        ref = np.rint(np.linspace(0, top, w)[None, :] +
+                      g.normal(0, top / 50.0, size=(h, w)))
+    ref = np.clip(ref, 0, top)
+    if g.integers(0, 2):
+        dist = ref + np.rint(g.normal(0, top * g.uniform(0.005, 0.1),
+                                      size=(h, w)))
+    else:
+        pad = np.pad(ref.astype(np.float64), 1, mode="edge")
+        dist = np.rint(sum(pad[i:i + h, j:j + w] for i in range(3)
+                           for j in range(3)) / 9.0)
+    dt = np.uint8 if bpc == 8 else np.uint16
+    return (ref.astype(dt), np.clip(dist, 0, top).astype(dt))
+
+
+def test_random_sweep(V, orc):
+    """A seeded sweep of 40 random cases: frame sizes 16..499 x 16..399,
+    bit depths 8/10/12/16, frame content, options (a third of the cases)
+    and submissions of 1 to 3 frames; every output and every per-scale sum
+    bit for bit as the oracle, and the row sums of each submission's last
+    frame."""
+    g = np.random.Generator(np.random.PCG64(2026))
+    for case in range(40):
+        w = int(g.integers(16, 500))
+        h = int(g.integers(16, 400))
+        bpc = int(g.choice([8, 10, 12, 16]))
+        n = int(g.integers(1, 4))
+        opt = None
+        if g.uniform() < 1 / 3:
+            opt = {"sigma_nsq": float(g.choice([0.5, 1.5, 2.0, 3.0, 4.7])),
+                   "enhn_gain_limit": float(g.choice([0.5, 1.0, 100.0])),
+                   "skip_scale0": int(g.integers(0, 2)),
+                   "scale_min_val": tuple(float(v) for v in
+                                          g.choice([0.0, 0.5, 0.99], 3))}
+        pairs = [_random_pair(g, w, h, bpc) for _ in range(n)]
+        print("sweep case %d: %dx%d bpc %d, %d frame(s), options %s"
+              % (case, w, h, bpc, n, opt), flush=True)
+        with V.Vif(w, h, bpc, options=opt, max_batch=n) as ctx:
+            dev = [(to_device(r), to_device(d)) for r, d in pairs]
+            ctx.submit_batch([a for a, _ in dev], [b for _, b in dev])
+            for i, (r, d) in enumerate(pairs):
+                got = ctx.collect()
+                exp, esums, erows = orc.score(r, d, bpc, want_rows=True,
+                                              options=opt)
+                assert got.view(np.uint64).tolist() == \
+                    exp.view(np.uint64).tolist(), (case, i, got, exp)
+                assert ctx.sums().view(np.uint32).tolist() == \
+                    esums.view(np.uint32).tolist(), (case, i)
+            grows = ctx.row_sums()
+            assert (grows.view(np.uint32) == erows.view(np.uint32)).all(), \
+                case
+
+
 def test_flat_and_identical_frames(V, orc):
     f = np.full((64, 80), 200, np.uint8)
     out = _compare(V, orc, f, f, 8, "flat")
