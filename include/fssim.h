@@ -143,10 +143,13 @@ int fssim_taps(float taps[FSSIM_TAPS]);
 
 /*
  * Kernel timing, as vif_set_profiling / vif_get_kernel_times, for the kinds
- *   0  decimation (both planes, one launch; absent at f = 1)
+ *   0  decimation (both planes; absent at f = 1)
  *   1  SSIM stage (filter and per-pixel value)
  *   2  ordered row sums
- * kinds is a bit mask (0x7 all).  fssim_get_kernel_times returns 3.
+ * kinds is a bit mask (0x7 all).  fssim_get_kernel_times returns 3.  A
+ * launch counted there is one kind's work for one submission: one kernel
+ * launch, or several in a row for planes with more than 65535 rows of
+ * blocks, timed as one.
  */
 int fssim_set_profiling(fssim_ctx *ctx, int kinds);
 int fssim_get_kernel_times(const fssim_ctx *ctx, double *ms, long *launches,

@@ -262,7 +262,10 @@ int vif_set_profiling(vif_ctx *ctx, int kinds);
  * launch counts since profiling was enabled, one entry per kernel kind:
  *   0..3  the kernel of scale s (filter, statistic, terms, next scale's
  *         planes)
- *   4     the ordered row sums of all four scales (one launch per frame)
+ *   4     the ordered row sums of all four scales
+ * A launch here is one kind's work for one submission (all its frames): one
+ * kernel launch, or several in a row for a scale with more than 65535 strips
+ * of 16 rows, timed as one.
  * ms and launches hold at least `capacity` entries (either may be NULL).
  * Returns the number of kinds (5) or VIF_EINVAL.
  */
