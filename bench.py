@@ -88,6 +88,7 @@ VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
 HBM_PEAK_GBS = 8000.0
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
+PROFILE_TRAFFIC_1080P = os.path.join(ROOT, "profiles", "traffic_1080p_10bit.json")
 
 
 def _code_only(text):
@@ -114,12 +115,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def load_traffic(batch):
+def load_traffic(batch, path=PROFILE_TRAFFIC):
     """Counter-derived HBM bytes per launch of the scale-0 kernel (a launch
     of `batch` frames) and per frame of the whole path, if taken on the
     current kernel source at that batch size."""
     try:
-        rec = json.load(open(PROFILE_TRAFFIC))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None, None
     if (rec.get("kernel_source_sha256") != kernel_source_hash() or
@@ -634,6 +635,13 @@ def main():
         gbs = frame_bytes * fps / 1e9
         extra["hbm_gbs_per_frame_counters"] = round(gbs, 1)
         extra["hbm_frac_of_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+    # the same for the 1920x1080 10-bit pairs in batches of 8
+    _, fb1080 = load_traffic(8, PROFILE_TRAFFIC_1080P)
+    if fb1080:
+        gbs = fb1080 * batched["1080p_10bit_batch8"] / 1e9
+        extra["hbm_1080p_10bit_batch8"] = {
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "frame_bytes": fb1080}
 
     cpu = None
     if not args.no_cpu_baseline:
