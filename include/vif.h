@@ -198,9 +198,10 @@ void vif_destroy(vif_ctx *ctx);
  * vif_set_stream -- the caller's HIP stream (a hipStream_t passed as void*,
  * e.g. torch's current stream; NULL = the default stream, the initial
  * setting): work queued on it before vif_submit (say, the copy that fills
- * the frames) is ordered before the frame's kernels, which run on two
- * streams the context owns.  Those are blocking streams, so work on the
- * default stream orders itself; a non-NULL stream costs one event per frame.
+ * the frames) is ordered before the frame's kernels, which run on the
+ * streams the context owns (one per queue slot).  Those are blocking
+ * streams, so work on the default stream orders itself; a non-NULL stream
+ * costs one event per submission.
  * The caller keeps the stream alive while the context uses it.  VIF_EINVAL
  * while frames are pending.
  */

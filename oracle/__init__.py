@@ -119,6 +119,9 @@ class Oracle:
             fn.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p,
                            ctypes.c_int, f32p]
             fn.restype = ctypes.c_int
+        lib.vifo_ordered_sums.argtypes = [f32p, f32p, ctypes.c_int,
+                                          ctypes.c_int, f32p, f32p, f32p]
+        lib.vifo_ordered_sums.restype = ctypes.c_int
         lib.vifo_total_rows.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.vifo_total_rows.restype = ctypes.c_int
         lib.vifo_score.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
@@ -245,6 +248,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("decimate rejected its arguments")
         return out
+
+    def ordered_sums(self, num_t, den_t):
+        """The ordered fp32 sums of two (h, w) term planes: returns
+        (rows (h, 2) float32 of n_y, d_y; N float32; D float32)."""
+        num_t = np.ascontiguousarray(num_t, dtype=np.float32)
+        den_t = np.ascontiguousarray(den_t, dtype=np.float32)
+        if num_t.shape != den_t.shape or num_t.ndim != 2:
+            raise ValueError("two equal 2-D term planes needed")
+        h, w = num_t.shape
+        rows = np.zeros((h, 2), dtype=np.float32)
+        n = np.zeros(1, dtype=np.float32)
+        d = np.zeros(1, dtype=np.float32)
+        rc = self.lib.vifo_ordered_sums(_fp(num_t), _fp(den_t), w, h,
+                                        _fp(rows), _fp(n), _fp(d))
+        if rc != 0:
+            raise ValueError("vifo_ordered_sums rejected its arguments")
+        return rows, n[0], d[0]
 
     def total_rows(self, w, h):
         return int(self.lib.vifo_total_rows(int(w), int(h)))
@@ -398,6 +418,10 @@ def filter2d(plane, tap):
 
 def decimate(plane, tap):
     return _load().decimate(plane, tap)
+
+
+def ordered_sums(num_t, den_t):
+    return _load().ordered_sums(num_t, den_t)
 
 
 def total_rows(w, h):

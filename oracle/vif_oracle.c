@@ -375,6 +375,39 @@ int vifo_total_rows(int w, int h)
 }
 
 /* ---------------------------------------------------------------------- */
+/* O9  ordered sums [ADR-1422 Context: the CPU adds the terms into one fp32
+ * sum per row and then adds the rows; ADR-1422 Decision: a row's terms go
+ * left to right into one fp32 accumulator that starts at zero, and the row
+ * sums are added top to bottom in fp32].  num_t and den_t are w*h term
+ * planes, row-major.  rowsums (optional) receives n_y, d_y for each row y;
+ * *n_out and *d_out the plane's two sums.                                */
+int vifo_ordered_sums(const float *num_t, const float *den_t, int w, int h,
+                      float *rowsums, float *n_out, float *d_out)
+{
+    if (num_t == NULL || den_t == NULL || n_out == NULL || d_out == NULL ||
+        w < 1 || h < 1)
+        return -1;
+    float n_s = 0.0f, d_s = 0.0f;
+    for (int y = 0; y < h; y++) {
+        float n_y = 0.0f, d_y = 0.0f;
+        for (int x = 0; x < w; x++) {
+            const size_t i = (size_t)y * w + x;
+            n_y = n_y + num_t[i];
+            d_y = d_y + den_t[i];
+        }
+        if (rowsums != NULL) {
+            rowsums[2 * y] = n_y;
+            rowsums[2 * y + 1] = d_y;
+        }
+        n_s = n_s + n_y;
+        d_s = d_s + d_y;
+    }
+    *n_out = n_s;
+    *d_out = d_s;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Options.  Reading: the pages name vif_sigma_nsq, vif_enhn_gain_limit,
  * vif_skip_scale0, vif_kernelscale and vif_scale1..3_min_val (default 0)
  * [ADR-1422 Decision and Consequences; ADR-1444 Decision and Consequences]
@@ -495,25 +528,17 @@ int vifo_score_ex(const void *ref, const void *dist, int w, int h, int bpc,
             vifo_filter(XY, ws, hs, taps, nt, fxy) != 0)
             goto done;
 
-        float n_s = 0.0f, d_s = 0.0f;
-        for (int y = 0; y < hs; y++) {
-            float n_y = 0.0f, d_y = 0.0f;
-            for (int x = 0; x < ws; x++) {
-                const size_t i = (size_t)y * ws + x;
-                float num_t, den_t;
-                vifo_statistic_ex(mu1[i], mu2[i], fxx[i], fyy[i], fxy[i],
-                                  opt->sigma_nsq, opt->enhn_gain_limit,
-                                  &num_t, &den_t);
-                n_y = n_y + num_t;
-                d_y = d_y + den_t;
-            }
-            if (rowsums != NULL) {
-                rowsums[2 * (row_base + y)] = n_y;
-                rowsums[2 * (row_base + y) + 1] = d_y;
-            }
-            n_s = n_s + n_y;
-            d_s = d_s + d_y;
-        }
+        /* the products' planes are free once filtered: they take the
+         * term planes (row-major, like the planes) */
+        float *num_t = XX, *den_t = YY;
+        for (size_t i = 0; i < ns; i++)
+            vifo_statistic_ex(mu1[i], mu2[i], fxx[i], fyy[i], fxy[i],
+                              opt->sigma_nsq, opt->enhn_gain_limit,
+                              &num_t[i], &den_t[i]);
+        float n_s, d_s;
+        vifo_ordered_sums(num_t, den_t, ws, hs,
+                          rowsums != NULL ? rowsums + 2 * row_base : NULL,
+                          &n_s, &d_s);
         row_base += (size_t)hs;
         N[s] = n_s;
         D[s] = d_s;

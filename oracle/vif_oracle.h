@@ -101,6 +101,13 @@ int vifo_filter(const float *src, int w, int h, const float *taps, int n,
 int vifo_decimate(const float *src, int w, int h, const float *taps, int n,
                   float *dst);
 
+/* Ordered sums of one scale's w*h term planes (row-major): each row's terms
+ * left to right into one fp32 accumulator from 0 (rowsums, optional: n_y,
+ * d_y per row), then the row sums top to bottom into one fp32 accumulator
+ * per plane (*n_out, *d_out).  Returns 0, or -1 for bad arguments. */
+int vifo_ordered_sums(const float *num_t, const float *den_t, int w, int h,
+                      float *rowsums, float *n_out, float *d_out);
+
 /* Number of rows over all four scales for a w*h frame (h + h/2 + ...). */
 int vifo_total_rows(int w, int h);
 

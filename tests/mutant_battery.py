@@ -43,6 +43,9 @@ def battery(orc):
         ("bitdepth", lambda: P.test_cross_bit_depth_invariance(orc)),
         ("flat_sums", lambda: P.test_flat_frame_sums_are_pixel_counts(
             orc, (40, 40))),
+        ("sums_closed", lambda: P.test_ordered_sums_closed_form(orc)),
+        ("sums_2_24",
+         lambda: P.test_ordered_sums_rounding_accumulates_past_2_24(orc)),
         ("flat_one", lambda: P.test_flat_frame_scores_exactly_one(orc, 8, 128)),
         ("self", lambda: P.test_reference_against_itself(orc, 1)),
         ("stat_low", lambda: P.test_statistic_low_variance_branch(orc)),

@@ -2,11 +2,11 @@
 host, bit for bit, before the pipeline is trusted.
 
 ADR-1444 "float_vif_hip runs the arithmetic of the CUDA twin ...",
-Decision: the device's fp64 add and divide were compared with the host's
-over 33.5 million operand pairs spanning 2^-40 to 2^40 and six noise
-variances (the sum, the quotient and both fp32 roundings of one plus the
-quotient).  Here: 2^25 pairs over the same span, six variances, plus
-targeted near-ties; the fp32 division; the log2 polynomial exhaustively
+Decision, reports a host comparison of the device's fp64 add and divide
+over tens of millions of operand pairs and several noise variances.  Here:
+2^25 pairs with magnitudes from 2^-40 to 2^40, six variances, targeted
+near-ties, each checked on the sum, the quotient and both fp32 roundings of
+one plus the quotient; the fp32 division; the log2 polynomial exhaustively
 (every mantissa of exponents 0..31); the ratios and the whole statistic
 against the oracle.
 """

@@ -451,10 +451,10 @@ def test_contexts_in_two_threads(V, orc):
 
 
 def test_graph_replays_match_direct_launches(V, orc):
-    """Untimed frames replay a per-slot HIP graph whose frame pointers are
-    rewritten each time; timed frames launch directly.  Interleave both,
-    with host synchronisation between replays, over changing frames: every
-    replay must give the oracle's bits."""
+    """Frames submitted with and without kernel timing (the timed ones
+    record HIP events around each launch) interleave over changing frames,
+    with host synchronisation between rounds: every frame must give the
+    oracle's bits whichever way it was launched."""
     from vif_image_fidelity_amd import synth
     frames = synth.netflix_576x324_8bit(frames=3)
     exps = [orc.score(r, d, b)[0] for (r, d, b) in frames]
@@ -599,12 +599,13 @@ def test_batch_4k_bench_configuration(V, orc):
 
 
 def test_4k_ordered_stream_paths(V, orc):
-    """At 3840x2160 consecutive scale-0 kernels run on the context's own
-    scale-0 stream and the other kernels wait for them across streams.
-    Every way in is checked on that path: a full queue of device frames with
-    every kernel timed, a queue of pinned host frames (copies on the slot's
-    stream, scale 0 on the other), and frames written on the caller's stream
-    just before the submit, behind other work on that stream."""
+    """At 3840x2160 one scale-0 kernel fills the GPU twice over, so
+    consecutive submissions' scale-0 kernels are ordered: each slot's stream
+    waits for the previous slot's scale-0 event.  Every way in is checked on
+    that path: a full queue of device frames with every kernel timed, a
+    queue of pinned host frames (copied on the slot's own stream ahead of
+    its kernels), and frames written on the caller's stream just before the
+    submit, behind other work on that stream."""
     import torch
     from vif_image_fidelity_amd import synth
     frames = [synth.pink_4k_frame(i) for i in range(2)]

@@ -81,6 +81,24 @@ MUTANTS = [
     ("log2_t_not_minus_one", "const float t = m - 1.0f;",
      "const float t = m - 0.5f;"),
     ("row_sum_swapped", "n_s = n_s + n_y;", "n_s = n_s + d_y;"),
+    # the ordered sums (O9)
+    ("row_acc_fp64", "float n_y = 0.0f, d_y = 0.0f;",
+     "double n_y = 0.0, d_y = 0.0;"),
+    ("scale_acc_fp64", "float n_s = 0.0f, d_s = 0.0f;\n    for (int y = 0;",
+     "double n_s = 0.0, d_s = 0.0;\n    for (int y = 0;"),
+    ("rows_bottom_up", "    for (int y = 0; y < h; y++) {\n        float n_y",
+     "    for (int y = h - 1; y >= 0; y--) {\n        float n_y"),
+    ("row_right_to_left",
+     "        for (int x = 0; x < w; x++) {\n"
+     "            const size_t i = (size_t)y * w + x;\n            n_y",
+     "        for (int x = w - 1; x >= 0; x--) {\n"
+     "            const size_t i = (size_t)y * w + x;\n            n_y"),
+    ("one_accumulator_per_plane",
+     "        n_s = n_s + n_y;\n        d_s = d_s + d_y;\n    }\n    *n_out",
+     "        for (int x = 0; x < w; x++) {\n"
+     "            n_s = n_s + num_t[(size_t)y * w + x];\n"
+     "            d_s = d_s + den_t[(size_t)y * w + x];\n"
+     "        }\n    }\n    *n_out"),
     ("totals_skip_scale1", "num = (double)N[0] + (double)N[1];",
      "num = (double)N[0] + (double)N[0];"),
     ("score_inverted", "out[s] = (double)N[s] / (double)D[s];",

@@ -272,6 +272,95 @@ def test_flat_frame_sums_are_pixel_counts(orc, wh):
     assert rows.shape[0] == base
 
 
+# -------------------------------------------------------------- P10 / O9
+
+# Two crafted 4x4 term planes whose ordered fp32 sums are closed forms.
+# fp32 holds every integer up to 2^24 = 16777216; above it the spacing is 2
+# (4 above 2^25), and round-to-nearest-even sends a tie to the neighbour
+# whose last significand bit is 0, i.e. the multiple of 4 here.
+#   num row 0  [2^24, 1, 1, 1]: each 2^24 + 1 is a tie, kept at 2^24.
+#   num row 1  [1, 1, 1, 1]: 4, exactly.
+#   num row 2  [1, 1, 1, 2^24]: 3 + 2^24 = 16777219 is a tie, 16777220.
+#   num row 3  zeros.
+#   N = 2^24 + 4, then + 16777220 = 2^25 + 8 (a multiple of 4, exact), + 0.
+#   den rows   [2^24, 0, 0, 0], then three rows [1, 0, 0, 0]: row sums
+#              2^24, 1, 1, 1; top to bottom each + 1 is a tie kept at
+#              2^24, so D = 2^24.
+# Mistakes this separates: rows added right to left (num row 0 gives
+# 2^24 + 4), rows or the plane accumulated in fp64 (2^24 + 3 rounds to
+# 2^24 + 4 when stored), rows summed bottom to top (D = 2^24 + 4), one
+# accumulator for the whole plane (N = 2^25).
+P24 = float(1 << 24)
+SUM_NUM = np.array([[P24, 1, 1, 1], [1, 1, 1, 1], [1, 1, 1, P24],
+                    [0, 0, 0, 0]], dtype=np.float32)
+SUM_DEN = np.array([[P24, 0, 0, 0], [1, 0, 0, 0], [1, 0, 0, 0],
+                    [1, 0, 0, 0]], dtype=np.float32)
+SUM_ROWS = np.array([[16777216.0, 16777216.0], [4.0, 1.0],
+                     [16777220.0, 1.0], [0.0, 1.0]], dtype=np.float32)
+SUM_N = np.float32(33554440.0)
+SUM_D = np.float32(16777216.0)
+
+
+def test_ordered_sums_closed_form(orc):
+    """O9 (ADR-1422 Context and Decision): one fp32 accumulator per row from
+    zero, terms left to right, then the row sums top to bottom in fp32."""
+    rows, n, d = orc.ordered_sums(SUM_NUM, SUM_DEN)
+    assert np.array_equal(rows, SUM_ROWS)
+    assert n == SUM_N and d == SUM_D
+    # each plane alone: the num rows' sums with zero den terms, and so on
+    rows2, n2, d2 = orc.ordered_sums(SUM_DEN, SUM_NUM)
+    assert np.array_equal(rows2, SUM_ROWS[:, ::-1])
+    assert n2 == SUM_D and d2 == SUM_N
+
+
+def test_ordered_sums_rounding_accumulates_past_2_24(orc):
+    """O9 over many rows: a 3 x 2^23 plane of ones has row sums 3.  The
+    running fp32 total is exact up to 3 * 5592405 = 2^24 - 1; from there an
+    odd partial sum lies halfway between two representable even integers,
+    and RNE takes the multiple of 4, so every further row adds 4 (or 2 once)
+    and the total is not 3 * 2^23, which fp32 holds exactly."""
+    h = 1 << 23
+    ones = np.ones((h, 3), dtype=np.float32)
+    rows, n, d = orc.ordered_sums(ones, ones)
+    assert np.all(rows == 3.0)
+    # the running total in fp32, row by row: below 2^24 every partial sum
+    # 3k is exact; at and above it, S + 3 is odd, so fl32 goes to the
+    # neighbour that is a multiple of 4 (S is even there)
+    s = 0
+    for _ in range(h):
+        t = s + 3
+        if t > (1 << 24) and t % 2 == 1:
+            t = t - 1 if (t - 1) % 4 == 0 else t + 1
+        s = t
+    assert float(n) == float(s) == float(d)
+    assert s != 3 * h
+
+
+def test_frame_sums_round_in_fp32_past_2_24(orc):
+    """O9 through the whole feature: with a noise variance of 1e30 every
+    pixel takes the low-variance branch, so every term is exactly 1 and
+    each scale-0 row sums to w = 1023 exactly.  The frame has 1023 x 16500 >
+    2^24 pixels: the top-to-bottom fp32 total is exact up to row 16400
+    (16777200) and from there each odd partial sum is a tie that RNE sends
+    to the multiple of 4.  N_0 and D_0 must be that total, not w * h."""
+    w, h = 1023, 16500
+    g = np.random.Generator(np.random.PCG64(11))
+    r = g.integers(0, 256, size=(h, w), dtype=np.uint8)
+    out, sums, rows = orc.score(r, r, 8, want_rows=True,
+                                options={"sigma_nsq": 1e30})
+    assert np.all(rows[:h] == w)
+    s = 0
+    for _ in range(h):
+        t = s + w
+        if t > (1 << 24) and t % 2 == 1:
+            t = t - 1 if (t - 1) % 4 == 0 else t + 1
+        s = t
+    assert s != w * h
+    assert float(sums[0]) == float(s) and float(sums[1]) == float(s)
+    # scale 1 has 511 x 8250 < 2^24 pixels: its sums are exact
+    assert float(sums[2]) == 511 * 8250 == float(sums[3])
+
+
 # --------------------------------------------------------------------- P7
 
 @pytest.mark.parametrize("bpc,val", [(8, 0), (8, 128), (8, 255), (10, 1023),
