@@ -34,6 +34,7 @@ The line carries, besides the contract fields:
                 oracle's rate.
 """
 import argparse
+import collections
 import hashlib
 import json
 import os
@@ -87,6 +88,10 @@ VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
 
 HBM_PEAK_GBS = 8000.0
 
+# The pages' parity gate: an output further than this from the CPU's fails
+# (ADR-1422 and ADR-1444, Context).  Bit identity is reported beside it.
+PARITY_GATE = 5e-5
+
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
 PROFILE_TRAFFIC_1080P = os.path.join(ROOT, "profiles", "traffic_1080p_10bit.json")
 
@@ -136,112 +141,162 @@ def ensure_lib():
     _lib.load()
 
 
-def time_frames(V, frames, w, h, bpc, steps, warmup, prof_kinds=0,
-                batch=1):
-    """Scores `steps` frames (cycling over the resident pairs) through the
-    context's queue, `batch` frames per submission (one launch per kernel
-    for the whole batch).  Returns (seconds, kernel times)."""
+def _device_pairs(frames):
     import torch
     dev = torch.device("cuda:0")
 
     def td(a):
-        import numpy as np
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
     pairs = [(td(r), td(d)) for (r, d, _) in frames]
-    ctx = V.Vif(w, h, bpc, max_batch=batch)
+    torch.cuda.synchronize()
+    return pairs
+
+
+def steady_state(V, frames, w, h, bpc, steps, warmup, batch=1, reps=5,
+                 prof_kinds=0, settle_s=0.25):
+    """Scores the resident frames (cycling over them) through one context's
+    queue, `batch` frames per submission (each kernel launched once for the
+    batch), and times the queue in steady state.
+
+    The queue is kept full throughout: a new submission goes in as soon as
+    the oldest one's frames have been collected.  `warmup` submissions run
+    first, untimed, and more after them until `settle_s` seconds have
+    passed since the first (the device's clocks rise over the first tens of
+    milliseconds of work after an idle spell; the number run is returned);
+    the queue is then filled, if it is not yet.  Each
+    of the `reps` timed repetitions then counts exactly `steps`
+    submissions: t0 is taken with the queue full, each step collects the
+    oldest submission (a collect waits for that submission's completion
+    event on the device, so its work is finished) and submits the next, and
+    t1 follows the last step's collect and submit.  The repetitions run back
+    to back, and the queue is drained after the last, untimed.  So the
+    region covers `steps` submission completions of a pipeline that neither
+    fills nor drains inside it.
+
+    Returns {"seconds": [per repetition], "kernel": {kind: (ms, launches)}
+    over the timed repetitions, "host_us": per-frame host time of submit and
+    collect calls, "outputs": {frame index: set of out[8] byte strings},
+    "warmup_run": warm-up submissions run}."""
+    import torch
     from vif_image_fidelity_amd import _lib
+    pairs = _device_pairs(frames)
     ptrs = [(r.data_ptr(), d.data_ptr()) for r, d in pairs]
-
-    host = {"submit": 0.0, "collect": 0.0}
-
-    def run(n):
-        # keep the context's queue full: a submission goes in as soon as the
-        # oldest one's frames have been collected
-        clock = time.perf_counter
-        i = 0
-        while i < n:
-            k = min(batch, n - i)
-            if ctx.pending() + k > V.QUEUE_DEPTH * batch:
-                c0 = clock()
-                for _ in range(batch):
-                    ctx.collect()
-                host["collect"] += clock() - c0
-            c0 = clock()
-            if batch == 1:
-                r, d = pairs[i % len(pairs)]
-                ctx.submit(r, d)
-            else:
-                sel = [ptrs[(i + j) % len(ptrs)] for j in range(k)]
-                rc = _lib.vif_submit_batch(ctx._ctx, [a for a, _ in sel],
-                                           [b for _, b in sel])
-                if rc != 0:
-                    raise V.VifError(rc, "vif_submit_batch")
-            host["submit"] += clock() - c0
-            i += k
-        while ctx.pending():
-            ctx.collect()
-
-    run(warmup)
+    ctx = V.Vif(w, h, bpc, max_batch=batch)
     ctx.set_profiling(prof_kinds)
-    host["submit"] = host["collect"] = 0.0
+    nf = len(ptrs)
+    pending = collections.deque()  # frame index of every pending frame
+    outputs = {}
+    state = {"next": 0, "submit": 0.0, "collect": 0.0}
+    clock = time.perf_counter
+
+    def submit():
+        idx = [(state["next"] + j) % nf for j in range(batch)]
+        state["next"] = (state["next"] + batch) % nf
+        c0 = clock()
+        if batch == 1:
+            rc = _lib.vif_submit(ctx._ctx, *ptrs[idx[0]])
+        else:
+            rc = _lib.vif_submit_batch(ctx._ctx, [ptrs[i][0] for i in idx],
+                                       [ptrs[i][1] for i in idx])
+        state["submit"] += clock() - c0
+        if rc != 0:
+            raise V.VifError(rc, "vif_submit_batch")
+        pending.extend(idx)
+
+    def collect():
+        c0 = clock()
+        got = [ctx.collect() for _ in range(batch)]
+        state["collect"] += clock() - c0
+        for out in got:
+            outputs.setdefault(pending.popleft(), set()).add(out.tobytes())
+
+    depth = V.QUEUE_DEPTH
+    warm0 = clock()
+    warm_run = 0
+    while warm_run < warmup or clock() - warm0 < settle_s:
+        if len(pending) == depth * batch:
+            collect()
+        submit()
+        warm_run += 1
+    while len(pending) < depth * batch:
+        submit()
+    k0 = ctx.kernel_times()
+    state["submit"] = state["collect"] = 0.0
+    seconds = []
+    for _ in range(reps):
+        t0 = clock()
+        for _ in range(steps):
+            collect()
+            submit()
+        seconds.append(clock() - t0)
+    k1 = ctx.kernel_times()
+    host = {"submit": 1e6 * state["submit"] / (reps * steps * batch),
+            "collect": 1e6 * state["collect"] / (reps * steps * batch)}
+    while pending:
+        collect()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(steps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kt = ctx.kernel_times()
-    kt["_host_submit_us"] = 1e6 * host["submit"] / max(steps, 1)
-    kt["_host_collect_us"] = 1e6 * host["collect"] / max(steps, 1)
     ctx.close()
-    return (t1 - t0), kt
+    kernel = {k: (k1[k][0] - k0[k][0], k1[k][1] - k0[k][1]) for k in k1}
+    return {"seconds": seconds, "kernel": kernel, "host_us": host,
+            "outputs": outputs, "warmup_run": warm_run}
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def rate(res, steps, batch):
+    """Frames/s of the median repetition."""
+    return steps * batch / median(res["seconds"])
 
 
 def time_fssim(V, frames, w, h, bpc, steps, warmup, prof_kinds=0, batch=1):
-    """The float SSIM queue over resident frames, as time_frames does for
-    VIF, `batch` frames per submission.  Returns (seconds, kernel times,
-    geometry)."""
+    """The float SSIM queue over resident frames, timed in steady state as
+    steady_state() times VIF: the queue is full at t0, and the region counts
+    `steps` frames' completions (steps a multiple of `batch`).  Returns
+    (seconds, kernel times, geometry)."""
     import torch
-    dev = torch.device("cuda:0")
-
-    def td(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            a = a.view(np.int16)
-        return torch.from_numpy(a).to(dev)
-
-    pairs = [(td(r), td(d)) for (r, d, _) in frames]
+    pairs = _device_pairs(frames)
     ctx = V.FloatSsim(w, h, bpc, max_batch=batch)
-
-    def run(n):
-        i = 0
-        while i < n:
-            k = min(batch, n - i)
-            if ctx.pending() + k > V.FSSIM_QUEUE_DEPTH * batch:
-                for _ in range(batch):
-                    ctx.collect()
-            sel = [pairs[(i + j) % len(pairs)] for j in range(k)]
-            if batch == 1:
-                ctx.submit(*sel[0])
-            else:
-                ctx.submit_batch([a for a, _ in sel], [b for _, b in sel])
-            i += k
-        while ctx.pending():
-            ctx.collect()
-
-    run(warmup)
     ctx.set_profiling(prof_kinds)
-    torch.cuda.synchronize()
+    state = {"next": 0}
+
+    def submit():
+        sel = [pairs[(state["next"] + j) % len(pairs)] for j in range(batch)]
+        state["next"] += batch
+        if batch == 1:
+            ctx.submit(*sel[0])
+        else:
+            ctx.submit_batch([a for a, _ in sel], [b for _, b in sel])
+
+    full = V.FSSIM_QUEUE_DEPTH * batch
+    for _ in range(max(warmup // batch, 1)):
+        if ctx.pending() == full:
+            for _ in range(batch):
+                ctx.collect()
+        submit()
+    while ctx.pending() < full:
+        submit()
+    k0 = ctx.kernel_times()
     t0 = time.perf_counter()
-    run(steps)
-    torch.cuda.synchronize()
+    for _ in range(max(steps // batch, 1)):
+        for _ in range(batch):
+            ctx.collect()
+        submit()
     t1 = time.perf_counter()
-    kt = ctx.kernel_times()
+    k1 = ctx.kernel_times()
+    while ctx.pending():
+        ctx.collect()
+    torch.cuda.synchronize()
     geom = ctx.geometry()
     ctx.close()
+    kt = {k: (k1[k][0] - k0[k][0], k1[k][1] - k0[k][1]) for k in k1}
     return (t1 - t0), kt, geom
 
 
@@ -436,18 +491,19 @@ def cpu_baseline_all_cores(budget_s=12.0, procs=None):
     return sum(n / t for n, t in res), procs
 
 
-def cpu_baseline(frames, budget_s=12.0):
+def cpu_baseline(frames, budget_s=40.0):
+    """The oracle, single-threaded, over the frames in order (one pass,
+    stopping early once budget_s is spent).  Returns (frames/s, the oracle's
+    out[8] of each frame scored, seconds)."""
     import oracle
-    n = 0
+    outs = []
     t0 = time.perf_counter()
-    while True:
-        r, d, b = frames[n % len(frames)]
-        oracle.score(r, d, b)
-        n += 1
+    for r, d, b in frames:
+        outs.append(oracle.score(r, d, b)[0])
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return n / dt, n, dt
+    return len(outs) / dt, outs, dt
 
 
 def main():
@@ -456,6 +512,9 @@ def main():
     ap.add_argument("--steps", type=int, default=150,
                     help="timed steps; a step is one batch of --batch frames")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed repetitions of --steps steps each; the "
+                    "median one gives the value")
     ap.add_argument("--frames", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-1080p", type=int, default=500)
@@ -504,16 +563,16 @@ def main():
     if not 1 <= batch <= V.MAX_BATCH:
         print("--batch must be 1..%d" % V.MAX_BATCH, file=sys.stderr)
         sys.exit(2)
+    reps = args.reps
     if args.mode == "frames" and args.workload == "1080p10":
         frames = synth.checker_1080p_10bit()
-        nframes = args.steps * batch
-        dt, kt = time_frames(V, frames, 1920, 1080, 10, nframes,
-                             args.warmup * batch, prof_kinds=["scale0"],
-                             batch=batch)
-        s0_ms, s0_n = kt["scale0"]
+        res = steady_state(V, frames, 1920, 1080, 10, args.steps, args.warmup,
+                           batch=batch, reps=reps, prof_kinds=["scale0"])
+        s0_ms, s0_n = res["kernel"]["scale0"]
         print("1080p 10-bit: %.1f frames/s, %.3f ms/step of %d frames; "
               "scale-0 kernel %.1f us per launch"
-              % (nframes / dt, 1000.0 * dt / args.steps, batch,
+              % (rate(res, args.steps, batch),
+                 1000.0 * median(res["seconds"]) / args.steps, batch,
                  1000.0 * s0_ms / max(s0_n, 1)), file=sys.stderr, flush=True)
         return
 
@@ -530,60 +589,58 @@ def main():
               flush=True)
         return
 
-    nframes = args.steps * batch
-    dt, kt = time_frames(V, frames4k, w, h, bpc, nframes,
-                         args.warmup * batch, prof_kinds=["scale0"],
-                         batch=batch)
-    fps = nframes / dt
-    ms_step = 1000.0 * dt / args.steps
-    s0_ms, s0_n = kt["scale0"]
+    # the headline: steps of `batch` frames, median of the repetitions
+    main_res = steady_state(V, frames4k, w, h, bpc, args.steps, args.warmup,
+                            batch=batch, reps=reps, prof_kinds=["scale0"])
+    fps = rate(main_res, args.steps, batch)
+    ms_step = 1000.0 * median(main_res["seconds"]) / args.steps
+    s0_ms, s0_n = main_res["kernel"]["scale0"]
     s0_avg_ms = s0_ms / max(s0_n, 1)
-    print("4K: %.1f frames/s, %.3f ms/step of %d frames; scale-0 kernel "
-          "%.1f us per launch" % (fps, ms_step, batch, 1000 * s0_avg_ms),
-          file=sys.stderr, flush=True)
+    print("4K: %.1f frames/s (repetitions: %s), %.3f ms/step of %d frames; "
+          "scale-0 kernel %.1f us per launch"
+          % (fps, ", ".join("%.1f" % (args.steps * batch / t)
+                            for t in main_res["seconds"]),
+             ms_step, batch, 1000 * s0_avg_ms), file=sys.stderr, flush=True)
     if args.mode == "frames":
         return
 
     # one frame per submission (the pages' per-frame call), same frames
-    dt1, kt1 = time_frames(V, frames4k, w, h, bpc, 500, 20,
-                           prof_kinds=["scale0"])
-    fps_one = 500 / dt1
-    s0_one_ms = kt1["scale0"][0] / max(kt1["scale0"][1], 1)
-
-    host_submit_us = kt1["_host_submit_us"]
-    host_collect_us = kt1["_host_collect_us"]
+    one = steady_state(V, frames4k, w, h, bpc, 500, 20, reps=3,
+                       prof_kinds=["scale0"])
+    fps_one = rate(one, 500, 1)
+    s0_one_ms = one["kernel"]["scale0"][0] / max(one["kernel"]["scale0"][1],
+                                                 1)
+    print("4K one frame per submission: %.1f frames/s" % fps_one,
+          file=sys.stderr, flush=True)
     iso_s0_us = isolated_scale0_us(V, frames4k, w, h, bpc)
 
     # per-kernel split (all kinds timed; separate run, not the headline)
-    _, kt_all = time_frames(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
-                            prof_kinds=0x1F)
+    allk = steady_state(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
+                        batch=batch, reps=1, prof_kinds=0x1F)
     split = {k: round(1000.0 * v[0] / max(v[1], 1), 2)
-             for k, v in kt_all.items() if not k.startswith("_")}
+             for k, v in allk["kernel"].items()}
 
-    # 1080p (10-bit checkerboard workload) for the metric's second size
+    # 1080p (10-bit checkerboard workload) for the metric's second size, and
+    # the bright 16-bit pairs of the same size; 576x324
     f1080 = synth.checker_1080p_10bit()
-    dt1080, kt1080 = time_frames(V, f1080, 1920, 1080, 10, args.steps_1080p,
-                                 10)
-    fps1080 = args.steps_1080p / dt1080
-    # and the bright 16-bit pairs of the same size
+    r1080 = steady_state(V, f1080, 1920, 1080, 10, args.steps_1080p, 10,
+                         reps=3)
     f1080b = synth.bright_1080p_16bit()
-    dt1080b, _ = time_frames(V, f1080b, 1920, 1080, 16, args.steps_1080p, 10)
-    fps1080b = args.steps_1080p / dt1080b
-
-    # 576x324 (the launch-bound small frame) and 4K fed from host memory
+    r1080b = steady_state(V, f1080b, 1920, 1080, 16, args.steps_1080p, 10,
+                          reps=3)
     fsmall = synth.netflix_576x324_8bit()
-    dts, kts = time_frames(V, fsmall, 576, 324, 8, 2000, 50)
-    fps_small = 2000 / dts
+    rsmall = steady_state(V, fsmall, 576, 324, 8, 2000, 50, reps=3)
 
     # batched submissions: each kernel launched once for several frames
     batched = {}
     for key, fr, bw, bh, bb, nb, steps in (
-            ("1080p_10bit_batch8", f1080, 1920, 1080, 10, 8, 3000),
-            ("1080p_16bit_batch8", f1080b, 1920, 1080, 16, 8, 3000),
-            ("576x324_8bit_batch16", fsmall, 576, 324, 8, 16, 8000)):
-        dtb, _ = time_frames(V, fr, bw, bh, bb, steps, 4 * nb, batch=nb)
-        batched[key] = round(steps / dtb, 1)
+            ("1080p_10bit_batch8", f1080, 1920, 1080, 10, 8, 375),
+            ("1080p_16bit_batch8", f1080b, 1920, 1080, 16, 8, 375),
+            ("576x324_8bit_batch16", fsmall, 576, 324, 8, 16, 500)):
+        rb = steady_state(V, fr, bw, bh, bb, steps, 4, batch=nb, reps=3)
+        batched[key] = round(rate(rb, steps, nb), 1)
     fps_host = time_host_frames(V, frames4k, w, h, bpc, 200, 10)
+    print("side figures done", file=sys.stderr, flush=True)
 
     # float SSIM with its exact decimation, on the same 4K frames and on the
     # 1080p 10-bit frames
@@ -597,11 +654,23 @@ def main():
     peak = VALU_PEAK_OPS / 1e12
     traffic, frame_bytes = load_traffic(batch)
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
-                "peak": round(peak, 2), "unit": "TFLOP/s",
+                "peak": round(peak, 2), "unit": "Top/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
     pops = path_ops(w, h)
-    extra = {"scale0_ops_per_pixel": {
+    extra = {"timing": {
+                 "repetitions": reps,
+                 "frames_per_s_each": [round(args.steps * batch / t, 1)
+                                       for t in main_res["seconds"]],
+                 "warmup_steps_run": main_res["warmup_run"],
+                 "method": "untimed warm-up of at least `warmup` steps and "
+                           "0.25 s; queue full at t0; each repetition counts "
+                           "exactly `steps` submission completions in "
+                           "steady state; value = median repetition"},
+             "roofline_unit_note": "plain IEEE operations per second "
+                                   "(multiplies, adds, compares, selects, "
+                                   "conversions), not fused flops",
+             "scale0_ops_per_pixel": {
                  "filter_and_decimation": FILTER_OPS_PER_PIXEL_SCALE0,
                  "statistic": STAT_OPS_PER_PIXEL},
              "scale0_frac_filter_ops_only": round(
@@ -609,14 +678,13 @@ def main():
              "fps_4k_one_frame_per_submission": round(fps_one, 1),
              "scale0_frac_one_frame_per_submission": round(
                  ops / (s0_one_ms / 1000.0) / VALU_PEAK_OPS, 4),
-             "fps_1080p_10bit": round(fps1080, 1),
-             "fps_1080p_16bit": round(fps1080b, 1),
-             "fps_576x324_8bit": round(fps_small, 1),
+             "fps_1080p_10bit": round(rate(r1080, args.steps_1080p, 1), 1),
+             "fps_1080p_16bit": round(rate(r1080b, args.steps_1080p, 1), 1),
+             "fps_576x324_8bit": round(rate(rsmall, 2000, 1), 1),
              "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
              "fps_batched": batched,
              "host_us_per_frame_576x324": {
-                 "submit": round(kts["_host_submit_us"], 2),
-                 "collect": round(kts["_host_collect_us"], 2)},
+                 k: round(v, 2) for k, v in rsmall["host_us"].items()},
              "kernel_avg_us_4k": split,
              "scale0_launch_avg_us": round(1000 * s0_avg_ms, 2),
              "scale0_frames_per_launch": batch,
@@ -625,11 +693,10 @@ def main():
                  ops / (iso_s0_us * 1e-6) / VALU_PEAK_OPS, 4),
              "path_ops_per_frame": pops,
              "path_frac_of_valu_peak": round(pops * fps / VALU_PEAK_OPS, 4),
-             "host_us_per_frame_4k": {"submit": round(host_submit_us, 2),
-                                      "collect": round(host_collect_us, 2)},
+             "host_us_per_frame_4k": {
+                 k: round(v, 2) for k, v in one["host_us"].items()},
              "host_us_per_frame_1080p": {
-                 "submit": round(kt1080["_host_submit_us"], 2),
-                 "collect": round(kt1080["_host_collect_us"], 2)},
+                 k: round(v, 2) for k, v in r1080["host_us"].items()},
              "fssim": fssim}
     if frame_bytes:
         gbs = frame_bytes * fps / 1e9
@@ -643,14 +710,34 @@ def main():
             "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "frame_bytes": fb1080}
 
+    # every timed frame gave one output, the same every time it was scored
+    stable = all(len(v) == 1 for v in main_res["outputs"].values())
     cpu = None
+    parity_fail = False
     if not args.no_cpu_baseline:
-        cfps, cn, cdt = cpu_baseline(frames4k)
+        cfps, ref_outs, cdt = cpu_baseline(frames4k)
+        cn = len(ref_outs)
         cpu = {"value": round(cfps, 4), "unit": "frames/s", "cores": 1,
                "kind": "oracle",
-               "sample": "%d of the 3840x2160 8-bit frame pairs, single "
-                         "thread, %.1f s" % (cn, cdt)}
+               "sample": "frames 0..%d of the 3840x2160 8-bit frame pairs "
+                         "the GPU timed, one pass, single thread, %.1f s"
+                         % (cn - 1, cdt)}
         extra["cpu_oracle_all_cores"] = cpu_all
+        # the GPU's outputs of the same frames, from the timed loop
+        maxd, same = 0.0, stable
+        for i, want in enumerate(ref_outs):
+            for got_b in main_res["outputs"].get(i, ()):
+                got = np.frombuffer(got_b, dtype=np.float64)
+                maxd = max(maxd, float(np.max(np.abs(got - want))))
+                same = same and got.tobytes() == want.tobytes()
+            if i not in main_res["outputs"]:
+                same = False
+        extra["parity_vs_oracle"] = {
+            "frames": cn, "bit_identical": bool(same),
+            "max_abs_diff": maxd, "gate": PARITY_GATE}
+        parity_fail = not maxd <= PARITY_GATE
+    else:
+        extra["outputs_stable_across_repeats"] = stable
 
     line = {
         "metric": METRIC,
@@ -677,6 +764,10 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    if parity_fail:
+        print("PARITY FAILURE: the GPU's outputs differ from the oracle's by "
+              "more than %g" % PARITY_GATE, file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -749,3 +749,38 @@ def test_batch_profiling_counts_one_launch_per_kind(V):
     t = ctx.kernel_times()
     assert [t[k][1] for k in V.KERNEL_KINDS] == [2] * 5
     ctx.close()
+
+
+def test_4k_every_frame_bench_configuration(V, orc):
+    """Every frame of the 3840x2160 1/f workload (20 pairs), as the benchmark
+    scores them: submissions of four frames (each kernel launched once for
+    the four) through the full three-slot queue.  Every frame's out[8], its
+    eight sums and all 4050 row sums equal the oracle's bit for bit
+    (ADR-1422, Consequences: every output of every frame equals the CPU's).
+    The oracle runs in threads (its C calls release the interpreter)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from vif_image_fidelity_amd import synth
+    frames = synth.pink_4k_8bit(frames=20)
+    print("oracle on 20 frames of pink_4k_8bit", flush=True)
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        exps = list(ex.map(lambda f: orc.score(f[0], f[1], f[2],
+                                               want_rows=True), frames))
+    dev = [(to_device(r), to_device(d)) for r, d, _ in frames]
+    ctx = V.Vif(3840, 2160, 8, max_batch=4)
+    nxt = 0
+    for k in range(len(frames)):
+        while nxt < len(frames) and ctx.pending() + 4 <= 4 * V.QUEUE_DEPTH:
+            sel = dev[nxt:nxt + 4]
+            ctx.submit_batch([a for a, _ in sel], [b for _, b in sel])
+            nxt += 4
+        got = ctx.collect()
+        exp, esums, erows = exps[k]
+        print("pink_4k_8bit[%d] collected" % k, flush=True)
+        _check_outputs(got, exp, "pink_4k_8bit[%d]" % k)
+        assert ctx.sums().view(np.uint32).tolist() == \
+            esums.view(np.uint32).tolist(), k
+        bad = np.nonzero(ctx.row_sums().view(np.uint32) !=
+                         erows.view(np.uint32))
+        assert bad[0].size == 0, (k, bad[0][:10])
+    assert ctx.pending() == 0
+    ctx.close()
