@@ -92,6 +92,11 @@ HBM_PEAK_GBS = 8000.0
 # (ADR-1422 and ADR-1444, Context).  Bit identity is reported beside it.
 PARITY_GATE = 5e-5
 
+# One device's share when 3840x2160 frames are split in eight row strips on
+# 272-row boundaries (strip boundaries fall on multiples of 8 rows): rows
+# 272..543, read with their halo as input rows 248..556.
+STRIP_SHARE = (272, 544)
+
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scale0_4k.json")
 PROFILE_TRAFFIC_1080P = os.path.join(ROOT, "profiles", "traffic_1080p_10bit.json")
 
@@ -157,7 +162,7 @@ def _device_pairs(frames):
 
 
 def steady_state(V, frames, w, h, bpc, steps, warmup, batch=1, reps=5,
-                 prof_kinds=0, settle_s=0.25):
+                 prof_kinds=0, settle_s=0.25, strip=None):
     """Scores the resident frames (cycling over them) through one context's
     queue, `batch` frames per submission (each kernel launched once for the
     batch), and times the queue in steady state.
@@ -177,6 +182,10 @@ def steady_state(V, frames, w, h, bpc, steps, warmup, batch=1, reps=5,
     region covers `steps` submission completions of a pipeline that neither
     fills nor drains inside it.
 
+    strip: None, or (row0, row1): a strip context (vif_create_strip) fed
+    the strip's input rows of each frame, one device's share of a frame
+    split by rows.
+
     Returns {"seconds": [per repetition], "kernel": {kind: (ms, launches)}
     over the timed repetitions, "host_us": per-frame host time of submit and
     collect calls, "outputs": {frame index: set of out[8] byte strings},
@@ -184,8 +193,10 @@ def steady_state(V, frames, w, h, bpc, steps, warmup, batch=1, reps=5,
     import torch
     from vif_image_fidelity_amd import _lib
     pairs = _device_pairs(frames)
+    ctx = V.Vif(w, h, bpc, max_batch=batch, strip=strip)
+    a, b = ctx.in0, ctx.in0 + ctx.in_rows
+    pairs = [(r[a:b], d[a:b]) for r, d in pairs]
     ptrs = [(r.data_ptr(), d.data_ptr()) for r, d in pairs]
-    ctx = V.Vif(w, h, bpc, max_batch=batch)
     ctx.set_profiling(prof_kinds)
     nf = len(ptrs)
     pending = collections.deque()  # frame index of every pending frame
@@ -524,10 +535,14 @@ def main():
     ap.add_argument("--workload", choices=["4k", "1080p10"], default="4k",
                     help="frames mode only: the 3840x2160 8-bit frames, or "
                     "the 1920x1080 10-bit checkerboard pairs")
-    ap.add_argument("--mode", choices=["full", "frames", "copy", "fssim"],
+    ap.add_argument("--mode", choices=["full", "frames", "strip", "copy",
+                                       "fssim"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
-                    "loop (for profiler runs); copy: a plain device copy of "
+                    "loop (for profiler runs); strip: the same for one "
+                    "device's share of 4K frames split in eight row strips "
+                    "(rows 272..543, 309 input rows); copy: a plain device "
+                    "copy of "
                     "known size (counter calibration); fssim: only the 4K "
                     "float SSIM loop (for profiler runs)")
     args = ap.parse_args()
@@ -589,6 +604,17 @@ def main():
               flush=True)
         return
 
+    if args.mode == "strip":
+        res = steady_state(V, frames4k, w, h, bpc, args.steps, args.warmup,
+                           batch=batch, reps=reps, prof_kinds=0x1F,
+                           strip=STRIP_SHARE)
+        kt = {k: round(1000.0 * v[0] / max(v[1], 1), 2)
+              for k, v in res["kernel"].items()}
+        print("4K strip share %s: %.1f shares/s, kernels (us per launch of "
+              "%d): %s" % (STRIP_SHARE, rate(res, args.steps, batch), batch,
+                           kt), file=sys.stderr, flush=True)
+        return
+
     # the headline: steps of `batch` frames, median of the repetitions
     main_res = steady_state(V, frames4k, w, h, bpc, args.steps, args.warmup,
                             batch=batch, reps=reps, prof_kinds=["scale0"])
@@ -640,6 +666,17 @@ def main():
         rb = steady_state(V, fr, bw, bh, bb, steps, 4, batch=nb, reps=3)
         batched[key] = round(rate(rb, steps, nb), 1)
     fps_host = time_host_frames(V, frames4k, w, h, bpc, 200, 10)
+    # one device's share of 4K frames split in eight row strips
+    rstrip = steady_state(V, frames4k, w, h, bpc, 100, 5, batch=batch,
+                          reps=3, prof_kinds=["scale0"], strip=STRIP_SHARE)
+    sg = V.strip_geometry(w, h, *STRIP_SHARE)
+    strip_leg = {
+        "strip_rows": list(STRIP_SHARE), "input_rows": sg["in_rows"],
+        "frames_per_submission": batch,
+        "shares_per_s": round(rate(rstrip, 100, batch), 1),
+        "scale0_launch_avg_us": round(
+            1000.0 * rstrip["kernel"]["scale0"][0] /
+            max(rstrip["kernel"]["scale0"][1], 1), 2)}
     print("side figures done", file=sys.stderr, flush=True)
 
     # float SSIM with its exact decimation, on the same 4K frames and on the
@@ -683,6 +720,7 @@ def main():
              "fps_576x324_8bit": round(rate(rsmall, 2000, 1), 1),
              "fps_4k_host_frames_pinned_pcie": round(fps_host, 1),
              "fps_batched": batched,
+             "strip_share_4k": strip_leg,
              "host_us_per_frame_576x324": {
                  k: round(v, 2) for k, v in rsmall["host_us"].items()},
              "kernel_avg_us_4k": split,

@@ -188,6 +188,62 @@ vif_ctx *vif_create_batch(int w, int h, int bpc, const vif_options *opt,
 int vif_submit_batch(vif_ctx *ctx, int n, const void *const *refs,
                      const void *const *dists);
 
+/*
+ * Row strips: one device's share of a frame split by rows across devices.
+ * Every device scores its strip of every frame with no exchange; the host
+ * concatenates the strips' row sums and adds them as for a whole frame.  The
+ * bits are the whole frame's: the device returns each row's fp32 sum and the
+ * host adds the rows top to bottom (ADR-1422 "float_vif_sycl computes the
+ * CPU's arithmetic ...", Decision), so whole rows of disjoint strips,
+ * concatenated, are the frame's rows; and each strip recomputes the rows
+ * around it that its own rows depend on, mirroring only at the frame's top
+ * and bottom (ADR-1444 "float_vif_hip runs the arithmetic of the CUDA twin
+ * ...", Decision: indices reflect at the plane's edges, then clamp).
+ *
+ * A strip is scale-0 rows [row0, row1) of a w x h frame: row0 a multiple
+ * of 8 with 0 <= row0 < row1, row1 a multiple of 8 or h, row1 <= h.  It
+ * owns rows [row0 >> s, row1 >> s) of scale s's plane (floor(h / 2^s) rows;
+ * the strip ending at h owns the plane's remaining rows), so strips that
+ * tile [0, h) tile every scale's rows.
+ *
+ * vif_strip_geometry -- host only.  Writes info[0] = in0, the first frame
+ * row the strip reads, max(0, row0 - 24); info[1] = the rows it reads,
+ * min(h, row1 + 13) - in0; and for s = 0..3 info[2 + 2s] = the first row
+ * it owns at scale s (in the frame's plane), info[3 + 2s] = how many (0 is
+ * possible at the coarse scales of a strip of fewer than 8 rows at the
+ * bottom).  The reach is 20 rows up and 13 down, the filter radii 8/4/2/1
+ * carried through the decimations; in0 is rounded down to a multiple of 8
+ * so that every scale's planes start on one of the frame's rows.  VIF_OK,
+ * or VIF_EINVAL for a geometry vif_create refuses or a strip outside the
+ * rules above.
+ *
+ * vif_create_strip -- vif_create_batch for the strip of w x h frames.  The
+ * frames given to vif_score, vif_submit, vif_submit_batch and
+ * vif_submit_host are the strip's input rows: info[1] rows of w samples,
+ * starting at frame row info[0] (a pointer to the frame plus in0 * w
+ * samples).  The outputs cover the strip's own rows only: out[8] and
+ * vif_get_sums are the scores and fp32 sums of those rows, and
+ * vif_get_row_sums returns them scale by scale (scale 0's own rows, then
+ * scale 1's, ...; the total own rows is its return value).  A strip of
+ * [0, h) is the whole frame: the same as vif_create_batch.
+ *
+ * vif_scores_from_rows -- host only.  The outputs of a w x h frame from
+ * its row sums: rows holds, for scale s = 0..3 and each row y of that scale
+ * (h >> s rows), the pair n_y, d_y -- what vif_get_row_sums returns for a
+ * whole frame, or the strips' vif_get_row_sums concatenated scale by scale
+ * in row order.  Each scale's rows are added top to bottom in fp32, and
+ * out[8] is formed as vif_score forms it, with the options opt (NULL: the
+ * defaults; skip_scale0 ignores scale 0's rows).  sums (may be NULL)
+ * receives the eight fp32 sums.  VIF_OK or VIF_EINVAL.
+ */
+#define VIF_STRIP_INFO 10
+int vif_strip_geometry(int w, int h, int row0, int row1,
+                       int info[VIF_STRIP_INFO]);
+vif_ctx *vif_create_strip(int w, int h, int bpc, const vif_options *opt,
+                          int max_batch, int row0, int row1);
+int vif_scores_from_rows(int w, int h, const vif_options *opt,
+                         const float *rows, double out[8], float sums[8]);
+
 /* vif_pending -- frames submitted and not yet collected (or VIF_EINVAL). */
 int vif_pending(const vif_ctx *ctx);
 
@@ -233,10 +289,11 @@ int vif_get_debug(const vif_ctx *ctx, double out[VIF_NDEBUG]);
 /*
  * vif_get_row_sums -- the per-row fp32 sums of the last frame returned by
  * vif_score or vif_collect, as they came back from the device: for scale
- * 0..3, for row
- * y = 0..h_s-1, the pair (n_y, d_y).  rows must hold 2 * capacity floats.
- * Returns the total number of rows (h_0 + h_1 + h_2 + h_3) when capacity
- * is large enough, else VIF_EINVAL.  Plane heights halve with floor.
+ * 0..3, for row y = 0..h_s-1, the pair (n_y, d_y) (a strip context: its own
+ * rows of each scale, see vif_create_strip).  rows must hold 2 * capacity
+ * floats.  Returns the total number of rows (h_0 + h_1 + h_2 + h_3, plane
+ * heights halving with floor) when capacity is large enough, else
+ * VIF_EINVAL.
  */
 int vif_get_row_sums(const vif_ctx *ctx, float *rows, int capacity);
 

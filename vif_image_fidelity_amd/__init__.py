@@ -23,6 +23,7 @@ from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
                    FSSIM_QUEUE_DEPTH, FSSIM_MAX_PIXELS, FSSIM_MAX_FACTOR)
 
 __all__ = ["Vif", "VifError", "FloatSsim", "fssim_taps", "taps",
+           "strip_geometry", "scores_from_rows",
            "make_options", "DEFAULT_OPTIONS",
            "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
            "KERNEL_KINDS", "QUEUE_DEPTH", "MAX_BATCH", "MIN_SIDE",
@@ -82,10 +83,24 @@ class Vif:
     """One scoring context for w x h frames of bpc bits (8, 10, 12, 16).
     options: None or a dict of overrides of DEFAULT_OPTIONS."""
 
-    def __init__(self, w, h, bpc, stream=None, options=None, max_batch=1):
+    def __init__(self, w, h, bpc, stream=None, options=None, max_batch=1,
+                 strip=None):
+        """strip: None, or (row0, row1) for a context that scores scale-0
+        rows [row0, row1) of w x h frames (vif_create_strip): its frames are
+        the strip's input rows, shape (in_rows, w) from input row in0
+        (strip_geometry), and its outputs cover its own rows."""
         self.w, self.h, self.bpc = int(w), int(h), int(bpc)
         self.max_batch = int(max_batch)
-        if self.max_batch != 1:
+        self.strip = None if strip is None else tuple(int(r) for r in strip)
+        self.in0, self.in_rows = 0, self.h
+        if self.strip is not None:
+            g = strip_geometry(self.w, self.h, *self.strip)
+            self.in0, self.in_rows = g["in0"], g["in_rows"]
+            ctx = _lib.vif_create_strip(
+                self.w, self.h, self.bpc,
+                None if options is None else make_options(options),
+                self.max_batch, *self.strip)
+        elif self.max_batch != 1:
             ctx = _lib.vif_create_batch(
                 self.w, self.h, self.bpc,
                 None if options is None else make_options(options),
@@ -102,7 +117,10 @@ class Vif:
         # until their collect() returns, so the memory of a temporary frame
         # is not reused while the kernels still read it
         self._inflight = collections.deque()
-        self.total_rows = sum((self.h >> s) for s in range(4))
+        if self.strip is None:
+            self.total_rows = sum((self.h >> s) for s in range(4))
+        else:
+            self.total_rows = sum(g["own_rows"])
         if stream is not None:
             self.set_stream(stream)
 
@@ -115,9 +133,9 @@ class Vif:
 
     def _check_frame(self, t):
         if hasattr(t, "shape"):
-            if tuple(t.shape) != (self.h, self.w):
+            if tuple(t.shape) != (self.in_rows, self.w):
                 raise ValueError("frame shape %s, context is (%d, %d)"
-                                 % (tuple(t.shape), self.h, self.w))
+                                 % (tuple(t.shape), self.in_rows, self.w))
             want = 1 if self.bpc == 8 else 2
             if t.element_size() != want:
                 raise ValueError("bpc %d needs %d-byte samples"
@@ -148,9 +166,9 @@ class Vif:
             raise TypeError("expected a numpy array or a CPU tensor")
         if not a.flags["C_CONTIGUOUS"]:
             raise ValueError("frames must be contiguous")
-        if a.shape != (self.h, self.w):
+        if a.shape != (self.in_rows, self.w):
             raise ValueError("frame shape %s, context is (%d, %d)"
-                             % (a.shape, self.h, self.w))
+                             % (a.shape, self.in_rows, self.w))
         if a.dtype != (np.uint8 if self.bpc == 8 else np.uint16):
             raise ValueError("bpc %d needs %s samples"
                              % (self.bpc, "uint8" if self.bpc == 8
@@ -289,6 +307,37 @@ class Vif:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def strip_geometry(w, h, row0, row1):
+    """The rows a strip of scale-0 rows [row0, row1) of w x h frames reads
+    and owns (vif_strip_geometry): {"in0", "in_rows", "own0": [4],
+    "own_rows": [4]}."""
+    info = np.zeros(_lib.STRIP_INFO, dtype=np.int32)
+    rc = _lib.vif_strip_geometry(w, h, row0, row1, info)
+    if rc != VIF_OK:
+        raise VifError(rc, "vif_strip_geometry")
+    return {"in0": int(info[0]), "in_rows": int(info[1]),
+            "own0": [int(v) for v in info[2::2]],
+            "own_rows": [int(v) for v in info[3::2]]}
+
+
+def scores_from_rows(w, h, rows, options=None):
+    """out[8] and the eight fp32 sums of a w x h frame from its row sums
+    (vif_scores_from_rows): rows is (h + h/2 + h/4 + h/8, 2) float32, scale
+    by scale, top to bottom."""
+    rows = np.ascontiguousarray(rows, dtype=np.float32)
+    need = sum(int(h) >> s for s in range(4))
+    if rows.shape != (need, 2):
+        raise ValueError("rows must be (%d, 2)" % need)
+    out = np.zeros(8, dtype=np.float64)
+    sums = np.zeros(8, dtype=np.float32)
+    rc = _lib.vif_scores_from_rows(w, h, None if options is None
+                                   else make_options(options), rows, out,
+                                   sums)
+    if rc != VIF_OK:
+        raise VifError(rc, "vif_scores_from_rows")
+    return out, sums
 
 
 def fssim_taps():

@@ -19,6 +19,7 @@ NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
 MAX_BATCH = 16
+STRIP_INFO = 10
 MIN_SIDE = 16
 MAX_PIXELS = 1 << 27
 NDEBUG = 15
@@ -80,6 +81,11 @@ def load():
                              vp),
         "vif_submit_batch": ([vp, ip, ctypes.POINTER(vp),
                               ctypes.POINTER(vp)], ip),
+        "vif_create_strip": ([ip, ip, ip, ctypes.POINTER(VifOptions), ip,
+                              ip, ip], vp),
+        "vif_strip_geometry": ([ip, ip, ip, ip, ctypes.POINTER(ip)], ip),
+        "vif_scores_from_rows": ([ip, ip, ctypes.POINTER(VifOptions), fp, dp,
+                                  fp], ip),
         "vif_default_options": ([ctypes.POINTER(VifOptions)], None),
         "vif_get_options": ([vp, ctypes.POINTER(VifOptions)], ip),
         "vif_get_debug": ([vp, dp], ip),
@@ -136,7 +142,8 @@ def load():
 def exported_symbols():
     """Names of every C function this binding declares."""
     return ["vif_default_options", "vif_create", "vif_create_ex",
-            "vif_create_batch", "vif_submit_batch",
+            "vif_create_batch", "vif_submit_batch", "vif_create_strip",
+            "vif_strip_geometry", "vif_scores_from_rows",
             "vif_get_options", "vif_score", "vif_submit", "vif_collect",
             "vif_submit_host", "vif_score_host",
             "vif_pending", "vif_get_debug",
@@ -178,6 +185,29 @@ def vif_create_batch(w, h, bpc, options, max_batch):
     return load().vif_create_batch(int(w), int(h), int(bpc),
                                    None if options is None
                                    else ctypes.byref(options), int(max_batch))
+
+
+def vif_create_strip(w, h, bpc, options, max_batch, row0, row1):
+    """options: a VifOptions or None (the defaults)."""
+    return load().vif_create_strip(int(w), int(h), int(bpc),
+                                   None if options is None
+                                   else ctypes.byref(options), int(max_batch),
+                                   int(row0), int(row1))
+
+
+def vif_strip_geometry(w, h, row0, row1, info):
+    """info: a contiguous int32 numpy array of STRIP_INFO entries."""
+    return load().vif_strip_geometry(
+        int(w), int(h), int(row0), int(row1),
+        ctypes.cast(info.ctypes.data, ctypes.POINTER(ctypes.c_int)))
+
+
+def vif_scores_from_rows(w, h, options, rows, out, sums):
+    """rows: float32 (h + h/2 + h/4 + h/8, 2); out: float64[8]; sums:
+    float32[8] or None; options: a VifOptions or None."""
+    return load().vif_scores_from_rows(
+        int(w), int(h), None if options is None else ctypes.byref(options),
+        _fptr(rows), _dptr(out), None if sums is None else _fptr(sums))
 
 
 def vif_submit_batch(ctx, ref_ptrs, dist_ptrs):

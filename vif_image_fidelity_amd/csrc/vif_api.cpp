@@ -86,8 +86,16 @@ struct vif_ctx {
   int max_batch = 1;                   // frames one submission may carry
   size_t plane_elems[kScales] = {};    // floats per frame, pyramid plane
   size_t terms_elems[kScales] = {};    // floats per frame, term buffer
-  int total_rows = 0;
+  int total_rows = 0;             // rows of the planes, all scales
   int row_base[kScales] = {};
+  // the rows the context reports: scale s's planes' rows [own0[s],
+  // own0[s] + nown[s]) (all of them for a whole frame; a strip's own rows
+  // for a strip context, whose planes start at input row in0 of the frame)
+  int in0 = 0;
+  int own0[kScales] = {};
+  int nown[kScales] = {};
+  int own_base[kScales] = {};
+  int own_rows = 0;
   int rowsum_waves = 0;
   bool order_scale0 = false; // consecutive frames' scale-0 kernels ordered
   vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
@@ -95,7 +103,7 @@ struct vif_ctx {
   long shead = 0, stail = 0; // submitted / released slot counts
   float sums[8] = {};
   double last_out[8] = {};
-  float *last_rows = nullptr; // host copy of the last collected row sums
+  float *last_rows = nullptr; // the last collected frame's own row sums
   bool have_sums = false;
   int prof_mask = 0;
   double kernel_ms[kKinds] = {};
@@ -262,7 +270,7 @@ int submit_frame(vif_ctx *ctx, const void *ref, const void *dist) {
 // slot's previous frame read those buffers earlier on the same stream.
 int submit_host_frame(vif_ctx *ctx, const void *ref, const void *dist) {
   Slot &sl = ctx->slots[ctx->shead % kDepth];
-  const size_t bytes = static_cast<size_t>(ctx->w) * ctx->h *
+  const size_t bytes = static_cast<size_t>(ctx->w) * ctx->geom[0].h *
                        (ctx->bpc == 8 ? 1 : 2);
   hipError_t e = hipMemcpyAsync(sl.frame_ref, ref, bytes,
                                 hipMemcpyHostToDevice, sl.stream);
@@ -299,63 +307,25 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
       }
     }
   }
+  // the own rows of each scale, in scale order
+  const float *rows = sl.rows_host + static_cast<size_t>(z) * 2 * ctx->total_rows;
+  for (int s = 0; s < kScales; ++s)
+    std::memcpy(ctx->last_rows + 2 * ctx->own_base[s],
+                rows + 2 * (ctx->row_base[s] + ctx->own0[s]),
+                sizeof(float) * 2 * ctx->nown[s]);
   // a skipped scale 0 contributes nothing: its rows read 0 (the kernels
   // still build the pyramid from it)
-  const bool skip0 = ctx->opt.skip_scale0 != 0;
-  std::memcpy(ctx->last_rows,
-              sl.rows_host + static_cast<size_t>(z) * 2 * ctx->total_rows,
-              sizeof(float) * 2 * ctx->total_rows);
-  if (skip0)
-    std::memset(ctx->last_rows, 0, sizeof(float) * 2 * ctx->geom[0].h);
-  float N[kScales], D[kScales];
-  for (int s = 0; s < kScales; ++s) {
-    const float *r = ctx->last_rows + 2 * ctx->row_base[s];
-    float n = 0.0f, d = 0.0f;
-    for (int y = 0; y < ctx->geom[s].h; ++y) {
-      n = n + r[2 * y];
-      d = d + r[2 * y + 1];
-    }
-    N[s] = n;
-    D[s] = d;
-    ctx->sums[2 * s] = n;
-    ctx->sums[2 * s + 1] = d;
-  }
+  if (ctx->opt.skip_scale0 != 0)
+    std::memset(ctx->last_rows, 0, sizeof(float) * 2 * ctx->nown[0]);
+  vifk::scores_from_rows(ctx->last_rows, ctx->nown, ctx->opt, out,
+                         ctx->sums);
   ctx->have_sums = true;
   ctx->tail += 1;
   sl.taken = z + 1;
   if (sl.taken == sl.n)
     ctx->stail += 1;
-  for (int s = 0; s < kScales; ++s)
-    out[s] = static_cast<double>(N[s]) / static_cast<double>(D[s]);
-  if (skip0)
-    out[0] = 0.0;
-  // floors of the reported scores of scales 1..3
-  for (int s = 1; s < kScales; ++s)
-    if (out[s] < ctx->opt.scale_min_val[s - 1])
-      out[s] = ctx->opt.scale_min_val[s - 1];
-  double num = static_cast<double>(N[0]) + static_cast<double>(N[1]);
-  num = num + static_cast<double>(N[2]);
-  num = num + static_cast<double>(N[3]);
-  double den = static_cast<double>(D[0]) + static_cast<double>(D[1]);
-  den = den + static_cast<double>(D[2]);
-  den = den + static_cast<double>(D[3]);
-  out[4] = num;
-  out[5] = den;
-  out[6] = num / den;
-  out[7] = 0.0;
   std::memcpy(ctx->last_out, out, sizeof(ctx->last_out));
   return vifk::set_status(VIF_OK);
-}
-
-bool options_ok(const vif_options &o) {
-  vifk::OptionValues v{};
-  v.sigma_nsq = o.sigma_nsq;
-  v.enhn_gain_limit = o.enhn_gain_limit;
-  v.kernelscale = o.kernelscale;
-  for (int i = 0; i < 3; ++i)
-    v.scale_min_val[i] = o.scale_min_val[i];
-  v.skip_scale0 = o.skip_scale0;
-  return o.reserved == 0 && vifk::options_valid(v);
 }
 
 bool bad_frame_ptrs(const vif_ctx *ctx, const void *ref, const void *dist) {
@@ -392,14 +362,22 @@ vif_create_ex(int w, int h, int bpc, const vif_options *opt) {
 __attribute__((visibility("default"))) vif_ctx *
 vif_create_batch(int w, int h, int bpc, const vif_options *opt,
                  int max_batch) {
+  return vif_create_strip(w, h, bpc, opt, max_batch, 0, h);
+}
+
+__attribute__((visibility("default"))) vif_ctx *
+vif_create_strip(int w, int h, int bpc, const vif_options *opt,
+                 int max_batch, int row0, int row1) {
   vif_options o;
   vif_default_options(&o);
   if (opt != nullptr)
     o = *opt;
+  vifk::StripRows sr;
   if (w < VIF_MIN_SIDE || h < VIF_MIN_SIDE ||
       static_cast<long>(w) * h > VIF_MAX_PIXELS ||
-      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) || !options_ok(o) ||
-      max_batch < 1 || max_batch > VIF_MAX_BATCH) {
+      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16) ||
+      !vifk::options_ok(o) || max_batch < 1 || max_batch > VIF_MAX_BATCH ||
+      !vifk::strip_rows(h, row0, row1, &sr)) {
     vifk::set_status(VIF_EINVAL);
     return nullptr;
   }
@@ -424,7 +402,11 @@ vif_create_batch(int w, int h, int bpc, const vif_options *opt,
     vifk::status_from_hip(e);
     return nullptr;
   }
-  int ws = w, hs = h, rows = 0;
+  // the planes hold the input rows: the whole frame, or a strip's rows
+  // [in0, in0 + in_rows), a multiple of 8 rows below the frame's top, so
+  // that scale s's planes start at the frame's row in0 >> s
+  c->in0 = sr.in0;
+  int ws = w, hs = sr.in_rows, rows = 0, own = 0;
   for (int s = 0; s < kScales; ++s) {
     if (s > 0) {
       ws /= 2;
@@ -437,6 +419,10 @@ vif_create_batch(int w, int h, int bpc, const vif_options *opt,
     g.ntx = (ws + vifk::kTileW - 1) / vifk::kTileW;
     c->row_base[s] = rows;
     rows += hs;
+    c->own0[s] = sr.own0[s] - (sr.in0 >> s);
+    c->nown[s] = sr.nown[s];
+    c->own_base[s] = own;
+    own += sr.nown[s];
     c->plane_elems[s] = static_cast<size_t>(ws) * hs;
     c->terms_elems[s] = static_cast<size_t>(g.strips) *
                         vifk::term_groups(ws) * vifk::kSeq * 4;
@@ -464,8 +450,9 @@ vif_create_batch(int w, int h, int bpc, const vif_options *opt,
         e == hipSuccess && c->geom[0].tiles() >= 2 * static_cast<size_t>(resident);
   }
   c->total_rows = rows;
-  c->last_rows =
-      static_cast<float *>(std::calloc(static_cast<size_t>(2) * rows, 4));
+  c->own_rows = own;
+  c->last_rows = static_cast<float *>(
+      std::calloc(static_cast<size_t>(2) * (own > 0 ? own : 1), 4));
   if (c->last_rows == nullptr)
     e = hipErrorOutOfMemory;
 
@@ -476,7 +463,8 @@ vif_create_batch(int w, int h, int bpc, const vif_options *opt,
       if (e == hipSuccess)
         e = dev_alloc(&sl.pyr_dist[s], nb * c->plane_elems[s]);
     }
-    const size_t frame_bytes = static_cast<size_t>(w) * h * (bpc == 8 ? 1 : 2);
+    const size_t frame_bytes =
+        static_cast<size_t>(w) * sr.in_rows * (bpc == 8 ? 1 : 2);
     if (e == hipSuccess)
       e = hipMalloc(&sl.frame_ref, frame_bytes);
     if (e == hipSuccess)
@@ -650,11 +638,11 @@ vif_get_debug(const vif_ctx *ctx, double out[VIF_NDEBUG]) {
 __attribute__((visibility("default"))) int
 vif_get_row_sums(const vif_ctx *ctx, float *rows, int capacity) {
   if (ctx == nullptr || rows == nullptr || !ctx->have_sums ||
-      capacity < ctx->total_rows)
+      capacity < ctx->own_rows)
     return vifk::set_status(VIF_EINVAL);
-  std::memcpy(rows, ctx->last_rows, sizeof(float) * 2 * ctx->total_rows);
+  std::memcpy(rows, ctx->last_rows, sizeof(float) * 2 * ctx->own_rows);
   vifk::set_status(VIF_OK);
-  return ctx->total_rows;
+  return ctx->own_rows;
 }
 
 __attribute__((visibility("default"))) int vif_taps(int scale, float *taps) {

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct vif_options; // include/vif.h
+
 namespace vifk {
 
 constexpr int kScales = 4;
@@ -95,6 +97,28 @@ struct RowSumArgs {
   int w[kScales], h[kScales], strips[kScales];
   int pair_base[kScales + 1];
 };
+
+// Host arithmetic on row sums (vif_rows.cpp).  scores_from_rows: rows
+// holds nrows[s] pairs (n_y, d_y) for scale 0, then scale 1, ...; writes
+// out[8] and the eight fp32 sums as the context's collect does.
+void scores_from_rows(const float *rows, const int nrows[kScales],
+                      const vif_options &opt, double out[8], float sums[8]);
+// out[8] from the eight fp32 sums N_0, D_0, ..., N_3, D_3 (a skipped scale
+// 0's two are set to 0 in place).
+void scores_from_sums(float sums[8], const vif_options &opt, double out[8]);
+
+// The rows a strip of scale-0 rows [row0, row1) of an h-row frame reads
+// (input rows [in0, in0 + in_rows) of the frame) and owns (rows [own0[s],
+// own0[s] + nown[s]) of the frame's scale-s plane).  False for a strip the
+// boundary does not accept.
+struct StripRows {
+  int in0, in_rows;
+  int own0[kScales], nown[kScales];
+};
+bool strip_rows(int h, int row0, int row1, StripRows *sr);
+
+// The option checks of the C ABI (vif_api.cpp).
+bool options_ok(const vif_options &o);
 
 // Host tap generator (vif_taps.cpp).
 int gaussian_taps(int scale, float *taps);

@@ -8,6 +8,7 @@
 // meaning taken for each is stated in include/vif.h.
 #include <cmath>
 
+#include "../../include/vif.h"
 #include "vif_internal.h"
 
 namespace vifk {
@@ -23,6 +24,17 @@ bool options_valid(const OptionValues &o) {
     if (std::isnan(v))
       return false;
   return o.skip_scale0 == 0 || o.skip_scale0 == 1;
+}
+
+bool options_ok(const vif_options &o) {
+  OptionValues v{};
+  v.sigma_nsq = o.sigma_nsq;
+  v.enhn_gain_limit = o.enhn_gain_limit;
+  v.kernelscale = o.kernelscale;
+  for (int i = 0; i < 3; ++i)
+    v.scale_min_val[i] = o.scale_min_val[i];
+  v.skip_scale0 = o.skip_scale0;
+  return o.reserved == 0 && options_valid(v);
 }
 
 StatArgs make_stat_args(double nsq, double gain_limit) {
