@@ -73,11 +73,16 @@ __device__ __forceinline__ float num_ratio(float a, float sv, double nsq) {
 }
 
 // fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.  For a
-// power-of-two nsq the quotient is the exact product with 1 / nsq.
+// power-of-two nsq (kPow2, sa.inv_nsq = 1 / nsq, not 0) the quotient is the
+// exact product with 1 / nsq.  kPow2 is a compile-time choice: the kernels
+// come in both forms and the host launches the one that matches nsq, so
+// neither carries the other's arithmetic (a run-time branch on it was
+// turned into both computations and a select).
+template <bool kPow2>
 __device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
   const double s = static_cast<double>(s1);
   double q;
-  if (sa.inv_nsq != 0.0)
+  if constexpr (kPow2)
     q = s * sa.inv_nsq;
   else
     q = s / sa.nsq;
@@ -94,6 +99,7 @@ __device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
 //   numerator (C's MIN(g, limit), see StatArgs); then the two ratios and
 //   their log2.  With nsq = 0 nothing is special-cased: IEEE arithmetic
 //   throughout, as in the plain definition.
+template <bool kPow2>
 __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
                                             float yy, float xy,
                                             const StatArgs &sa, float &num,
@@ -127,7 +133,7 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
   const float gg = g * g;
   const float a = gg * s1;
   num = log2_poly(num_ratio(a, sv, sa.nsq));
-  den = log2_poly(den_ratio(s1, sa));
+  den = log2_poly(den_ratio<kPow2>(s1, sa));
 }
 
 }  // namespace vifk

@@ -135,7 +135,7 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
 // and writes at its own offsets of the next scale's planes and the terms.
 // Tile (blockIdx.x, strip0 + blockIdx.y): a frame with more strips than a
 // grid's y dimension allows is covered by several launches.
-template <int R, int RD, typename InT>
+template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
     StatArgs stat, int strip0) {
@@ -373,8 +373,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
     settle(fb);
 #pragma unroll
     for (int i = 0; i < HB; ++i)
-      pixel_terms(fa[0][i], fa[1][i], fb[0][i], fb[1][i], fb[2][i], stat,
-                  tnum[i], tden[i]);
+      pixel_terms<kPow2>(fa[0][i], fa[1][i], fb[0][i], fb[1][i], fb[2][i],
+                         stat, tnum[i], tden[i]);
   }
   __syncthreads(); // every read of round B is done: its region takes the terms
 
@@ -492,6 +492,37 @@ __global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
 
 // ------------------------------------------------------------------ launch
 
+// One launch of the scale kernel of `scale` for the statistic's form kPow2
+// (a power-of-two noise variance, see den_ratio).
+template <bool kPow2>
+void launch_one(int scale, int bpc, dim3 grid, dim3 block, hipStream_t stream,
+                const ScaleIO &io, const ScaleGeom &g, float sc,
+                const TapArgs &taps, const TapArgs &next_taps,
+                const StatArgs &stat, int s0) {
+  switch (scale) {
+  case 0:
+    if (bpc == 8)
+      scale_kernel<8, 4, uint8_t, kPow2><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, sc, taps, next_taps, stat, s0);
+    else
+      scale_kernel<8, 4, uint16_t, kPow2><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, sc, taps, next_taps, stat, s0);
+    break;
+  case 1:
+    scale_kernel<4, 2, float, kPow2><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    break;
+  case 2:
+    scale_kernel<2, 1, float, kPow2><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    break;
+  default:
+    scale_kernel<1, 0, float, kPow2><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    break;
+  }
+}
+
 hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
                         const ScaleGeom &g, const TapArgs &taps,
                         const TapArgs &next_taps, const StatArgs &stat,
@@ -508,28 +539,12 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
     const dim3 grid(static_cast<unsigned>(g.ntx),
                     static_cast<unsigned>(std::min(kMaxGridY, g.strips - s0)),
                     static_cast<unsigned>(n));
-    switch (scale) {
-    case 0:
-      if (bpc == 8)
-        scale_kernel<8, 4, uint8_t><<<grid, block, 0, stream>>>(
-            io, g.w, g.h, sc, taps, next_taps, stat, s0);
-      else
-        scale_kernel<8, 4, uint16_t><<<grid, block, 0, stream>>>(
-            io, g.w, g.h, sc, taps, next_taps, stat, s0);
-      break;
-    case 1:
-      scale_kernel<4, 2, float><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
-      break;
-    case 2:
-      scale_kernel<2, 1, float><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
-      break;
-    default:
-      scale_kernel<1, 0, float><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
-      break;
-    }
+    if (stat.inv_nsq != 0.0)
+      launch_one<true>(scale, bpc, grid, block, stream, io, g, sc, taps,
+                       next_taps, stat, s0);
+    else
+      launch_one<false>(scale, bpc, grid, block, stream, io, g, sc, taps,
+                        next_taps, stat, s0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
       return e;
@@ -541,9 +556,10 @@ hipError_t scale0_resident_blocks(int bpc, int *blocks) {
   int per_cu = 0;
   hipError_t e =
       bpc == 8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint8_t>, kThreads, 0)
+                     &per_cu, scale_kernel<8, 4, uint8_t, true>, kThreads, 0)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint16_t>, kThreads, 0);
+                     &per_cu, scale_kernel<8, 4, uint16_t, true>, kThreads,
+                     0);
   int dev = 0, cus = 0;
   if (e == hipSuccess)
     e = hipGetDevice(&dev);

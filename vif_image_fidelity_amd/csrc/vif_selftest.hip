@@ -44,6 +44,7 @@ __global__ void log2_kernel(const float *__restrict__ x, long n,
     y[i] = vifk::log2_poly(x[i]);
 }
 
+template <bool kPow2>
 __global__ void ratios_kernel(const float *__restrict__ a,
                               const float *__restrict__ sv, long n,
                               vifk::StatArgs sa, float *__restrict__ num,
@@ -51,10 +52,11 @@ __global__ void ratios_kernel(const float *__restrict__ a,
   const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
   if (i < n) {
     num[i] = vifk::num_ratio(a[i], sv[i], sa.nsq);
-    den[i] = vifk::den_ratio(a[i], sa);
+    den[i] = vifk::den_ratio<kPow2>(a[i], sa);
   }
 }
 
+template <bool kPow2>
 __global__ void statistic_kernel(const float *__restrict__ mu1,
                                  const float *__restrict__ mu2,
                                  const float *__restrict__ xx,
@@ -65,7 +67,7 @@ __global__ void statistic_kernel(const float *__restrict__ mu1,
   const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
   if (i < n) {
     float a, b;
-    vifk::pixel_terms(mu1[i], mu2[i], xx[i], yy[i], xy[i], sa, a, b);
+    vifk::pixel_terms<kPow2>(mu1[i], mu2[i], xx[i], yy[i], xy[i], sa, a, b);
     num[i] = a;
     den[i] = b;
   }
@@ -144,8 +146,12 @@ vif_selftest_ratios(const float *a, const float *sv, double nsq, long n,
   if (n == 0)
     return vifk::set_status(VIF_OK);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ratios_kernel<<<grid_for(n), kBlock, 0, s>>>(
-      a, sv, n, vifk::make_stat_args(nsq, 100.0), num, den);
+  const vifk::StatArgs sa = vifk::make_stat_args(nsq, 100.0);
+  if (sa.inv_nsq != 0.0)
+    ratios_kernel<true><<<grid_for(n), kBlock, 0, s>>>(a, sv, n, sa, num, den);
+  else
+    ratios_kernel<false><<<grid_for(n), kBlock, 0, s>>>(a, sv, n, sa, num,
+                                                        den);
   return finish(s);
 }
 
@@ -160,9 +166,13 @@ vif_selftest_statistic(const float *mu1, const float *mu2, const float *xx,
   if (n == 0)
     return vifk::set_status(VIF_OK);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  statistic_kernel<<<grid_for(n), kBlock, 0, s>>>(
-      mu1, mu2, xx, yy, xy, n, vifk::make_stat_args(nsq, gain_limit), num,
-      den);
+  const vifk::StatArgs sa = vifk::make_stat_args(nsq, gain_limit);
+  if (sa.inv_nsq != 0.0)
+    statistic_kernel<true><<<grid_for(n), kBlock, 0, s>>>(
+        mu1, mu2, xx, yy, xy, n, sa, num, den);
+  else
+    statistic_kernel<false><<<grid_for(n), kBlock, 0, s>>>(
+        mu1, mu2, xx, yy, xy, n, sa, num, den);
   return finish(s);
 }
 
