@@ -37,6 +37,7 @@ extern "C" {
 #define VIF_EINVAL (-1) /* bad geometry, bit depth, NULL pointer, state   */
 #define VIF_ENOMEM (-2) /* device or pinned host allocation failed        */
 #define VIF_EHIP (-3)   /* any other HIP runtime error (see vif_strerror)  */
+#define VIF_ETOOBIG (-4) /* frame too large for vif_score_noalloc's array  */
 
 #define VIF_NSCALES 4
 #define VIF_MAX_TAPS 17
@@ -243,6 +244,34 @@ vif_ctx *vif_create_strip(int w, int h, int bpc, const vif_options *opt,
                           int max_batch, int row0, int row1);
 int vif_scores_from_rows(int w, int h, const vif_options *opt,
                          const float *rows, double out[8], float sums[8]);
+
+/*
+ * vif_score_noalloc -- vif_score for callers that cannot allocate memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Scores one frame pair of w x h samples at bpc bits with the
+ * options opt (NULL: the defaults) on the HIP stream hip_stream (a
+ * hipStream_t as void*; NULL: the default stream), without a context and
+ * without allocating anything: no device, pinned or host allocation, no
+ * library routine that allocates.  The kernels are vif_score's and so are
+ * the bits of out.  ref, dist and out as for vif_score (device frames, host
+ * out).
+ * The buffers the kernels need beyond the frames and out (pyramid planes,
+ * term buffers, row sums, the eight sums) live in one array of
+ * VIF_NOALLOC_SCRATCH bytes of device memory that the library defines: each
+ * device the call runs on holds it from the call's first use there until
+ * the process ends.  A frame whose buffers do not fit is refused with
+ * VIF_ETOOBIG before any work is queued (3840x2160 needs about 105 MiB,
+ * 4096x2160 about 112 MiB).
+ * Synchronous: returns once out is written (it synchronises hip_stream).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (two streams or two host
+ * threads at once) race, and the caller must serialise them.  VIF_EINVAL for
+ * bad arguments (as vif_create_ex and vif_score), VIF_EHIP for a HIP error.
+ */
+#define VIF_NOALLOC_SCRATCH (128L << 20)
+int vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
+                      const void *ref, const void *dist, void *hip_stream,
+                      double out[8]);
 
 /* vif_pending -- frames submitted and not yet collected (or VIF_EINVAL). */
 int vif_pending(const vif_ctx *ctx);

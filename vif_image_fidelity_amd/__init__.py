@@ -18,12 +18,13 @@ import numpy as np
 
 from . import _lib
 from ._lib import (VIF_EHIP, VIF_EINVAL, VIF_ENOMEM, VIF_OK, VifError,
+                   VIF_ETOOBIG, NOALLOC_SCRATCH,
                    DEBUG_NAMES, KERNEL_KINDS, QUEUE_DEPTH, MAX_BATCH,
                    MIN_SIDE, MAX_PIXELS, FSSIM_KERNEL_KINDS,
                    FSSIM_QUEUE_DEPTH, FSSIM_MAX_PIXELS, FSSIM_MAX_FACTOR)
 
 __all__ = ["Vif", "VifError", "FloatSsim", "fssim_taps", "taps",
-           "strip_geometry", "scores_from_rows",
+           "strip_geometry", "scores_from_rows", "score_noalloc",
            "make_options", "DEFAULT_OPTIONS",
            "VIF_OK", "VIF_EINVAL", "VIF_ENOMEM", "VIF_EHIP", "DEBUG_NAMES",
            "KERNEL_KINDS", "QUEUE_DEPTH", "MAX_BATCH", "MIN_SIDE",
@@ -307,6 +308,25 @@ class Vif:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def score_noalloc(ref, dist, bpc, options=None, stream=None):
+    """Score one pair with vif_score_noalloc: no context and no allocation
+    (the library's fixed device array holds the intermediate buffers).
+    ref, dist: device tensors (h, w) or device pointers with the sizes given
+    by the tensors; returns float64[8] as Vif.score."""
+    h, w = (int(v) for v in ref.shape)
+    if tuple(dist.shape) != (h, w):
+        raise ValueError("ref and dist differ in shape")
+    out = np.zeros(8, dtype=np.float64)
+    sp = getattr(stream, "cuda_stream", stream)
+    rc = _lib.vif_score_noalloc(w, h, int(bpc),
+                                None if options is None
+                                else make_options(options),
+                                _ptr(ref), _ptr(dist), sp, out)
+    if rc != VIF_OK:
+        raise VifError(rc, "vif_score_noalloc")
+    return out
 
 
 def strip_geometry(w, h, row0, row1):

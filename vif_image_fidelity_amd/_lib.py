@@ -15,6 +15,8 @@ VIF_OK = 0
 VIF_EINVAL = -1
 VIF_ENOMEM = -2
 VIF_EHIP = -3
+VIF_ETOOBIG = -4
+NOALLOC_SCRATCH = 128 << 20
 NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
@@ -86,6 +88,8 @@ def load():
         "vif_strip_geometry": ([ip, ip, ip, ip, ctypes.POINTER(ip)], ip),
         "vif_scores_from_rows": ([ip, ip, ctypes.POINTER(VifOptions), fp, dp,
                                   fp], ip),
+        "vif_score_noalloc": ([ip, ip, ip, ctypes.POINTER(VifOptions), vp,
+                               vp, vp, dp], ip),
         "vif_default_options": ([ctypes.POINTER(VifOptions)], None),
         "vif_get_options": ([vp, ctypes.POINTER(VifOptions)], ip),
         "vif_get_debug": ([vp, dp], ip),
@@ -144,6 +148,7 @@ def exported_symbols():
     return ["vif_default_options", "vif_create", "vif_create_ex",
             "vif_create_batch", "vif_submit_batch", "vif_create_strip",
             "vif_strip_geometry", "vif_scores_from_rows",
+            "vif_score_noalloc",
             "vif_get_options", "vif_score", "vif_submit", "vif_collect",
             "vif_submit_host", "vif_score_host",
             "vif_pending", "vif_get_debug",
@@ -208,6 +213,15 @@ def vif_scores_from_rows(w, h, options, rows, out, sums):
     return load().vif_scores_from_rows(
         int(w), int(h), None if options is None else ctypes.byref(options),
         _fptr(rows), _dptr(out), None if sums is None else _fptr(sums))
+
+
+def vif_score_noalloc(w, h, bpc, options, ref_ptr, dist_ptr, stream, out):
+    """options: a VifOptions or None; stream: a hipStream_t (int) or None;
+    out: a float64[8] numpy array."""
+    return load().vif_score_noalloc(
+        int(w), int(h), int(bpc),
+        None if options is None else ctypes.byref(options), ref_ptr,
+        dist_ptr, stream, _dptr(out))
 
 
 def vif_submit_batch(ctx, ref_ptrs, dist_ptrs):

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvif_amd.so")
 
 SOURCES = ["vif_kernels.hip", "vif_selftest.hip", "vif_api.cpp",
-           "vif_taps.cpp", "vif_options.cpp", "vif_rows.cpp", "fssim_kernels.hip",
+           "vif_taps.cpp", "vif_options.cpp", "vif_rows.cpp", "vif_noalloc.hip",
+           "fssim_kernels.hip",
            "fssim_api.cpp", "fssim_taps.cpp"]
 
 ARCH = "gfx950"

@@ -698,6 +698,9 @@ __attribute__((visibility("default"))) const char *vif_strerror(int code) {
   case VIF_EHIP:
     return vifk::t_hip != hipSuccess ? hipGetErrorString(vifk::t_hip)
                                      : "HIP runtime error";
+  case VIF_ETOOBIG:
+    return "frame needs more than vif_score_noalloc's device array "
+           "(VIF_NOALLOC_SCRATCH bytes)";
   default:
     return "unknown error code";
   }
