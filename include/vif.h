@@ -348,8 +348,9 @@ int vif_set_profiling(vif_ctx *ctx, int kinds);
  * vif_get_kernel_times -- accumulated kernel durations in milliseconds and
  * launch counts since profiling was enabled, one entry per kernel kind:
  *   0..3  the kernel of scale s (filter, statistic, terms, next scale's
- *         planes)
- *   4     the ordered row sums of all four scales
+ *         planes; scale 0's also adds its rows' terms in order, carrying
+ *         each row's sum from tile to tile)
+ *   4     the ordered row sums of scales 1..3
  * A launch here is one kind's work for one submission (all its frames): one
  * kernel launch, or several in a row for a scale with more than 65535 strips
  * of 16 rows, timed as one.

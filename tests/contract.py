@@ -11,7 +11,10 @@ Context and Consequences).  This module checks three layers:
   flags    the library's compiler flags fix contraction off, IEEE division,
            denormals and no fast-math, with packed fp32 disabled;
   sources  the kernel sources call no fused multiply-add, no library or
-           hardware log/exp, no atomics, and include no CUDA or Triton;
+           hardware log/exp, no atomic read-modify-write (an atomic add
+           would merge sums in arrival order; atomic loads and stores that
+           only hand a value from one block to the next are allowed), and
+           include no CUDA or Triton;
   ISA      the compiled gfx950 code of every kernel: each fp32 / fp64 fused
            multiply-add belongs to a correctly rounded division expansion
            (five per v_div_fixup), and there are no packed-fp32, float mad,
@@ -30,9 +33,9 @@ CSRC = os.path.join(ROOT, "vif_image_fidelity_amd", "csrc")
 
 # Device code: every file whose functions run on the GPU.
 KERNEL_SOURCES = ("vif_kernels.hip", "vif_device_math.h", "vif_selftest.hip",
-                  "fssim_kernels.hip")
+                  "vif_noalloc.hip", "fssim_kernels.hip")
 # Compiled for the ISA check (the others are included by these).
-ISA_SOURCES = ("vif_kernels.hip", "fssim_kernels.hip")
+ISA_SOURCES = ("vif_kernels.hip", "vif_noalloc.hip", "fssim_kernels.hip")
 
 REQUIRED_FLAGS = ("--offload-arch=gfx950", "-ffp-contract=off",
                   "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -63,8 +66,9 @@ _SOURCE_RULES = (
     (r"\b(?:log2f?|logf?|log10f?|__log2f|__logf|exp2f?|expf?|__expf|"
      r"__builtin_amdgcn_(?:log|exp)\w*|__builtin_(?:log|exp)\w*)\s*\(",
      "library or hardware log/exp in device code"),
-    (r"\batomic\w*\s*\(|\b__hip_atomic\w*|\b__atomic_\w+",
-     "atomic operation"),
+    (r"\batomic(?!_load\b|_store\b)\w*\s*\(|"
+     r"\b__hip_atomic_(?!load\b|store\b)\w*|\b__atomic_\w+",
+     "atomic read-modify-write"),
     (r"#\s*include\s*[<\"](?:cuda|cublas|cub/|thrust/)", "CUDA include"),
     (r"\btriton\b", "Triton"),
     (r"__HIP_PLATFORM_|__CUDA_ARCH__|__NVCC__", "dual-platform code path"),

@@ -45,6 +45,9 @@ def test_compiled_kernels(isa):
     assert any("decimate_pow2_kernel" in k for k in names)
     assert any("decimate_kernelI" in k for k in names)
     assert any("ssim_kernel" in k for k in names)
+    assert any("scale_sums_kernel" in k for k in names)
+    # scale 0 carries its row sums from tile to tile
+    assert any("scale_kernelILi8ELi4EhLb1ELb1E" in k for k in names)
 
 
 # ----------------------------------------------------------- planted mistakes
@@ -68,8 +71,14 @@ SOURCE_MUTANTS = [
      "acc[0][i] = __builtin_fmaf(t, x, acc[0][i]);"),
     ("vif_device_math.h", "  return static_cast<float>(e) + q;",
      "  return log2f(x);"),
-    ("vif_kernels.hip", "  float acc = 0.0f;",
-     "  float acc = 0.0f;\n  atomicAdd(&a.rows[0][0], 1.0f);"),
+    ("vif_kernels.hip", "  const int seq = lane & 31;",
+     "  const int seq = lane & 31;\n  atomicAdd(&a.rows[0][0], 1.0f);"),
+    ("vif_kernels.hip", "  float acc = 0.0f;\n  if (tx > 0)",
+     "  float acc = 0.0f;\n  __hip_atomic_fetch_add(io.rows, 1.0f, "
+     "__ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n  if (tx > 0)"),
+    ("vif_noalloc.hip", "    carry[i] = 0ull;",
+     "    __hip_atomic_exchange(carry + i, 0ull, __ATOMIC_RELAXED, "
+     "__HIP_MEMORY_SCOPE_AGENT);"),
     ("fssim_kernels.hip", "#include <hip/hip_runtime.h>",
      "#include <hip/hip_runtime.h>\n#include <cuda_runtime.h>"),
     ("fssim_kernels.hip", "      s = s + wtap(sa, k) * v[i + k];",

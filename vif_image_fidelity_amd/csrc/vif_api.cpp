@@ -6,11 +6,13 @@
 // of a three-slot ring, and every slot its own stream and buffers (pyramid
 // planes, term buffers, and its row sums in pinned host memory, each sized
 // for max_batch frames).  The slot's stream runs the four per-scale kernels (filter,
-// statistic, terms, next scale's planes) and the ordered row sums of all
-// scales (one launch), which write two floats per row per scale straight
-// into the host buffer: one read-back per frame with no copy call
-// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Decision:
-// the row sums come back in one transfer and the host adds them).
+// statistic, terms, next scale's planes; scale 0's kernel also carries each
+// row's fp32 sum from tile to tile and stores the row sums) and the ordered
+// row sums of scales 1..3 (one launch); the row sums go straight into the
+// host buffer, two floats per row per scale: one read-back per frame with
+// no copy call (ADR-1422 "float_vif_sycl computes the CPU's arithmetic
+// ...", Decision: the row sums come back in one transfer and the host adds
+// them).
 // Frames in host memory are first copied into the slot's own frame buffers
 // on the slot's stream (vif_submit_host).
 // Consecutive frames rotate over the slots, so one frame's small
@@ -58,8 +60,11 @@ struct Slot {
   float *pyr_dist[kScales] = {};  // max_batch planes each, plane_elems apart
   void *frame_ref = nullptr;      // device copies of host frames
   void *frame_dist = nullptr;
-  float *terms[kScales] = {};     // term buffers of the four scales
-  float *rows_host = nullptr;     // pinned, written by the row-sum kernel
+  float *terms[kScales] = {};     // term buffers of scales 1..3
+  unsigned long long *carry = nullptr; // scale 0's row sums between tiles
+  float *rows_host = nullptr;     // pinned, written by the kernels
+  int *err_host = nullptr;        // pinned, raised by a carry wait that
+                                  // gave up
   hipStream_t stream = nullptr;   // owned: all of the slot's work
   hipEvent_t submitted = nullptr; // on the caller's stream
   hipEvent_t done = nullptr;      // on the slot's stream, after the row sums
@@ -98,6 +103,7 @@ struct vif_ctx {
   int own_rows = 0;
   int rowsum_waves = 0;
   bool order_scale0 = false; // consecutive frames' scale-0 kernels ordered
+  unsigned carry_tag = 0;    // tag of the last submission's carries
   vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
   long head = 0, tail = 0;   // submitted / collected frame counts
   long shead = 0, stail = 0; // submitted / released slot counts
@@ -150,6 +156,10 @@ void free_all(vif_ctx *c) {
       if (sl.terms[s])
         (void)hipFree(sl.terms[s]);
     }
+    if (sl.carry)
+      (void)hipFree(sl.carry);
+    if (sl.err_host)
+      (void)hipHostFree(sl.err_host);
     if (sl.frame_ref)
       (void)hipFree(sl.frame_ref);
     if (sl.frame_dist)
@@ -209,6 +219,16 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
     io.terms = sl.terms[s];
     io.terms_stride = ctx->terms_elems[s];
     if (s == 0) {
+      // the row sums of scale 0 are chained across each row's tiles inside
+      // the kernel: a fresh tag per submission marks this launch's carries
+      ctx->carry_tag = ctx->carry_tag + 1 == 0 ? 1 : ctx->carry_tag + 1;
+      io.carry = sl.carry;
+      io.carry_tag = ctx->carry_tag;
+      io.strips = ctx->geom[0].strips;
+      io.ntx = ctx->geom[0].ntx;
+      io.rows = sl.rows_host + 2 * ctx->row_base[0];
+      io.rows_stride = static_cast<size_t>(2) * ctx->total_rows;
+      io.err = sl.err_host;
       // 8 samples per load: rows start on 8-sample boundaries and the
       // planes are aligned to 8 samples' bytes
       const uintptr_t align = ctx->bpc == 8 ? 8 : 16;
@@ -294,6 +314,14 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
     sl.taken = sl.n;
     ctx->stail += 1;
     return vifk::status_from_hip(e);
+  }
+  if (*static_cast<volatile int *>(sl.err_host) != 0) {
+    // a wait for a row-sum carry gave up: the submission's sums are void
+    *static_cast<volatile int *>(sl.err_host) = 0;
+    ctx->tail += sl.n - z;
+    sl.taken = sl.n;
+    ctx->stail += 1;
+    return vifk::set_status(VIF_EHIP, hipErrorLaunchTimeOut);
   }
   if (z == 0) {
     for (int k = 0; k < kKinds; ++k) {
@@ -424,8 +452,10 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
     c->own_base[s] = own;
     own += sr.nown[s];
     c->plane_elems[s] = static_cast<size_t>(ws) * hs;
-    c->terms_elems[s] = static_cast<size_t>(g.strips) *
-                        vifk::term_groups(ws) * vifk::kSeq * 4;
+    // scale 0's row sums are chained inside its kernel: no term buffer
+    c->terms_elems[s] = s == 0 ? 0
+                               : static_cast<size_t>(g.strips) *
+                                     vifk::term_groups(ws) * vifk::kSeq * 4;
     const int nt = vifk::gaussian_taps(s, c->taps[s].t);
     // the kernels rely on bitwise symmetric taps (see tap() there)
     for (int k = 0; k < nt; ++k)
@@ -435,7 +465,8 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
     c->rowsum.w[s] = ws;
     c->rowsum.h[s] = hs;
     c->rowsum.strips[s] = g.strips;
-    c->rowsum.pair_base[s + 1] = c->rowsum.pair_base[s] + (g.strips + 1) / 2;
+    c->rowsum.pair_base[s + 1] =
+        c->rowsum.pair_base[s] + (s == 0 ? 0 : (g.strips + 1) / 2);
   }
   c->rowsum_waves = c->rowsum.pair_base[kScales];
   // order consecutive scale-0 kernels when one covers the device's resident
@@ -469,8 +500,21 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
       e = hipMalloc(&sl.frame_ref, frame_bytes);
     if (e == hipSuccess)
       e = hipMalloc(&sl.frame_dist, frame_bytes);
-    for (int s = 0; s < kScales && e == hipSuccess; ++s)
+    for (int s = 1; s < kScales && e == hipSuccess; ++s)
       e = dev_alloc(&sl.terms[s], nb * c->terms_elems[s]);
+    // scale 0's carries, cleared once: every launch writes its own tag
+    const size_t carries = nb * c->geom[0].strips *
+                           (c->geom[0].ntx > 1 ? c->geom[0].ntx - 1 : 1) *
+                           vifk::kSeq;
+    if (e == hipSuccess)
+      e = dev_alloc(&sl.carry, carries);
+    if (e == hipSuccess)
+      e = hipMemset(sl.carry, 0, carries * sizeof(unsigned long long));
+    if (e == hipSuccess)
+      e = hipHostMalloc(reinterpret_cast<void **>(&sl.err_host), sizeof(int),
+                        hipHostMallocCoherent);
+    if (e == hipSuccess)
+      *sl.err_host = 0;
     // coherent pinned memory: the row-sum kernel's stores reach the host
     // without a copy, visible once the slot's event has completed
     if (e == hipSuccess)

@@ -83,6 +83,18 @@ struct ScaleIO {
   // (width a multiple of 8, planes 8-byte aligned for 8-bit samples,
   // 16-byte for 16-bit ones); 0 otherwise and at scales 1-3
   int vec_in;
+  // scale 0 only (its row sums are chained from tile to tile instead of
+  // going through a term buffer): carry holds n * strips * (ntx - 1) * 32
+  // words (at least one), written with the tag carry_tag (never 0, new for
+  // every launch that reuses the buffer); rows receives the row sums
+  // (rows[z * rows_stride + 2 * y + c]); err is raised if a wait for a
+  // carry gives up.  strips and ntx are the scale's.
+  unsigned long long *carry;
+  unsigned carry_tag;
+  int strips, ntx;
+  float *rows;
+  size_t rows_stride;
+  int *err;
 };
 
 // Arguments of the row-sum kernel (all four scales in one launch): scale s
@@ -132,7 +144,9 @@ struct ScaleGeom {
 };
 
 // Per-scale kernel for n frames (1 <= n <= kMaxBatch): filter, statistic,
-// terms and the next scale's planes.  io.in_* are the scale's planes (native
+// terms and the next scale's planes.  At scale 0 the terms' row sums are
+// chained across the row's tiles inside the kernel (io.carry, io.rows): the
+// term buffer and the row-sum kernel serve scales 1..3 only.  io.in_* are the scale's planes (native
 // samples at scale 0, fp32 planes above); io.next_* receive the next scale's
 // planes (unused at scale 3); io.terms is the scale's term buffer (strips *
 // term_groups(w) * 128 floats per frame).

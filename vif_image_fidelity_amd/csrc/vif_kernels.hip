@@ -12,12 +12,15 @@
 //      and the vertical pass of the next scale's low-pass at even rows;
 //   3. the horizontal pass (7 outputs per thread, in two rounds of
 //      quantities so the block's LDS stays small), the per-pixel statistic
-//      and the two terms, staged in LDS and written to the scale's term
-//      buffer in the order the row sums read them;
+//      and the two terms, staged in LDS;
 //   4. the horizontal pass of the next scale's low-pass at even columns,
-//      written as the next scale's fp32 planes (2x decimation).
-// A second kernel (one launch for all scales) adds each row's terms in
-// order.
+//      written as the next scale's fp32 planes (2x decimation);
+//   5. at scale 0, the ordered row sums themselves: each row's fp32
+//      accumulator is carried from tile to tile along the row (chain_rows),
+//      so scale 0 has no term buffer; at scales 1..3, the terms go to the
+//      scale's term buffer in the order the row sums read them.
+// A second kernel (one launch for scales 1..3) adds each of those rows'
+// terms in order.
 //
 // Every multiply and add is its own IEEE fp32 rounding (the library is
 // built with -ffp-contract=off), taps in ascending order, vertical pass
@@ -118,6 +121,77 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
   }
 }
 
+// Row sums carried from tile to tile (the scale-0 kernel).  The sum of a
+// row is one fp32 accumulator over its terms from left to right (ADR-1422
+// "float_vif_sycl computes the CPU's arithmetic ...", Context and Decision),
+// so a row that spans several tiles is a chain: tile tx continues the
+// accumulator that tile tx - 1 ended with.  Tile tx - 1 hands it over in one
+// 64-bit word per sequence, io.carry[((z * strips + strip) * (ntx - 1) +
+// tx - 1) * 32 + q]: the launch's tag in the high half, the fp32 value in the
+// low half, written and read with relaxed atomics at device scope.  A word
+// carrying the value with its tag needs no fence: a reader that sees the tag
+// sees the value of the same store.  Words of an earlier launch carry an
+// earlier tag, so they are never taken for this launch's.
+//
+// Blocks of a launch take the same tile column of every strip and frame
+// before the next column (blockIdx.x runs over strips and frames), and the
+// hardware starts blocks in that order, so tile tx - 1 started long before
+// tile tx (a whole column of blocks earlier) and its word is usually there
+// when tile tx reads it.  The wait is bounded: after kCarrySpins reads
+// without the tag the block gives up, stores NaN and raises io.err, which
+// the host reports as an error, so a launch always ends.
+constexpr int kCarrySpins = 1 << 16;
+
+__device__ __forceinline__ float wait_carry(const unsigned long long *word,
+                                            unsigned tag, int *err) {
+  unsigned long long v =
+      __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int spins = 0;
+  while (static_cast<unsigned>(v >> 32) != tag) {
+    if (++spins >= kCarrySpins) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return __builtin_nanf("");
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __uint_as_float(static_cast<unsigned>(v));
+}
+
+// Lane q's part of the chain for tile (tx, strip) of frame z: `terms` is
+// its sequence's row of the tile in LDS, `cols` the tile's columns inside
+// the plane, y the sequence's row.
+__device__ __forceinline__ void chain_rows(const ScaleIO &io,
+                                           const float *__restrict__ terms,
+                                           int cols, int z, int strip, int tx,
+                                           int y, int h, int q) {
+  unsigned long long *word =
+      io.carry +
+      ((static_cast<size_t>(z) * io.strips + strip) * (io.ntx - 1) + tx) *
+          kSeq +
+      q;
+  float acc = 0.0f;
+  if (tx > 0)
+    acc = wait_carry(word - kSeq, io.carry_tag, io.err);
+  if (cols == kTileW) {
+#pragma unroll 16
+    for (int i = 0; i < kTileW; ++i)
+      acc = acc + terms[i];
+  } else {
+    for (int i = 0; i < cols; ++i)
+      acc = acc + terms[i];
+  }
+  if (tx == io.ntx - 1) {
+    if (y < h)
+      io.rows[static_cast<size_t>(z) * io.rows_stride + 2 * y + (q & 1)] = acc;
+  } else {
+    const unsigned long long v =
+        (static_cast<unsigned long long>(io.carry_tag) << 32) |
+        __float_as_uint(acc);
+    __hip_atomic_store(word, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
 //
@@ -135,16 +209,29 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
 // and writes at its own offsets of the next scale's planes and the terms.
 // Tile (blockIdx.x, strip0 + blockIdx.y): a frame with more strips than a
 // grid's y dimension allows is covered by several launches.
-template <int R, int RD, typename InT, bool kPow2>
+template <int R, int RD, typename InT, bool kPow2, bool kChain>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
-    StatArgs stat, int strip0) {
-  const int z = blockIdx.z;
+    StatArgs stat, int first) {
+  // Tile (tx, strip) of frame z.  Term-buffer form: tx = blockIdx.x, strip =
+  // first + blockIdx.y, z = blockIdx.z.  Chained form: blockIdx.x = z *
+  // strips + strip runs fastest, so that consecutive blocks take the same
+  // tile column of every strip and frame, and tx = first + blockIdx.y.
+  int z, tx, strip;
+  if constexpr (kChain) {
+    z = static_cast<int>(blockIdx.x) / io.strips;
+    strip = static_cast<int>(blockIdx.x) - z * io.strips;
+    tx = first + static_cast<int>(blockIdx.y);
+  } else {
+    z = blockIdx.z;
+    tx = blockIdx.x;
+    strip = first + static_cast<int>(blockIdx.y);
+  }
   const InT *__restrict__ ref = static_cast<const InT *>(io.in_ref[z]);
   const InT *__restrict__ dist = static_cast<const InT *>(io.in_dist[z]);
   float *__restrict__ next_ref = io.next_ref + z * io.next_stride;
   float *__restrict__ next_dist = io.next_dist + z * io.next_stride;
-  float *__restrict__ terms = io.terms + z * io.terms_stride;
+  float *__restrict__ terms = kChain ? nullptr : io.terms + z * io.terms_stride;
   constexpr int N = 2 * R + 1;
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
@@ -169,8 +256,6 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   InT *sIn = reinterpret_cast<InT *>(lds);
 
   const int tid = threadIdx.x;
-  const int tx = blockIdx.x;
-  const int strip = strip0 + static_cast<int>(blockIdx.y);
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
   // 1. input tile [IR][CW] for ref then dist.  A tile whose columns all lie
@@ -388,6 +473,17 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads(); // terms complete in LDS
 
+  if constexpr (kChain) {
+    // 8. the ordered row sums, continued from the tile on the left: lane q
+    //    of wave 0 owns sequence q (row q / 2, component q % 2); it takes
+    //    the row's fp32 accumulator where the left tile left it (0 at the
+    //    first tile), adds this tile's terms left to right, and hands the
+    //    accumulator on, or stores the row's sum at the last tile.
+    if (tid < kSeq)
+      chain_rows(io, sT + tid * kTermPitch, min(kTileW, w - x0), z, strip,
+                 tx, y0 + (tid >> 1), h, tid);
+    return;
+  }
   // 8. terms to the strip's term buffer: groups of 4 columns, each group
   //    holding the 32 sequences' 4 values ([g][seq][4] floats); this tile's
   //    28 groups are one contiguous 14 KiB block.  The stores are
@@ -408,8 +504,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
 }
 
-// Ordered row sums of every scale, one launch per submission.  One wave owns two
-// 16-row strips of one scale: lane l adds sequence l%32 (row (l%32)/2,
+// Ordered row sums of scales 1..3, one launch per submission (scale 0's are
+// chained inside its kernel).  One wave owns two 16-row strips of one scale: lane l adds sequence l%32 (row (l%32)/2,
 // component l%2) of strip 2p + l/32 left to right into one fp32
 // accumulator starting at 0.0f, exactly the serial loop over the row
 // (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Context and
@@ -498,27 +594,27 @@ template <bool kPow2>
 void launch_one(int scale, int bpc, dim3 grid, dim3 block, hipStream_t stream,
                 const ScaleIO &io, const ScaleGeom &g, float sc,
                 const TapArgs &taps, const TapArgs &next_taps,
-                const StatArgs &stat, int s0) {
+                const StatArgs &stat, int first) {
   switch (scale) {
   case 0:
     if (bpc == 8)
-      scale_kernel<8, 4, uint8_t, kPow2><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, sc, taps, next_taps, stat, s0);
+      scale_kernel<8, 4, uint8_t, kPow2, true><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, sc, taps, next_taps, stat, first);
     else
-      scale_kernel<8, 4, uint16_t, kPow2><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, sc, taps, next_taps, stat, s0);
+      scale_kernel<8, 4, uint16_t, kPow2, true><<<grid, block, 0, stream>>>(
+          io, g.w, g.h, sc, taps, next_taps, stat, first);
     break;
   case 1:
-    scale_kernel<4, 2, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    scale_kernel<4, 2, float, kPow2, false><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   case 2:
-    scale_kernel<2, 1, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    scale_kernel<2, 1, float, kPow2, false><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   default:
-    scale_kernel<1, 0, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, s0);
+    scale_kernel<1, 0, float, kPow2, false><<<grid, block, 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   }
 }
@@ -534,17 +630,31 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
                    : bpc == 10 ? 0.25f
                    : bpc == 12 ? 0.0625f
                                : 0.00390625f;
-  // grid y holds at most kMaxGridY strips per launch
-  for (int s0 = 0; s0 < g.strips; s0 += kMaxGridY) {
-    const dim3 grid(static_cast<unsigned>(g.ntx),
-                    static_cast<unsigned>(std::min(kMaxGridY, g.strips - s0)),
-                    static_cast<unsigned>(n));
+  // Grid y holds at most kMaxGridY rows of blocks per launch: strips for
+  // the term-buffer form, tile columns for the chained form (scale 0), whose
+  // grid x runs over the strips of every frame.  A later launch on the same
+  // stream starts after the earlier ones have finished, so a chain that
+  // crosses launches finds its carries written.
+  const bool chain = scale == 0;
+  const int rows = chain ? g.ntx : g.strips;
+  if (chain && (io.carry == nullptr || io.rows == nullptr ||
+                io.err == nullptr || io.strips != g.strips ||
+                io.ntx != g.ntx ||
+                static_cast<long>(n) * g.strips > 0x7fffffffL))
+    return hipErrorInvalidValue;
+  for (int first = 0; first < rows; first += kMaxGridY) {
+    const unsigned ny =
+        static_cast<unsigned>(std::min(kMaxGridY, rows - first));
+    const dim3 grid =
+        chain ? dim3(static_cast<unsigned>(n * g.strips), ny, 1)
+              : dim3(static_cast<unsigned>(g.ntx), ny,
+                     static_cast<unsigned>(n));
     if (stat.inv_nsq != 0.0)
       launch_one<true>(scale, bpc, grid, block, stream, io, g, sc, taps,
-                       next_taps, stat, s0);
+                       next_taps, stat, first);
     else
       launch_one<false>(scale, bpc, grid, block, stream, io, g, sc, taps,
-                        next_taps, stat, s0);
+                        next_taps, stat, first);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
       return e;
@@ -556,10 +666,11 @@ hipError_t scale0_resident_blocks(int bpc, int *blocks) {
   int per_cu = 0;
   hipError_t e =
       bpc == 8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint8_t, true>, kThreads, 0)
+                     &per_cu, scale_kernel<8, 4, uint8_t, true, true>,
+                     kThreads, 0)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint16_t, true>, kThreads,
-                     0);
+                     &per_cu, scale_kernel<8, 4, uint16_t, true, true>,
+                     kThreads, 0);
   int dev = 0, cus = 0;
   if (e == hipSuccess)
     e = hipGetDevice(&dev);

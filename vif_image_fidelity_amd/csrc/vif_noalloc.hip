@@ -4,13 +4,16 @@
 // nothing (for callers that cannot allocate device or pinned memory).
 //
 // The array `scratch` holds, per call, the pyramid planes of scales 1..3,
-// the four scales' term buffers, the row sums and the eight per-scale sums.
+// the term buffers of scales 1..3, scale 0's row-sum carries (cleared at the
+// start of every call), the row sums and the eight per-scale sums.
 // Its device address comes from hipGetSymbolAddress, once per device with
 // that device current (the array's name in host code is only a stand-in for
 // the symbol); kernels receive that address.  Every call on a device uses
 // the same array, so calls that overlap on one device race: the caller
 // serialises them (one stream, or one host thread at a time).  The kernels
-// write every word they read before reading it, so nothing is cleared.
+// write every word they read before reading it, except scale 0's carries
+// (a tile waits until its left neighbour's word carries the call's tag),
+// which a small kernel clears first.
 //
 // The row sums stay on the device: a small kernel adds each scale's rows
 // top to bottom in fp32, in the order the host adds them for vif_score
@@ -55,9 +58,13 @@ hipError_t scratch_address(int dev, unsigned char **p) {
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-// Offsets (bytes) of one call's buffers in the array.
+// Offsets (bytes) of one call's buffers in the array: the pyramid planes of
+// scales 1..3, the term buffers of scales 1..3, scale 0's row-sum carries,
+// the row sums, and the eight sums followed by the carry-wait error word.
 struct Layout {
-  size_t pyr_ref[kScales], pyr_dist[kScales], terms[kScales], rows, sums;
+  size_t pyr_ref[kScales], pyr_dist[kScales], terms[kScales], carry, rows,
+      sums;
+  size_t carry_words;
   size_t total;
 };
 
@@ -71,15 +78,19 @@ Layout layout(const ScaleGeom (&g)[kScales], int total_rows) {
     L.pyr_dist[s] = off;
     off += plane;
   }
-  for (int s = 0; s < kScales; ++s) {
+  for (int s = 1; s < kScales; ++s) {
     L.terms[s] = off;
     off += round256(sizeof(float) * g[s].strips * term_groups(g[s].w) *
                     kSeq * 4);
   }
+  L.carry = off;
+  L.carry_words = static_cast<size_t>(g[0].strips) *
+                  (g[0].ntx > 1 ? g[0].ntx - 1 : 1) * kSeq;
+  off += round256(sizeof(unsigned long long) * L.carry_words);
   L.rows = off;
   off += round256(sizeof(float) * 2 * total_rows);
   L.sums = off;
-  off += round256(sizeof(float) * 8);
+  off += round256(sizeof(float) * 8 + sizeof(int));
   L.total = off;
   return L;
 }
@@ -88,6 +99,19 @@ struct SumArgs {
   const float *rows[kScales]; // 2 floats per row of scale s
   int h[kScales];
 };
+
+// Clears the carries and the error word: the array's earlier contents are
+// another call's (or another geometry's), and every carry of this call
+// must read as not yet written until its tile writes it (tag 1).
+__global__ void clear_kernel(unsigned long long *carry, size_t words,
+                             int *err) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       i < words; i += stride)
+    carry[i] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    *err = 0;
+}
 
 constexpr int kSumChunk = 2048; // rows per LDS chunk
 
@@ -158,7 +182,9 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
     ra.w[s] = ws;
     ra.h[s] = hs;
     ra.strips[s] = g[s].strips;
-    ra.pair_base[s + 1] = ra.pair_base[s] + (g[s].strips + 1) / 2;
+    // scale 0's rows are summed inside its kernel (chained across tiles)
+    ra.pair_base[s + 1] =
+        ra.pair_base[s] + (s == 0 ? 0 : (g[s].strips + 1) / 2);
     sa.h[s] = hs;
   }
   const Layout L = layout(g, rows);
@@ -176,6 +202,10 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
   };
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const StatArgs stat = make_stat_args(o.sigma_nsq, o.enhn_gain_limit);
+  int *err = reinterpret_cast<int *>(at(L.sums) + 8);
+  auto *carry = reinterpret_cast<unsigned long long *>(base + L.carry);
+  clear_kernel<<<256, 256, 0, st>>>(carry, L.carry_words, err);
+  e = hipGetLastError();
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
     ScaleIO io = {};
     io.in_ref[0] = s == 0 ? ref : at(L.pyr_ref[s]);
@@ -184,8 +214,16 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
       io.next_ref = at(L.pyr_ref[s + 1]);
       io.next_dist = at(L.pyr_dist[s + 1]);
     }
-    io.terms = at(L.terms[s]);
+    if (s > 0)
+      io.terms = at(L.terms[s]);
     if (s == 0) {
+      io.carry = carry;
+      io.carry_tag = 1;
+      io.strips = g[0].strips;
+      io.ntx = g[0].ntx;
+      io.rows = at(L.rows);
+      io.rows_stride = static_cast<size_t>(2) * rows;
+      io.err = err;
       const uintptr_t align = bpc == 8 ? 8 : 16;
       io.vec_in = w % 8 == 0 &&
                   reinterpret_cast<uintptr_t>(ref) % align == 0 &&
@@ -195,24 +233,28 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
                      taps[s + 1 < kScales ? s + 1 : s], stat, st);
   }
   for (int s = 0; s < kScales; ++s) {
-    ra.terms[s] = at(L.terms[s]);
+    ra.terms[s] = s > 0 ? at(L.terms[s]) : nullptr;
     ra.rows[s] = at(L.rows) + 2 * row_base[s];
     sa.rows[s] = ra.rows[s];
   }
   if (e == hipSuccess)
     e = launch_rowsum(ra, ra.pair_base[kScales], 1, st);
+  // (the sums kernel reads the rows the scale-0 kernel and the row-sum
+  // kernel wrote, in stream order)
   if (e == hipSuccess) {
     scale_sums_kernel<<<1, 256, 0, st>>>(sa, at(L.sums));
     e = hipGetLastError();
   }
-  float sums[8];
+  float back[9]; // the eight sums and the error word
   if (e == hipSuccess)
-    e = hipMemcpyAsync(sums, at(L.sums), sizeof(sums), hipMemcpyDeviceToHost,
+    e = hipMemcpyAsync(back, at(L.sums), sizeof(back), hipMemcpyDeviceToHost,
                        st);
   if (e == hipSuccess)
     e = hipStreamSynchronize(st);
   if (e != hipSuccess)
     return status_from_hip(e);
-  scores_from_sums(sums, o, out);
+  if (__builtin_bit_cast(int, back[8]) != 0)
+    return set_status(VIF_EHIP, hipErrorLaunchTimeOut);
+  scores_from_sums(back, o, out);
   return set_status(VIF_OK);
 }
