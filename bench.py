@@ -606,7 +606,7 @@ def main():
 
     if args.mode == "strip":
         res = steady_state(V, frames4k, w, h, bpc, args.steps, args.warmup,
-                           batch=batch, reps=reps, prof_kinds=0x1F,
+                           batch=batch, reps=reps, prof_kinds=0xF,
                            strip=STRIP_SHARE)
         kt = {k: round(1000.0 * v[0] / max(v[1], 1), 2)
               for k, v in res["kernel"].items()}
@@ -642,7 +642,7 @@ def main():
 
     # per-kernel split (all kinds timed; separate run, not the headline)
     allk = steady_state(V, frames4k, w, h, bpc, min(args.steps, 100), 5,
-                        batch=batch, reps=1, prof_kinds=0x1F)
+                        batch=batch, reps=1, prof_kinds=0xF)
     split = {k: round(1000.0 * v[0] / max(v[1], 1), 2)
              for k, v in allk["kernel"].items()}
 

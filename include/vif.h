@@ -94,8 +94,8 @@ void vif_default_options(vif_options *opt);
  *          scored frame is 16x16 (ADR-1444, Consequences).
  *   bpc    8, 10, 12 or 16 (Research-2130, Sources: 8-bit samples used as
  *          they are, wider samples divided by 4, 16 or 256).
- * Allocates every device buffer the context needs (pyramid planes, term
- * planes, row sums) and a pinned host buffer, on the device current at the
+ * Allocates every device buffer the context needs (pyramid planes, the
+ * row sums' hand-over words) and pinned host buffers (row sums), on the device current at the
  * call, and computes the taps on the host.  Work goes to the default stream
  * unless vif_set_stream() is called.  Returns NULL on failure; vif_errno()
  * then gives VIF_EINVAL, VIF_ENOMEM or VIF_EHIP.  Geometry is refused here,
@@ -256,19 +256,19 @@ int vif_scores_from_rows(int w, int h, const vif_options *opt,
  * the bits of out.  ref, dist and out as for vif_score (device frames, host
  * out).
  * The buffers the kernels need beyond the frames and out (pyramid planes,
- * term buffers, row sums, the eight sums) live in one array of
+ * the row sums' hand-over words, row sums, the eight sums) live in one
+ * array of
  * VIF_NOALLOC_SCRATCH bytes of device memory that the library defines: each
  * device the call runs on holds it from the call's first use there until
  * the process ends.  A frame whose buffers do not fit is refused with
- * VIF_ETOOBIG before any work is queued (3840x2160 needs about 105 MiB,
- * 4096x2160 about 112 MiB).
+ * VIF_ETOOBIG before any work is queued (3840x2160 needs about 22 MiB).
  * Synchronous: returns once out is written (it synchronises hip_stream).
  * Every call on one device shares that device's array, which keeps the last
  * call's contents: calls that overlap on one device (two streams or two host
  * threads at once) race, and the caller must serialise them.  VIF_EINVAL for
  * bad arguments (as vif_create_ex and vif_score), VIF_EHIP for a HIP error.
  */
-#define VIF_NOALLOC_SCRATCH (128L << 20)
+#define VIF_NOALLOC_SCRATCH (32L << 20)
 int vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
                       const void *ref, const void *dist, void *hip_stream,
                       double out[8]);
@@ -336,7 +336,7 @@ int vif_taps(int scale, float *taps);
 
 /*
  * vif_set_profiling -- kinds is a bit mask of kernel kinds (bit k = kind k
- * of vif_get_kernel_times; 0x1f = all, 0 = off).  Frames submitted from
+ * of vif_get_kernel_times; 0xf = all, 0 = off).  Frames submitted from
  * then on record a pair of HIP events around each launch of those kinds on
  * the stream it runs on, and vif_collect accumulates their durations (a
  * small cost per event).  Every call resets the totals; VIF_EINVAL while
@@ -347,15 +347,14 @@ int vif_set_profiling(vif_ctx *ctx, int kinds);
 /*
  * vif_get_kernel_times -- accumulated kernel durations in milliseconds and
  * launch counts since profiling was enabled, one entry per kernel kind:
- *   0..3  the kernel of scale s (filter, statistic, terms, next scale's
- *         planes; scale 0's also adds its rows' terms in order, carrying
- *         each row's sum from tile to tile)
- *   4     the ordered row sums of scales 1..3
+ *   0..3  the kernel of scale s (filter, statistic, next scale's planes,
+ *         and the ordered row sums: each row's fp32 sum is carried from tile
+ *         to tile inside the kernel)
  * A launch here is one kind's work for one submission (all its frames): one
  * kernel launch, or several in a row for a scale with more than 65535 strips
  * of 16 rows, timed as one.
  * ms and launches hold at least `capacity` entries (either may be NULL).
- * Returns the number of kinds (5) or VIF_EINVAL.
+ * Returns the number of kinds (4) or VIF_EINVAL.
  */
 int vif_get_kernel_times(const vif_ctx *ctx, double *ms, long *launches,
                          int capacity);

@@ -5,11 +5,11 @@
  * same inline code, not copies) over caller-provided arrays, so a test can
  * compare the device's arithmetic with the host's bit for bit before
  * trusting the pipeline.  The pattern follows ADR-1444 "float_vif_hip runs
- * the arithmetic of the CUDA twin ...", Decision: the device's fp64 add and
- * divide were compared with the host's over 33.5 million operand pairs from
- * 2^-40 to 2^40 and six noise variances, checking the sum, the quotient and
- * both fp32 roundings of one plus the quotient; and Consequences: a
- * device-math test compares the shared arithmetic with the CPU's.
+ * the arithmetic of the CUDA twin ...", Decision (a host comparison of the
+ * device's fp64 add and divide over tens of millions of operand pairs and
+ * several noise variances, on the sum, the quotient and both fp32 roundings
+ * of one plus the quotient) and Consequences (a device-math test of the
+ * shared arithmetic against the CPU's).
  *
  * Every pointer is a DEVICE pointer owned by the caller; n >= 0 elements;
  * stream is a hipStream_t as void* (NULL = default stream).  Each call is
@@ -59,6 +59,15 @@ int vif_selftest_statistic(const float *mu1, const float *mu2,
                            const float *xx, const float *yy, const float *xy,
                            long n, double nsq, double gain_limit, float *num,
                            float *den, void *stream);
+
+/* The bounded wait of scale 0's row-sum hand-over, forced from the host:
+ * runs only the second tile column of a 224x16 frame of zeros, whose left
+ * neighbour never hands its words over, so every waiting lane must give up
+ * after its bounded number of reads (about a tenth of a second), raise the
+ * error word and store NaN; the kernel still ends.  Writes *raised = the
+ * error word (1 expected) and *row = the first row's numerator sum (NaN
+ * expected).  Host pointers; allocates its own small device buffers. */
+int vif_selftest_carry_wait(int *raised, float *row, void *stream);
 
 #ifdef __cplusplus
 }

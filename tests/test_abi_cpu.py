@@ -203,7 +203,7 @@ def test_binding_constants_match_headers():
 def test_package_import_needs_no_gpu():
     import vif_image_fidelity_amd as V
     assert V.VIF_OK == 0
-    assert len(V.KERNEL_KINDS) == 5
+    assert len(V.KERNEL_KINDS) == 4
     assert V.QUEUE_DEPTH == 3
     assert len(V.DEBUG_NAMES) == 15 and V.DEBUG_NAMES[4] == "vif"
 

@@ -224,3 +224,26 @@ def test_selftests_reject_bad_options(dev):
             _lib.VIF_EINVAL
     assert L.vif_selftest_ratios(None, None, -2.0, 0, None, None, None) == \
         _lib.VIF_EINVAL
+
+
+def test_carry_wait_gives_up_and_reports(dev):
+    """Scale 0 hands each row's fp32 sum from tile to tile; a tile waits for
+    its left neighbour's word with a bounded number of reads.  Forced from
+    the host: only the second tile column of a two-column frame runs, so the
+    words it waits for never arrive.  The kernel must still end, raise its
+    error word and store NaN rather than a sum."""
+    import ctypes
+    import time
+    from vif_image_fidelity_amd import _lib
+    raised = ctypes.c_int(0)
+    row = np.zeros(1, dtype=np.float32)
+    t0 = time.time()
+    rc = _lib.load().vif_selftest_carry_wait(
+        ctypes.byref(raised), row.ctypes.data_as(ctypes.POINTER(
+            ctypes.c_float)), None)
+    took = time.time() - t0
+    print("carry wait gave up after %.3f s" % took, flush=True)
+    assert rc == _lib.VIF_OK
+    assert raised.value == 1
+    assert np.isnan(row[0])
+    assert took < 30

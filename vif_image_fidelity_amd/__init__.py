@@ -267,13 +267,13 @@ class Vif:
             raise VifError(rc, "vif_get_row_sums")
         return rows
 
-    def set_profiling(self, kinds=0x1F):
-        """Time the kernel kinds in the bit mask (0x1F all, 0 off); a list
+    def set_profiling(self, kinds=0xF):
+        """Time the kernel kinds in the bit mask (0xF all, 0 off); a list
         of kind names is accepted too."""
         if isinstance(kinds, (list, tuple)):
             kinds = sum(1 << KERNEL_KINDS.index(k) for k in kinds)
         elif kinds is True:
-            kinds = 0x1F
+            kinds = (1 << len(KERNEL_KINDS)) - 1
         elif kinds is False or kinds is None:
             kinds = 0
         rc = _lib.vif_set_profiling(self._ctx, int(kinds))

@@ -16,7 +16,7 @@ VIF_EINVAL = -1
 VIF_ENOMEM = -2
 VIF_EHIP = -3
 VIF_ETOOBIG = -4
-NOALLOC_SCRATCH = 128 << 20
+NOALLOC_SCRATCH = 32 << 20
 NSCALES = 4
 MAX_TAPS = 17
 QUEUE_DEPTH = 3
@@ -25,7 +25,7 @@ STRIP_INFO = 10
 MIN_SIDE = 16
 MAX_PIXELS = 1 << 27
 NDEBUG = 15
-KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3", "rowsum")
+KERNEL_KINDS = ("scale0", "scale1", "scale2", "scale3")
 FSSIM_TAPS = 11
 FSSIM_QUEUE_DEPTH = 3
 FSSIM_MAX_PIXELS = 1 << 27
@@ -117,6 +117,7 @@ def load():
         "vif_selftest_statistic": ([vp, vp, vp, vp, vp, ctypes.c_long,
                                     ctypes.c_double, ctypes.c_double, vp, vp,
                                     vp], ip),
+        "vif_selftest_carry_wait": ([ctypes.POINTER(ip), fp, vp], ip),
         "fssim_create": ([ip, ip, ip], vp),
         "fssim_create_batch": ([ip, ip, ip, ip], vp),
         "fssim_submit_batch": ([vp, ip, ctypes.POINTER(vp),
@@ -157,7 +158,7 @@ def exported_symbols():
             "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
             "vif_selftest_log2", "vif_selftest_ratios",
-            "vif_selftest_statistic",
+            "vif_selftest_statistic", "vif_selftest_carry_wait",
             "fssim_create", "fssim_create_batch", "fssim_submit_batch",
             "fssim_destroy", "fssim_geometry", "fssim_score",
             "fssim_submit", "fssim_collect", "fssim_pending",

@@ -5,14 +5,13 @@
 // each kernel processes in one launch, blockIdx.z being the frame) has a slot
 // of a three-slot ring, and every slot its own stream and buffers (pyramid
 // planes, term buffers, and its row sums in pinned host memory, each sized
-// for max_batch frames).  The slot's stream runs the four per-scale kernels (filter,
-// statistic, terms, next scale's planes; scale 0's kernel also carries each
-// row's fp32 sum from tile to tile and stores the row sums) and the ordered
-// row sums of scales 1..3 (one launch); the row sums go straight into the
-// host buffer, two floats per row per scale: one read-back per frame with
-// no copy call (ADR-1422 "float_vif_sycl computes the CPU's arithmetic
-// ...", Decision: the row sums come back in one transfer and the host adds
-// them).
+// for max_batch frames).  The slot's stream runs the four per-scale kernels
+// (filter, statistic, next scale's planes, and the ordered row sums, each
+// row's fp32 sum carried from tile to tile inside the kernel); the row sums
+// go straight into the host buffer, two floats per row per scale: one
+// read-back per frame with no copy call (ADR-1422 "float_vif_sycl computes
+// the CPU's arithmetic ...", Decision: the row sums come back in one
+// transfer and the host adds them).
 // Frames in host memory are first copied into the slot's own frame buffers
 // on the slot's stream (vif_submit_host).
 // Consecutive frames rotate over the slots, so one frame's small
@@ -20,10 +19,10 @@
 // GPU.  When one scale-0 kernel covers the GPU twice over, consecutive
 // frames' scale-0 kernels run one after the other (a stream wait on the
 // previous frame's scale-0 event): two of them side by side gain nothing,
-// and each launch's duration then is its own.  A submission is six runtime
-// calls (five launches, one event), plus an event and that stream wait when
+// and each launch's duration then is its own.  A submission is five runtime
+// calls (four launches, one event), plus an event and that stream wait when
 // the scale-0 kernels are ordered (and a launch more per scale for every
-// 65535 strips beyond the first: see launch_scale).
+// 65535 tile columns beyond the first: see launch_scale).
 //
 // The slot streams are blocking streams, so they are ordered after work on
 // the default stream (where a caller typically fills the frames); a caller
@@ -53,21 +52,20 @@ using vifk::destroy_event;
 
 constexpr int kDepth = VIF_QUEUE_DEPTH;
 
-constexpr int kKinds = kScales + 1; // scale kernels 0..3, row sums
+constexpr int kKinds = kScales; // the scale kernels 0..3
 
 struct Slot {
   float *pyr_ref[kScales] = {};   // [0] unused: scale 0 reads the frames;
   float *pyr_dist[kScales] = {};  // max_batch planes each, plane_elems apart
   void *frame_ref = nullptr;      // device copies of host frames
   void *frame_dist = nullptr;
-  float *terms[kScales] = {};     // term buffers of scales 1..3
-  unsigned long long *carry = nullptr; // scale 0's row sums between tiles
+  unsigned long long *carry[kScales] = {}; // row sums between tiles
   float *rows_host = nullptr;     // pinned, written by the kernels
   int *err_host = nullptr;        // pinned, raised by a carry wait that
                                   // gave up
   hipStream_t stream = nullptr;   // owned: all of the slot's work
   hipEvent_t submitted = nullptr; // on the caller's stream
-  hipEvent_t done = nullptr;      // on the slot's stream, after the row sums
+  hipEvent_t done = nullptr;      // on the slot's stream, after scale 3
   hipEvent_t s0_end = nullptr;    // on the slot's stream, after scale 0
   hipEvent_t s0_done = nullptr;   // the event after this submission's scale
                                   // 0: s0_end, or the timing event there
@@ -90,7 +88,7 @@ struct vif_ctx {
   Slot slots[kDepth];
   int max_batch = 1;                   // frames one submission may carry
   size_t plane_elems[kScales] = {};    // floats per frame, pyramid plane
-  size_t terms_elems[kScales] = {};    // floats per frame, term buffer
+  size_t carry_words[kScales] = {};    // hand-over words per frame
   int total_rows = 0;             // rows of the planes, all scales
   int row_base[kScales] = {};
   // the rows the context reports: scale s's planes' rows [own0[s],
@@ -101,10 +99,8 @@ struct vif_ctx {
   int nown[kScales] = {};
   int own_base[kScales] = {};
   int own_rows = 0;
-  int rowsum_waves = 0;
   bool order_scale0 = false; // consecutive frames' scale-0 kernels ordered
   unsigned carry_tag = 0;    // tag of the last submission's carries
-  vifk::RowSumArgs rowsum = {}; // per-frame fields filled at submit
   long head = 0, tail = 0;   // submitted / collected frame counts
   long shead = 0, stail = 0; // submitted / released slot counts
   float sums[8] = {};
@@ -153,11 +149,9 @@ void free_all(vif_ctx *c) {
         (void)hipFree(sl.pyr_ref[s]);
       if (sl.pyr_dist[s])
         (void)hipFree(sl.pyr_dist[s]);
-      if (sl.terms[s])
-        (void)hipFree(sl.terms[s]);
+      if (sl.carry[s])
+        (void)hipFree(sl.carry[s]);
     }
-    if (sl.carry)
-      (void)hipFree(sl.carry);
     if (sl.err_host)
       (void)hipHostFree(sl.err_host);
     if (sl.frame_ref)
@@ -216,19 +210,18 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
       io.next_dist = sl.pyr_dist[s + 1];
       io.next_stride = ctx->plane_elems[s + 1];
     }
-    io.terms = sl.terms[s];
-    io.terms_stride = ctx->terms_elems[s];
-    if (s == 0) {
-      // the row sums of scale 0 are chained across each row's tiles inside
-      // the kernel: a fresh tag per submission marks this launch's carries
+    // the row sums are chained across each row's tiles inside the kernel:
+    // a fresh tag per submission marks this submission's hand-over words
+    if (s == 0)
       ctx->carry_tag = ctx->carry_tag + 1 == 0 ? 1 : ctx->carry_tag + 1;
-      io.carry = sl.carry;
-      io.carry_tag = ctx->carry_tag;
-      io.strips = ctx->geom[0].strips;
-      io.ntx = ctx->geom[0].ntx;
-      io.rows = sl.rows_host + 2 * ctx->row_base[0];
-      io.rows_stride = static_cast<size_t>(2) * ctx->total_rows;
-      io.err = sl.err_host;
+    io.carry = sl.carry[s];
+    io.carry_tag = ctx->carry_tag;
+    io.strips = ctx->geom[s].strips;
+    io.ntx = ctx->geom[s].ntx;
+    io.rows = sl.rows_host + 2 * ctx->row_base[s];
+    io.rows_stride = static_cast<size_t>(2) * ctx->total_rows;
+    io.err = sl.err_host;
+    if (s == 0) {
       // 8 samples per load: rows start on 8-sample boundaries and the
       // planes are aligned to 8 samples' bytes
       const uintptr_t align = ctx->bpc == 8 ? 8 : 16;
@@ -256,20 +249,6 @@ int submit_frames(vif_ctx *ctx, int n, const void *const *refs,
         e = hipEventRecord(sl.s0_end, st);
     }
   }
-  vifk::RowSumArgs ra = ctx->rowsum;
-  for (int s = 0; s < kScales; ++s) {
-    ra.terms[s] = sl.terms[s];
-    ra.terms_stride[s] = ctx->terms_elems[s];
-    ra.rows[s] = sl.rows_host + 2 * ctx->row_base[s];
-  }
-  ra.rows_stride = static_cast<size_t>(2) * ctx->total_rows;
-  const bool timed = (sl.prof_mask >> kScales) & 1;
-  if (e == hipSuccess && timed)
-    e = hipEventRecord(sl.prof[kScales][0], st);
-  if (e == hipSuccess)
-    e = vifk::launch_rowsum(ra, ctx->rowsum_waves, n, st);
-  if (e == hipSuccess && timed)
-    e = hipEventRecord(sl.prof[kScales][1], st);
   if (e == hipSuccess)
     e = hipEventRecord(sl.done, st);
   if (e != hipSuccess)
@@ -452,23 +431,16 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
     c->own_base[s] = own;
     own += sr.nown[s];
     c->plane_elems[s] = static_cast<size_t>(ws) * hs;
-    // scale 0's row sums are chained inside its kernel: no term buffer
-    c->terms_elems[s] = s == 0 ? 0
-                               : static_cast<size_t>(g.strips) *
-                                     vifk::term_groups(ws) * vifk::kSeq * 4;
+    // one hand-over word per sequence and inner tile boundary of a row
+    c->carry_words[s] = static_cast<size_t>(g.strips) *
+                        (g.ntx > 1 ? g.ntx - 1 : 1) * vifk::kSeq;
     const int nt = vifk::gaussian_taps(s, c->taps[s].t);
     // the kernels rely on bitwise symmetric taps (see tap() there)
     for (int k = 0; k < nt; ++k)
       if (std::memcmp(&c->taps[s].t[k], &c->taps[s].t[nt - 1 - k],
                       sizeof(float)) != 0)
         e = hipErrorInvalidValue;
-    c->rowsum.w[s] = ws;
-    c->rowsum.h[s] = hs;
-    c->rowsum.strips[s] = g.strips;
-    c->rowsum.pair_base[s + 1] =
-        c->rowsum.pair_base[s] + (s == 0 ? 0 : (g.strips + 1) / 2);
   }
-  c->rowsum_waves = c->rowsum.pair_base[kScales];
   // order consecutive scale-0 kernels when one covers the device's resident
   // blocks at least twice: two side by side then gain nothing, and the wait
   // (a cross-stream dependency, a few tens of microseconds of host time) is
@@ -500,16 +472,14 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
       e = hipMalloc(&sl.frame_ref, frame_bytes);
     if (e == hipSuccess)
       e = hipMalloc(&sl.frame_dist, frame_bytes);
-    for (int s = 1; s < kScales && e == hipSuccess; ++s)
-      e = dev_alloc(&sl.terms[s], nb * c->terms_elems[s]);
-    // scale 0's carries, cleared once: every launch writes its own tag
-    const size_t carries = nb * c->geom[0].strips *
-                           (c->geom[0].ntx > 1 ? c->geom[0].ntx - 1 : 1) *
-                           vifk::kSeq;
-    if (e == hipSuccess)
-      e = dev_alloc(&sl.carry, carries);
-    if (e == hipSuccess)
-      e = hipMemset(sl.carry, 0, carries * sizeof(unsigned long long));
+    // the hand-over words, cleared once: every submission writes its own
+    // tag
+    for (int s = 0; s < kScales && e == hipSuccess; ++s) {
+      e = dev_alloc(&sl.carry[s], nb * c->carry_words[s]);
+      if (e == hipSuccess)
+        e = hipMemset(sl.carry[s], 0,
+                      nb * c->carry_words[s] * sizeof(unsigned long long));
+    }
     if (e == hipSuccess)
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.err_host), sizeof(int),
                         hipHostMallocCoherent);

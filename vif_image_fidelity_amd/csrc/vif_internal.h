@@ -49,65 +49,43 @@ struct OptionValues {
 bool options_valid(const OptionValues &o);
 StatArgs make_stat_args(double nsq, double gain_limit);
 
-// Terms of a 16-row strip: 32 sequences (16 rows x {num, den}).  In the
-// term buffer of a scale, strip p holds term_groups(w) groups of 4 columns,
-// each group the 32 sequences' 4 values: floats
-// [(p * term_groups(w) + g) * 128 + seq * 4 + (x % 4)] for column x = 4g + ...
-// In LDS a tile keeps them as [seq][x] with pitch kTermPitch.
+// Terms of a 16-row strip: 32 sequences (16 rows x {num, den}).  In LDS a
+// tile keeps them as [seq][x] with pitch kTermPitch.
 constexpr int kSeq = 32;
 constexpr int kTermPitch = kTileW + 4;
 
-__host__ __device__ inline int term_groups(int w) { return (w + 3) / 4; }
-
-// Frames one launch may carry: blockIdx.z of the scale kernels, blockIdx.y
-// of the row sums.
+// Frames one launch may carry (grid x of the scale kernels runs over the
+// strips of every frame).
 constexpr int kMaxBatch = 16;
-// Blocks per launch in grid dimension y (the runtime allows 65536; a frame
-// with more rows of tiles takes several launches).
+// Blocks per launch in grid dimension y (the runtime allows 65536; a plane
+// with more columns of tiles takes several launches).
 constexpr int kMaxGridY = 65535;
 
 // Inputs and outputs of one launch of a scale kernel for n frames: frame z
 // reads in_ref[z] / in_dist[z] (the caller's frames at scale 0, the
-// context's planes above) and writes the next scale's planes at
-// next_* + z * next_stride and its terms at terms + z * terms_stride
-// (strides in floats).
+// context's planes above) and writes the next scale's planes at next_* + z *
+// next_stride (floats) and its rows' sums at rows[z * rows_stride + 2 * y +
+// c] (c = 0 for the numerator, 1 for the denominator).  Each row's sum is
+// carried from tile to tile in carry: n * strips * (ntx - 1) * 32 words (at
+// least 32), written with the tag carry_tag (never 0, new for every launch
+// that reuses the words); err is raised if a wait for a word gives up.
+// strips and ntx are the scale's.
 struct ScaleIO {
   const void *in_ref[kMaxBatch];
   const void *in_dist[kMaxBatch];
   float *next_ref;
   float *next_dist;
-  float *terms;
   size_t next_stride;
-  size_t terms_stride;
   // scale 0: every in_ref/in_dist plane may be read 8 samples per load
   // (width a multiple of 8, planes 8-byte aligned for 8-bit samples,
   // 16-byte for 16-bit ones); 0 otherwise and at scales 1-3
   int vec_in;
-  // scale 0 only (its row sums are chained from tile to tile instead of
-  // going through a term buffer): carry holds n * strips * (ntx - 1) * 32
-  // words (at least one), written with the tag carry_tag (never 0, new for
-  // every launch that reuses the buffer); rows receives the row sums
-  // (rows[z * rows_stride + 2 * y + c]); err is raised if a wait for a
-  // carry gives up.  strips and ntx are the scale's.
   unsigned long long *carry;
   unsigned carry_tag;
   int strips, ntx;
   float *rows;
   size_t rows_stride;
   int *err;
-};
-
-// Arguments of the row-sum kernel (all four scales in one launch): scale s
-// owns the waves [pair_base[s], pair_base[s+1]), one wave per two strips;
-// frame z (blockIdx.y) reads terms[s] + z * terms_stride[s] and writes
-// rows[s] + z * rows_stride.
-struct RowSumArgs {
-  const float *terms[kScales];
-  float *rows[kScales]; // rows[s][2*y + c], in pinned host memory
-  size_t terms_stride[kScales];
-  size_t rows_stride;
-  int w[kScales], h[kScales], strips[kScales];
-  int pair_base[kScales + 1];
 };
 
 // Host arithmetic on row sums (vif_rows.cpp).  scores_from_rows: rows
@@ -129,7 +107,7 @@ struct StripRows {
 };
 bool strip_rows(int h, int row0, int row1, StripRows *sr);
 
-// The option checks of the C ABI (vif_api.cpp).
+// The option checks of the C ABI (vif_options.cpp).
 bool options_ok(const vif_options &o);
 
 // Host tap generator (vif_taps.cpp).
@@ -144,24 +122,24 @@ struct ScaleGeom {
 };
 
 // Per-scale kernel for n frames (1 <= n <= kMaxBatch): filter, statistic,
-// terms and the next scale's planes.  At scale 0 the terms' row sums are
-// chained across the row's tiles inside the kernel (io.carry, io.rows): the
-// term buffer and the row-sum kernel serve scales 1..3 only.  io.in_* are the scale's planes (native
-// samples at scale 0, fp32 planes above); io.next_* receive the next scale's
-// planes (unused at scale 3); io.terms is the scale's term buffer (strips *
-// term_groups(w) * 128 floats per frame).
+// the next scale's planes and the ordered row sums (each row's sum carried
+// across the row's tiles inside the kernel).  io.in_* are the scale's planes
+// (native samples at scale 0, fp32 planes above); io.next_* receive the next
+// scale's planes (unused at scale 3).
 hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
                         const ScaleGeom &g, const TapArgs &taps,
                         const TapArgs &next_taps, const StatArgs &stat,
                         hipStream_t stream);
 
+// Only tile column `col` of scale 0's chained kernel, for one 8-bit frame
+// (the check of the hand-over's bounded wait; see vif_selftest.hip).
+hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
+                                const TapArgs &taps, const TapArgs &next_taps,
+                                const StatArgs &stat, int col,
+                                hipStream_t stream);
+
 // Blocks of the scale-0 kernel the current device keeps resident at once
 // (blocks per CU times CUs).
 hipError_t scale0_resident_blocks(int bpc, int *blocks);
-
-// Ordered row sums of all scales of n frames (`waves` = pair_base[4] per
-// frame).
-hipError_t launch_rowsum(const RowSumArgs &args, int waves, int n,
-                         hipStream_t stream);
 
 }  // namespace vifk

@@ -15,12 +15,9 @@
 //      and the two terms, staged in LDS;
 //   4. the horizontal pass of the next scale's low-pass at even columns,
 //      written as the next scale's fp32 planes (2x decimation);
-//   5. at scale 0, the ordered row sums themselves: each row's fp32
-//      accumulator is carried from tile to tile along the row (chain_rows),
-//      so scale 0 has no term buffer; at scales 1..3, the terms go to the
-//      scale's term buffer in the order the row sums read them.
-// A second kernel (one launch for scales 1..3) adds each of those rows'
-// terms in order.
+//   5. the ordered row sums themselves: each row's fp32 accumulator is
+//      carried from tile to tile along the row (chain_rows), and the row's
+//      last tile stores its sum; no term ever leaves the block.
 //
 // Every multiply and add is its own IEEE fp32 rounding (the library is
 // built with -ffp-contract=off), taps in ascending order, vertical pass
@@ -40,10 +37,6 @@
 namespace vifk {
 
 constexpr int kThreads = 256;
-
-// Four floats as the compiler's native vector type, for the non-temporal
-// load and store builtins.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Planes hold at most 2^27 samples, so a 32-bit offset addresses them.
 // The input tile stays in LDS in the plane's own sample type (one byte per
@@ -121,7 +114,7 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
   }
 }
 
-// Row sums carried from tile to tile (the scale-0 kernel).  The sum of a
+// Row sums carried from tile to tile.  The sum of a
 // row is one fp32 accumulator over its terms from left to right (ADR-1422
 // "float_vif_sycl computes the CPU's arithmetic ...", Context and Decision),
 // so a row that spans several tiles is a chain: tile tx continues the
@@ -205,33 +198,23 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
 // scale's planes, then the three second moments); the second round's
 // vertical results wait in registers until its write.
 //
-// Frame z = blockIdx.z of a batched launch reads io.in_ref[z], io.in_dist[z]
-// and writes at its own offsets of the next scale's planes and the terms.
-// Tile (blockIdx.x, strip0 + blockIdx.y): a frame with more strips than a
-// grid's y dimension allows is covered by several launches.
-template <int R, int RD, typename InT, bool kPow2, bool kChain>
+// Tile (tx, strip) of frame z: blockIdx.x = z * strips + strip runs
+// fastest, so consecutive blocks take the same tile column of every strip
+// and frame, and tx = first + blockIdx.y (a plane wider than a grid's y
+// dimension allows is covered by several launches).  Frame z reads
+// io.in_ref[z], io.in_dist[z] and writes at its own offsets of the next
+// scale's planes and the row sums.
+template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
     StatArgs stat, int first) {
-  // Tile (tx, strip) of frame z.  Term-buffer form: tx = blockIdx.x, strip =
-  // first + blockIdx.y, z = blockIdx.z.  Chained form: blockIdx.x = z *
-  // strips + strip runs fastest, so that consecutive blocks take the same
-  // tile column of every strip and frame, and tx = first + blockIdx.y.
-  int z, tx, strip;
-  if constexpr (kChain) {
-    z = static_cast<int>(blockIdx.x) / io.strips;
-    strip = static_cast<int>(blockIdx.x) - z * io.strips;
-    tx = first + static_cast<int>(blockIdx.y);
-  } else {
-    z = blockIdx.z;
-    tx = blockIdx.x;
-    strip = first + static_cast<int>(blockIdx.y);
-  }
+  const int z = static_cast<int>(blockIdx.x) / io.strips;
+  const int strip = static_cast<int>(blockIdx.x) - z * io.strips;
+  const int tx = first + static_cast<int>(blockIdx.y);
   const InT *__restrict__ ref = static_cast<const InT *>(io.in_ref[z]);
   const InT *__restrict__ dist = static_cast<const InT *>(io.in_dist[z]);
   float *__restrict__ next_ref = io.next_ref + z * io.next_stride;
   float *__restrict__ next_dist = io.next_dist + z * io.next_stride;
-  float *__restrict__ terms = kChain ? nullptr : io.terms + z * io.terms_stride;
   constexpr int N = 2 * R + 1;
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
@@ -473,117 +456,14 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads(); // terms complete in LDS
 
-  if constexpr (kChain) {
-    // 8. the ordered row sums, continued from the tile on the left: lane q
-    //    of wave 0 owns sequence q (row q / 2, component q % 2); it takes
-    //    the row's fp32 accumulator where the left tile left it (0 at the
-    //    first tile), adds this tile's terms left to right, and hands the
-    //    accumulator on, or stores the row's sum at the last tile.
-    if (tid < kSeq)
-      chain_rows(io, sT + tid * kTermPitch, min(kTileW, w - x0), z, strip,
-                 tx, y0 + (tid >> 1), h, tid);
-    return;
-  }
-  // 8. terms to the strip's term buffer: groups of 4 columns, each group
-  //    holding the 32 sequences' 4 values ([g][seq][4] floats); this tile's
-  //    28 groups are one contiguous 14 KiB block.  The stores are
-  //    non-temporal: the row sums read the terms only after the frame's
-  //    last scale, so they should not displace the input tiles in L2.
-  {
-    f32x4 *dst = reinterpret_cast<f32x4 *>(
-        terms + (static_cast<size_t>(strip) * term_groups(w) + x0 / 4) *
-                    (kSeq * 4));
-    const int groups = min(kTileW, w - x0 + 3) / 4;
-    for (int i = tid; i < groups * kSeq; i += kThreads) {
-      const int g = i / kSeq;
-      const int q = i - g * kSeq;
-      __builtin_nontemporal_store(
-          *reinterpret_cast<const f32x4 *>(sT + q * kTermPitch + 4 * g),
-          dst + i);
-    }
-  }
-}
-
-// Ordered row sums of scales 1..3, one launch per submission (scale 0's are
-// chained inside its kernel).  One wave owns two 16-row strips of one scale: lane l adds sequence l%32 (row (l%32)/2,
-// component l%2) of strip 2p + l/32 left to right into one fp32
-// accumulator starting at 0.0f, exactly the serial loop over the row
-// (ADR-1422 "float_vif_sycl computes the CPU's arithmetic ...", Context and
-// Decision: one fp32 sum per row, in order, no group or atomic reduction).
-// Each float4 load brings four consecutive columns of a lane's sequence;
-// two register batches keep one batch of loads in flight while the other is
-// added.  No LDS, so these waves fit beside a running scale kernel.  The
-// loads are non-temporal: each term is read once.
-constexpr int kRowBatch = 12; // float4 loads per batch and lane
-
-__device__ __forceinline__ void load_batch(f32x4 (&v)[kRowBatch],
-                                           const f32x4 *__restrict__ src,
-                                           int g0, int groups) {
-#pragma unroll
-  for (int k = 0; k < kRowBatch; ++k) {
-    const int g = min(g0 + k, groups - 1); // in-bounds; extras are not added
-    v[k] = __builtin_nontemporal_load(src + static_cast<size_t>(g) * kSeq);
-  }
-}
-
-__device__ __forceinline__ float add_batch(float acc, const f32x4 (&v)[kRowBatch],
-                                           int x0, int w) {
-  if (x0 + 4 * kRowBatch <= w) {
-#pragma unroll
-    for (int k = 0; k < kRowBatch; ++k) {
-      acc = acc + v[k].x;
-      acc = acc + v[k].y;
-      acc = acc + v[k].z;
-      acc = acc + v[k].w;
-    }
-  } else {
-    for (int k = 0; k < kRowBatch; ++k) {
-      const int x = x0 + 4 * k;
-      if (x < w)
-        acc = acc + v[k].x;
-      if (x + 1 < w)
-        acc = acc + v[k].y;
-      if (x + 2 < w)
-        acc = acc + v[k].z;
-      if (x + 3 < w)
-        acc = acc + v[k].w;
-    }
-  }
-  return acc;
-}
-
-__global__ __launch_bounds__(64) void rowsum_kernel(RowSumArgs a) {
-  const int wave = blockIdx.x;
-  const int z = blockIdx.y; // frame of a batched launch
-  int s = 0;
-  while (s + 1 < kScales && wave >= a.pair_base[s + 1])
-    ++s;
-  const int lane = threadIdx.x;
-  const int strips = a.strips[s];
-  int strip = 2 * (wave - a.pair_base[s]) + (lane >> 5);
-  const bool live = strip < strips;
-  strip = live ? strip : strips - 1; // a real strip; its sums are dropped
-  const int seq = lane & 31;
-  const int w = a.w[s];
-  const int groups = term_groups(w);
-  const f32x4 *src = reinterpret_cast<const f32x4 *>(
-                         a.terms[s] + z * a.terms_stride[s] +
-                         static_cast<size_t>(strip) * groups * (kSeq * 4)) +
-                     seq;
-  float acc = 0.0f;
-  f32x4 va[kRowBatch], vb[kRowBatch];
-  load_batch(va, src, 0, groups);
-  for (int g = 0; g < groups; g += 2 * kRowBatch) {
-    load_batch(vb, src, g + kRowBatch, groups);
-    acc = add_batch(acc, va, 4 * g, w);
-    if (g + kRowBatch >= groups)
-      break;
-    load_batch(va, src, g + 2 * kRowBatch, groups);
-    acc = add_batch(acc, vb, 4 * (g + kRowBatch), w);
-  }
-  const int y = strip * kTileH + (seq >> 1);
-  if (live && y < a.h[s])
-    a.rows[s][z * a.rows_stride + 2 * y + (seq & 1)] = acc;
+  // 8. the ordered row sums, continued from the tile on the left: lane q of
+  //    wave 0 owns sequence q (row q / 2, component q % 2); it takes the
+  //    row's fp32 accumulator where the left tile left it (0 at the first
+  //    tile), adds this tile's terms left to right, and hands the
+  //    accumulator on, or stores the row's sum at the last tile.
+  if (tid < kSeq)
+    chain_rows(io, sT + tid * kTermPitch, min(kTileW, w - x0), z, strip, tx,
+               y0 + (tid >> 1), h, tid);
 }
 
 // ------------------------------------------------------------------ launch
@@ -598,22 +478,22 @@ void launch_one(int scale, int bpc, dim3 grid, dim3 block, hipStream_t stream,
   switch (scale) {
   case 0:
     if (bpc == 8)
-      scale_kernel<8, 4, uint8_t, kPow2, true><<<grid, block, 0, stream>>>(
+      scale_kernel<8, 4, uint8_t, kPow2><<<grid, block, 0, stream>>>(
           io, g.w, g.h, sc, taps, next_taps, stat, first);
     else
-      scale_kernel<8, 4, uint16_t, kPow2, true><<<grid, block, 0, stream>>>(
+      scale_kernel<8, 4, uint16_t, kPow2><<<grid, block, 0, stream>>>(
           io, g.w, g.h, sc, taps, next_taps, stat, first);
     break;
   case 1:
-    scale_kernel<4, 2, float, kPow2, false><<<grid, block, 0, stream>>>(
+    scale_kernel<4, 2, float, kPow2><<<grid, block, 0, stream>>>(
         io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   case 2:
-    scale_kernel<2, 1, float, kPow2, false><<<grid, block, 0, stream>>>(
+    scale_kernel<2, 1, float, kPow2><<<grid, block, 0, stream>>>(
         io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   default:
-    scale_kernel<1, 0, float, kPow2, false><<<grid, block, 0, stream>>>(
+    scale_kernel<1, 0, float, kPow2><<<grid, block, 0, stream>>>(
         io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
     break;
   }
@@ -630,25 +510,18 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
                    : bpc == 10 ? 0.25f
                    : bpc == 12 ? 0.0625f
                                : 0.00390625f;
-  // Grid y holds at most kMaxGridY rows of blocks per launch: strips for
-  // the term-buffer form, tile columns for the chained form (scale 0), whose
-  // grid x runs over the strips of every frame.  A later launch on the same
+  // Grid x runs over the strips of every frame, grid y over the tile
+  // columns, at most kMaxGridY per launch.  A later launch on the same
   // stream starts after the earlier ones have finished, so a chain that
   // crosses launches finds its carries written.
-  const bool chain = scale == 0;
-  const int rows = chain ? g.ntx : g.strips;
-  if (chain && (io.carry == nullptr || io.rows == nullptr ||
-                io.err == nullptr || io.strips != g.strips ||
-                io.ntx != g.ntx ||
-                static_cast<long>(n) * g.strips > 0x7fffffffL))
+  if (io.carry == nullptr || io.rows == nullptr || io.err == nullptr ||
+      io.strips != g.strips || io.ntx != g.ntx ||
+      static_cast<long>(n) * g.strips > 0x7fffffffL)
     return hipErrorInvalidValue;
-  for (int first = 0; first < rows; first += kMaxGridY) {
-    const unsigned ny =
-        static_cast<unsigned>(std::min(kMaxGridY, rows - first));
-    const dim3 grid =
-        chain ? dim3(static_cast<unsigned>(n * g.strips), ny, 1)
-              : dim3(static_cast<unsigned>(g.ntx), ny,
-                     static_cast<unsigned>(n));
+  for (int first = 0; first < g.ntx; first += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>(n * g.strips),
+                    static_cast<unsigned>(std::min(kMaxGridY, g.ntx - first)),
+                    1);
     if (stat.inv_nsq != 0.0)
       launch_one<true>(scale, bpc, grid, block, stream, io, g, sc, taps,
                        next_taps, stat, first);
@@ -662,15 +535,31 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
   return hipSuccess;
 }
 
+hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
+                                const TapArgs &taps, const TapArgs &next_taps,
+                                const StatArgs &stat, int col,
+                                hipStream_t stream) {
+  if (col < 0 || col >= g.ntx || io.carry == nullptr || io.rows == nullptr ||
+      io.err == nullptr || io.strips != g.strips || io.ntx != g.ntx)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(g.strips), 1, 1);
+  if (stat.inv_nsq != 0.0)
+    scale_kernel<8, 4, uint8_t, true><<<grid, dim3(kThreads), 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+  else
+    scale_kernel<8, 4, uint8_t, false><<<grid, dim3(kThreads), 0, stream>>>(
+        io, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+  return hipGetLastError();
+}
+
 hipError_t scale0_resident_blocks(int bpc, int *blocks) {
   int per_cu = 0;
   hipError_t e =
       bpc == 8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint8_t, true, true>,
-                     kThreads, 0)
+                     &per_cu, scale_kernel<8, 4, uint8_t, true>, kThreads, 0)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     &per_cu, scale_kernel<8, 4, uint16_t, true, true>,
-                     kThreads, 0);
+                     &per_cu, scale_kernel<8, 4, uint16_t, true>, kThreads,
+                     0);
   int dev = 0, cus = 0;
   if (e == hipSuccess)
     e = hipGetDevice(&dev);
@@ -679,14 +568,6 @@ hipError_t scale0_resident_blocks(int bpc, int *blocks) {
                               dev);
   *blocks = per_cu * cus;
   return e;
-}
-
-hipError_t launch_rowsum(const RowSumArgs &args, int waves, int n,
-                         hipStream_t stream) {
-  if (n < 1 || n > kMaxBatch)
-    return hipErrorInvalidValue;
-  rowsum_kernel<<<dim3(waves, n), dim3(64), 0, stream>>>(args);
-  return hipGetLastError();
 }
 
 } // namespace vifk

@@ -4,14 +4,14 @@
 // nothing (for callers that cannot allocate device or pinned memory).
 //
 // The array `scratch` holds, per call, the pyramid planes of scales 1..3,
-// the term buffers of scales 1..3, scale 0's row-sum carries (cleared at the
-// start of every call), the row sums and the eight per-scale sums.
+// the row-sum hand-over words of the four scales (cleared at the start of
+// every call), the row sums and the eight per-scale sums.
 // Its device address comes from hipGetSymbolAddress, once per device with
 // that device current (the array's name in host code is only a stand-in for
 // the symbol); kernels receive that address.  Every call on a device uses
 // the same array, so calls that overlap on one device race: the caller
 // serialises them (one stream, or one host thread at a time).  The kernels
-// write every word they read before reading it, except scale 0's carries
+// write every word they read before reading it, except the hand-over words
 // (a tile waits until its left neighbour's word carries the call's tag),
 // which a small kernel clears first.
 //
@@ -59,12 +59,11 @@ hipError_t scratch_address(int dev, unsigned char **p) {
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // Offsets (bytes) of one call's buffers in the array: the pyramid planes of
-// scales 1..3, the term buffers of scales 1..3, scale 0's row-sum carries,
-// the row sums, and the eight sums followed by the carry-wait error word.
+// scales 1..3, the four scales' hand-over words (one run), the row sums, and
+// the eight sums followed by the hand-over error word.
 struct Layout {
-  size_t pyr_ref[kScales], pyr_dist[kScales], terms[kScales], carry, rows,
-      sums;
-  size_t carry_words;
+  size_t pyr_ref[kScales], pyr_dist[kScales], carry[kScales], rows, sums;
+  size_t carry_words; // all four scales'
   size_t total;
 };
 
@@ -78,15 +77,14 @@ Layout layout(const ScaleGeom (&g)[kScales], int total_rows) {
     L.pyr_dist[s] = off;
     off += plane;
   }
-  for (int s = 1; s < kScales; ++s) {
-    L.terms[s] = off;
-    off += round256(sizeof(float) * g[s].strips * term_groups(g[s].w) *
-                    kSeq * 4);
+  const size_t carry0 = off;
+  for (int s = 0; s < kScales; ++s) {
+    L.carry[s] = off;
+    off += sizeof(unsigned long long) * g[s].strips *
+           (g[s].ntx > 1 ? g[s].ntx - 1 : 1) * kSeq;
   }
-  L.carry = off;
-  L.carry_words = static_cast<size_t>(g[0].strips) *
-                  (g[0].ntx > 1 ? g[0].ntx - 1 : 1) * kSeq;
-  off += round256(sizeof(unsigned long long) * L.carry_words);
+  L.carry_words = (off - carry0) / sizeof(unsigned long long);
+  off = carry0 + round256(off - carry0);
   L.rows = off;
   off += round256(sizeof(float) * 2 * total_rows);
   L.sums = off;
@@ -100,9 +98,9 @@ struct SumArgs {
   int h[kScales];
 };
 
-// Clears the carries and the error word: the array's earlier contents are
-// another call's (or another geometry's), and every carry of this call
-// must read as not yet written until its tile writes it (tag 1).
+// Clears the hand-over words and the error word: the array's earlier
+// contents are another call's (or another geometry's), and every word of
+// this call must read as not yet written until its tile writes it (tag 1).
 __global__ void clear_kernel(unsigned long long *carry, size_t words,
                              int *err) {
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
@@ -161,7 +159,6 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
     return set_status(VIF_EINVAL);
   ScaleGeom g[kScales];
   TapArgs taps[kScales];
-  RowSumArgs ra{};
   SumArgs sa{};
   int ws = w, hs = h, rows = 0, row_base[kScales];
   for (int s = 0; s < kScales; ++s) {
@@ -179,12 +176,6 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
     for (int k = 0; k < nt; ++k)
       if (taps[s].t[k] != taps[s].t[nt - 1 - k])
         return set_status(VIF_EINVAL);
-    ra.w[s] = ws;
-    ra.h[s] = hs;
-    ra.strips[s] = g[s].strips;
-    // scale 0's rows are summed inside its kernel (chained across tiles)
-    ra.pair_base[s + 1] =
-        ra.pair_base[s] + (s == 0 ? 0 : (g[s].strips + 1) / 2);
     sa.h[s] = hs;
   }
   const Layout L = layout(g, rows);
@@ -203,8 +194,9 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const StatArgs stat = make_stat_args(o.sigma_nsq, o.enhn_gain_limit);
   int *err = reinterpret_cast<int *>(at(L.sums) + 8);
-  auto *carry = reinterpret_cast<unsigned long long *>(base + L.carry);
-  clear_kernel<<<256, 256, 0, st>>>(carry, L.carry_words, err);
+  clear_kernel<<<256, 256, 0, st>>>(
+      reinterpret_cast<unsigned long long *>(base + L.carry[0]),
+      L.carry_words, err);
   e = hipGetLastError();
   for (int s = 0; s < kScales && e == hipSuccess; ++s) {
     ScaleIO io = {};
@@ -214,16 +206,14 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
       io.next_ref = at(L.pyr_ref[s + 1]);
       io.next_dist = at(L.pyr_dist[s + 1]);
     }
-    if (s > 0)
-      io.terms = at(L.terms[s]);
+    io.carry = reinterpret_cast<unsigned long long *>(base + L.carry[s]);
+    io.carry_tag = 1;
+    io.strips = g[s].strips;
+    io.ntx = g[s].ntx;
+    io.rows = at(L.rows) + 2 * row_base[s];
+    io.rows_stride = static_cast<size_t>(2) * rows;
+    io.err = err;
     if (s == 0) {
-      io.carry = carry;
-      io.carry_tag = 1;
-      io.strips = g[0].strips;
-      io.ntx = g[0].ntx;
-      io.rows = at(L.rows);
-      io.rows_stride = static_cast<size_t>(2) * rows;
-      io.err = err;
       const uintptr_t align = bpc == 8 ? 8 : 16;
       io.vec_in = w % 8 == 0 &&
                   reinterpret_cast<uintptr_t>(ref) % align == 0 &&
@@ -232,15 +222,10 @@ vif_score_noalloc(int w, int h, int bpc, const vif_options *opt,
     e = launch_scale(s, bpc, io, 1, g[s], taps[s],
                      taps[s + 1 < kScales ? s + 1 : s], stat, st);
   }
-  for (int s = 0; s < kScales; ++s) {
-    ra.terms[s] = s > 0 ? at(L.terms[s]) : nullptr;
-    ra.rows[s] = at(L.rows) + 2 * row_base[s];
-    sa.rows[s] = ra.rows[s];
-  }
-  if (e == hipSuccess)
-    e = launch_rowsum(ra, ra.pair_base[kScales], 1, st);
-  // (the sums kernel reads the rows the scale-0 kernel and the row-sum
-  // kernel wrote, in stream order)
+  for (int s = 0; s < kScales; ++s)
+    sa.rows[s] = at(L.rows) + 2 * row_base[s];
+  // (the sums kernel reads the rows the scale kernels wrote, in stream
+  // order)
   if (e == hipSuccess) {
     scale_sums_kernel<<<1, 256, 0, st>>>(sa, at(L.sums));
     e = hipGetLastError();

@@ -6,6 +6,7 @@
 
 #include "../../include/vif_selftest.h"
 #include "vif_device_math.h"
+#include "vif_internal.h"
 #include "vif_status.h"
 
 namespace {
@@ -174,6 +175,73 @@ vif_selftest_statistic(const float *mu1, const float *mu2, const float *xx,
     statistic_kernel<false><<<grid_for(n), kBlock, 0, s>>>(
         mu1, mu2, xx, yy, xy, n, sa, num, den);
   return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_carry_wait(int *raised, float *row, void *stream) {
+  if (raised == nullptr || row == nullptr)
+    return vifk::set_status(VIF_EINVAL);
+  // a 224 x 16 frame of zeros: two tile columns, one strip; only column 1
+  // runs, so the words it waits for never carry the launch's tag
+  constexpr int kW = 224, kH = 16;
+  vifk::ScaleGeom g{};
+  g.w = kW;
+  g.h = kH;
+  g.strips = 1;
+  g.ntx = 2;
+  vifk::TapArgs taps[2];
+  vifk::gaussian_taps(0, taps[0].t);
+  vifk::gaussian_taps(1, taps[1].t);
+  const vifk::StatArgs stat = vifk::make_stat_args(2.0, 100.0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *frame = nullptr;
+  float *next = nullptr, *rows = nullptr;
+  unsigned long long *carry = nullptr;
+  int *err = nullptr;
+  hipError_t e = hipMalloc(&frame, kW * kH);
+  if (e == hipSuccess)
+    e = hipMalloc(&next, sizeof(float) * (kW / 2) * (kH / 2) * 2);
+  if (e == hipSuccess)
+    e = hipMalloc(&rows, sizeof(float) * 2 * kH);
+  if (e == hipSuccess)
+    e = hipMalloc(&carry, sizeof(unsigned long long) * vifk::kSeq);
+  if (e == hipSuccess)
+    e = hipMalloc(&err, sizeof(int));
+  if (e == hipSuccess)
+    e = hipMemsetAsync(frame, 0, kW * kH, s);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(carry, 0, sizeof(unsigned long long) * vifk::kSeq, s);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(err, 0, sizeof(int), s);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(rows, 0, sizeof(float) * 2 * kH, s);
+  if (e == hipSuccess) {
+    vifk::ScaleIO io{};
+    io.in_ref[0] = frame;
+    io.in_dist[0] = frame;
+    io.next_ref = next;
+    io.next_dist = next + (kW / 2) * (kH / 2);
+    io.carry = carry;
+    io.carry_tag = 7;
+    io.strips = 1;
+    io.ntx = 2;
+    io.rows = rows;
+    io.rows_stride = 2 * kH;
+    io.err = err;
+    e = vifk::launch_scale0_column(io, g, taps[0], taps[1], stat, 1, s);
+  }
+  if (e == hipSuccess)
+    e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipMemcpy(raised, err, sizeof(int), hipMemcpyDeviceToHost);
+  if (e == hipSuccess)
+    e = hipMemcpy(row, rows, sizeof(float), hipMemcpyDeviceToHost);
+  (void)hipFree(frame);
+  (void)hipFree(next);
+  (void)hipFree(rows);
+  (void)hipFree(carry);
+  (void)hipFree(err);
+  return vifk::status_from_hip(e);
 }
 
 } // extern "C"
