@@ -95,11 +95,14 @@ def _noisy8(seed, w, h, spread=20):
     return ref, dist
 
 
-@pytest.mark.parametrize("wh", [(16, 1048704), (1048704, 16)])
+@pytest.mark.parametrize("wh", [(16, 1048704), (1048704, 16), (7400000, 16)])
 def test_extreme_aspect_frames(V, orc, wh):
-    """A frame 16 pixels wide has 65 544 tile rows at scale 0, more than a
-    grid's y dimension allows (65 536 blocks): the tiles are laid out in one
-    grid dimension.  Its transpose has 9364 tiles in a row."""
+    """A frame 16 pixels wide has 65 544 strips of 16 rows at scale 0, all in
+    grid x (strips of every frame).  Its transpose has 9364 tiles in a row.
+    7 400 000 x 16 has 66 072 tiles in a row at scale 0, more than a grid's
+    y dimension allows (65 535): scale 0 takes two launches, and each row's
+    sum is handed from the first launch's last tile to the second launch's
+    first."""
     w, h = wh
     ref, dist = _noisy8(w + 3 * h, w, h)
     ctx = V.Vif(w, h, 8)
