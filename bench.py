@@ -92,6 +92,11 @@ HBM_PEAK_GBS = 8000.0
 # (ADR-1422 and ADR-1444, Context).  Bit identity is reported beside it.
 PARITY_GATE = 5e-5
 
+# The other workloads of frames mode: generator in synth, w, h, bpc.
+SMALL_WORKLOADS = {"1080p10": ("checker_1080p_10bit", 1920, 1080, 10),
+                   "1080p16": ("bright_1080p_16bit", 1920, 1080, 16),
+                   "576x324": ("netflix_576x324_8bit", 576, 324, 8)}
+
 # One device's share when 3840x2160 frames are split in eight row strips on
 # 272-row boundaries (strip boundaries fall on multiples of 8 rows): rows
 # 272..543, read with their halo as input rows 248..556.
@@ -532,9 +537,11 @@ def main():
     ap.add_argument("--batch", type=int, default=4,
                     help="frames per step (one submission, each kernel "
                     "launched once for them); the fssim mode defaults to 1")
-    ap.add_argument("--workload", choices=["4k", "1080p10"], default="4k",
+    ap.add_argument("--workload", choices=list(SMALL_WORKLOADS) + ["4k"],
+                    default="4k",
                     help="frames mode only: the 3840x2160 8-bit frames, or "
-                    "the 1920x1080 10-bit checkerboard pairs")
+                    "the 1920x1080 10-bit checkerboard pairs, the 1920x1080 "
+                    "16-bit bright pairs, the 576x324 8-bit pairs")
     ap.add_argument("--mode", choices=["full", "frames", "strip", "copy",
                                        "fssim"],
                     default="full",
@@ -579,14 +586,15 @@ def main():
         print("--batch must be 1..%d" % V.MAX_BATCH, file=sys.stderr)
         sys.exit(2)
     reps = args.reps
-    if args.mode == "frames" and args.workload == "1080p10":
-        frames = synth.checker_1080p_10bit()
-        res = steady_state(V, frames, 1920, 1080, 10, args.steps, args.warmup,
+    if args.mode == "frames" and args.workload in SMALL_WORKLOADS:
+        gen, w, h, bpc = SMALL_WORKLOADS[args.workload]
+        frames = getattr(synth, gen)()
+        res = steady_state(V, frames, w, h, bpc, args.steps, args.warmup,
                            batch=batch, reps=reps, prof_kinds=["scale0"])
         s0_ms, s0_n = res["kernel"]["scale0"]
-        print("1080p 10-bit: %.1f frames/s, %.3f ms/step of %d frames; "
+        print("%s: %.1f frames/s, %.3f ms/step of %d frames; "
               "scale-0 kernel %.1f us per launch"
-              % (rate(res, args.steps, batch),
+              % (gen, rate(res, args.steps, batch),
                  1000.0 * median(res["seconds"]) / args.steps, batch,
                  1000.0 * s0_ms / max(s0_n, 1)), file=sys.stderr, flush=True)
         return
@@ -691,7 +699,7 @@ def main():
     peak = VALU_PEAK_OPS / 1e12
     traffic, frame_bytes = load_traffic(batch)
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
-                "peak": round(peak, 2), "unit": "Top/s",
+                "peak": round(peak, 2), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
     pops = path_ops(w, h)
@@ -704,9 +712,13 @@ def main():
                            "0.25 s; queue full at t0; each repetition counts "
                            "exactly `steps` submission completions in "
                            "steady state; value = median repetition"},
-             "roofline_unit_note": "plain IEEE operations per second "
-                                   "(multiplies, adds, compares, selects, "
-                                   "conversions), not fused flops",
+             "roofline_unit_note": "roofline.achieved and peak count plain "
+                                   "IEEE operations per second, 1e12 per "
+                                   "unit: fp32/fp64 multiplies and adds and "
+                                   "the statistic's compares, selects and "
+                                   "conversions, one each (no fused "
+                                   "multiply-add); the unit keeps the name "
+                                   "TFLOP/s",
              "scale0_ops_per_pixel": {
                  "filter_and_decimation": FILTER_OPS_PER_PIXEL_SCALE0,
                  "statistic": STAT_OPS_PER_PIXEL},
