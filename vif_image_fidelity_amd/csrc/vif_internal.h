@@ -50,9 +50,11 @@ bool options_valid(const OptionValues &o);
 StatArgs make_stat_args(double nsq, double gain_limit);
 
 // Terms of a 16-row strip: 32 sequences (16 rows x {num, den}).  In LDS a
-// tile keeps them as [seq][x] with pitch kTermPitch.
+// tile keeps them as [seq][x] with pitch kTermPitch; an odd pitch puts the
+// 32 sequences' same column in 32 different banks, so the lanes that read
+// one sequence each (the row sums) never share a bank.
 constexpr int kSeq = 32;
-constexpr int kTermPitch = kTileW + 4;
+constexpr int kTermPitch = kTileW + 1;
 
 // Frames one launch may carry (grid x of the scale kernels runs over the
 // strips of every frame).

@@ -85,14 +85,39 @@ __device__ __forceinline__ void settle(float (&v)[A][B]) {
       asm volatile("" : "+v"(v[a][b]));
 }
 
-// Horizontal pass of NQ quantities stored in LDS as [q][kTileH][pitch]:
+// LDS layout of the vertical results (bank = dword address mod 64 for a
+// whole wave, or mod 32 for each half of it; the layouts below avoid
+// conflicts in both readings).
+//
+// Rows of the five quantities: pitch vpitch(R), the smallest pitch >= the
+// vertical pass's CW = kTileW + 2R columns that is 8 mod 16.  The horizontal
+// pass reads with lane l of a wave at row (l >> 3) + 8a and column
+// 7 * ((l & 7) + 8b) + j: the 8 lanes of a row read 8 columns 7 apart, and
+// rows 8 (mod 16) dwords apart move those 8 banks to 8 disjoint sets, so
+// the 64 lanes (and each half's 32) hit distinct banks.
+template <int R>
+__host__ __device__ constexpr int vpitch() {
+  return kTileW + 2 * R + ((8 - (kTileW + 2 * R)) % 16 + 16) % 16;
+}
+
+// Rows of the next scale's vertical low-pass (8 rows per plane): row yd
+// starts at dec_row(yd), which is (yd & 3) + 32 * (yd >> 2) mod 64, and a
+// plane takes kDecPlane floats.  The decimation reads with lane l at row
+// (l >> 3) & 7 and columns 4 * (l & 7) + c apart: the 8 columns of a row lie
+// 4 apart, and the rows' start residues (0..3 and 32..35) interleave them.
+__device__ __forceinline__ int dec_row(int yd) {
+  return 128 * yd + (yd & 3) + 32 * (yd >> 2);
+}
+constexpr int kDecPlane = 1088; // >= dec_row(7) + 128, 0 mod 64
+
+// Horizontal pass of NQ quantities stored in LDS as [q][kTileH][vpitch]:
 // thread (ty, seg) computes tile row ty, columns seg*HB .. seg*HB+HB-1.
 template <int R, int NQ, int HB>
 __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
                                       int seg, const TapArgs &taps,
                                       float (&f)[NQ][HB]) {
   constexpr int N = 2 * R + 1;
-  constexpr int CWP = kTileW + 2 * R + 1;
+  constexpr int CWP = vpitch<R>();
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const float *row = sV + (q * kTileH + ty) * CWP + seg * HB;
@@ -188,11 +213,12 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
 //
-// LDS is reused phase by phase so that a block needs about 24 KiB:
+// LDS is reused phase by phase so that a block needs at most 25.5 KiB (six
+// blocks per CU):
 //   phases 1-2  input tile, native samples       [2][IR][CW] InT
-//   phases 3-4  vertical results of x, y         [2][kTileH][CWP]
-//               + the low-pass at even rows      [2][kTileH/2][CWP]
-//   phases 5-6  vertical results of x*x, y*y, x*y [3][kTileH][CWP]
+//   phases 3-4  vertical results of x, y         [2][kTileH][vpitch]
+//               + the low-pass at even rows      [2][kDecPlane] (dec_row)
+//   phases 5-6  vertical results of x*x, y*y, x*y [3][kTileH][vpitch]
 //   phases 7-8  terms                            [kSeq][kTermPitch]
 // The horizontal pass therefore runs in two rounds (x, y and the next
 // scale's planes, then the three second moments); the second round's
@@ -219,13 +245,13 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   constexpr int ND = 2 * RD + 1;
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
   constexpr int IR = kTileH + 2 * R; // input rows
-  constexpr int CWP = CW + 1;        // odd pitch: conflict-free row reads
+  constexpr int CWP = vpitch<R>();   // conflict-free horizontal reads
   constexpr int VB = 8;              // rows per thread in the vertical pass
   constexpr int HB = 7;              // outputs per thread, horizontal pass
   constexpr int kQA = 2;             // quantities of the first round
   constexpr int kInFloats =
       (2 * IR * CW * static_cast<int>(sizeof(InT)) + 3) / 4;
-  constexpr int kVd = RD > 0 ? 2 * (kTileH / 2) * CWP : 0;
+  constexpr int kVd = RD > 0 ? 2 * kDecPlane : 0;
   constexpr int kVA = kQA * kTileH * CWP + kVd;
   constexpr int kVB = (5 - kQA) * kTileH * CWP;
   constexpr int kT = kSeq * kTermPitch;
@@ -233,6 +259,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   constexpr int kL1 = kL0 > kT ? kL0 : kT;
   constexpr int kLds = kL1 > kInFloats ? kL1 : kInFloats;
   static_assert(CW <= 128, "one thread per vertical column in two halves");
+  static_assert(CWP >= CW && CWP % 16 == 8, "vertical-result pitch");
+  static_assert(kTileH / 2 == 8 && kTileW / 4 <= 32, "decimation rows");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
   static_assert(kTileH == 2 * VB, "two row blocks");
   __shared__ __attribute__((aligned(16))) float lds[kLds];
@@ -364,8 +392,10 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
 
   float *sV = lds;
   float *sVd = lds + kQA * kTileH * CWP;
-  const int ty = tid & 15;
-  const int seg = tid >> 4;
+  // horizontal pass: wave w takes tile rows 8 * (w & 1) .. + 7 and segments
+  // 8 * (w >> 1) .. + 7; lane l row l >> 3, segment l & 7 (see vpitch)
+  const int seg = (tid & 7) + 8 * (tid >> 7);
+  const int ty = ((tid >> 3) & 7) + 8 * ((tid >> 6) & 1);
 
   // 3. round A: vertical results of x, y and the next scale's vertical
   //    low-pass to LDS
@@ -380,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int m = 0; m < VB / 2; ++m)
-          sVd[(p * (kTileH / 2) + vb * (VB / 2) + m) * CWP + vc] = dacc[p][m];
+          sVd[p * kDecPlane + dec_row(vb * (VB / 2) + m) + vc] = dacc[p][m];
     }
   }
   __syncthreads();
@@ -392,10 +422,12 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   settle(fa);
 
   //    next scale's planes: horizontal low-pass at even columns of the even
-  //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1.
+  //    rows.  Thread (yd, sd) owns decimated row yd and columns 2sd, 2sd+1;
+  //    wave w takes sd = 8w .. 8w + 7, lane l row (l >> 3) & 7 and
+  //    sd = 8w + (l & 7) (see dec_row).
   if constexpr (RD > 0) {
-    const int yd = tid & 7;
-    const int sd = tid >> 3;
+    const int sd = (tid & 7) + 8 * (tid >> 6);
+    const int yd = (tid >> 3) & 7;
     const int wd = w >> 1;
     const int hd = h >> 1;
     const int ydg = (y0 >> 1) + yd;
@@ -408,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const float *row =
-                sVd + (p * (kTileH / 2) + yd) * CWP + 2 * xl + R - RD;
+                sVd + p * kDecPlane + dec_row(yd) + 2 * xl + R - RD;
             float a = tap(dtaps, 0, ND) * row[0];
 #pragma unroll
             for (int k = 1; k < ND; ++k)
