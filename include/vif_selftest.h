@@ -47,7 +47,11 @@ int vif_selftest_log2(const float *x, long n, float *y, void *stream);
  * >= 0, as vif_options.sigma_nsq; else VIF_EINVAL), each through fp64 and
  * one rounding to fp32:
  *   num[i] = fl32(1 + a[i] / (sv[i] + nsq)),  den[i] = fl32(1 + a[i] / nsq).
- * A power-of-two nsq takes the kernels' exact-reciprocal path. */
+ * A power-of-two nsq in [2^-20, 2^20] takes the kernels' power-of-two form:
+ * the exact reciprocal for den, and for num the fp64 division without its
+ * scaling steps, whose domain needs finite a[i] and sv[i] >= 0 (the
+ * kernels' values always are); an infinite or NaN a[i] or sv[i] may then
+ * give a different NaN or infinity than the general form. */
 int vif_selftest_ratios(const float *a, const float *sv, double nsq, long n,
                         float *num, float *den, void *stream);
 

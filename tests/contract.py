@@ -10,14 +10,18 @@ Context and Consequences).  This module checks three layers:
 
   flags    the library's compiler flags fix contraction off, IEEE division,
            denormals and no fast-math, with packed fp32 disabled;
-  sources  the kernel sources call no fused multiply-add, no library or
-           hardware log/exp, no atomic read-modify-write (an atomic add
-           would merge sums in arrival order; atomic loads and stores that
-           only hand a value from one block to the next are allowed), and
-           include no CUDA or Triton;
-  ISA      the compiled gfx950 code of every kernel: each fp32 / fp64 fused
+  sources  the kernel sources call no fused multiply-add (except the five
+           of the fp64 division written out in div_in_range, checked to be
+           exactly that sequence), no library or hardware log/exp, no atomic
+           read-modify-write (an atomic add would merge sums in arrival
+           order; atomic loads and stores that only hand a value from one
+           block to the next are allowed), and include no CUDA or Triton;
+  ISA      the compiled gfx950 code of every kernel: each fp32 fused
            multiply-add belongs to a correctly rounded division expansion
-           (five per v_div_fixup), and there are no packed-fp32, float mad,
+           (five per v_div_fixup_f32), each fp64 one to an fp64 division
+           (one v_rcp_f64 each: five fused multiply-adds and a v_div_fmas in
+           the compiler's expansion, which ends in v_div_fixup_f64, six in
+           the written-out one), and there are no packed-fp32, float mad,
            hardware log/exp, atomic, scalar-memory-store or scratch
            instructions.
 
@@ -80,11 +84,41 @@ def _strip_comments(text):
     return re.sub(r"//[^\n]*", "", text)
 
 
+# The one place the sources may fuse: the fp64 division written out step by
+# step (a reciprocal, two Newton-Raphson refinements of two fused
+# multiply-adds each, the product, the remainder and the corrected quotient),
+# the same steps as the compiler's expansion.
+_DIV_HELPER = re.compile(
+    r"double div_in_range\(double a, double d\) \{(?P<body>.*?)\n\}", re.S)
+_DIV_BODY = [
+    "double r = __builtin_amdgcn_rcp(d);",
+    "double e = __builtin_fma(-d, r, 1.0);",
+    "r = __builtin_fma(r, e, r);",
+    "e = __builtin_fma(-d, r, 1.0);",
+    "r = __builtin_fma(r, e, r);",
+    "const double q = a * r;",
+    "const double rem = __builtin_fma(-d, q, a);",
+    "return __builtin_fma(rem, r, q);",
+]
+
+
+def _take_div_helper(name, code, v):
+    """Checks the written-out division, then removes its body from the
+    code the other rules scan."""
+    m = _DIV_HELPER.search(code)
+    if m is None:
+        return code
+    body = [ln.strip() for ln in m.group("body").splitlines() if ln.strip()]
+    if body != _DIV_BODY:
+        v.append("%s: div_in_range is not the fp64 division's steps" % name)
+    return code[:m.start("body")] + code[m.end("body"):]
+
+
 def source_violations(sources):
     """sources: {file name: text} of device code."""
     v = []
     for name, text in sources.items():
-        code = _strip_comments(text)
+        code = _take_div_helper(name, _strip_comments(text), v)
         for pat, what in _SOURCE_RULES:
             for m in re.finditer(pat, code):
                 v.append("%s: %s (%s)" % (name, what, m.group(0).strip()))
@@ -162,12 +196,13 @@ def isa_violations(asm):
         fix32 = count(r"v_div_fixup_f32(?:_e64)?")
         fma64 = count(r"v_fmac?_f64(?:_e32|_e64)?")
         fix64 = count(r"v_div_fixup_f64(?:_e64)?")
+        rcp64 = count(r"v_rcp_f64(?:_e32|_e64)?")
         if fma32 != 5 * fix32:
             v.append("%s: %d fp32 fused multiply-adds for %d divisions"
                      % (name, fma32, fix32))
-        if fma64 != 5 * fix64:
+        if fix64 > rcp64 or fma64 != 5 * fix64 + 6 * (rcp64 - fix64):
             v.append("%s: %d fp64 fused multiply-adds for %d divisions"
-                     % (name, fma64, fix64))
+                     % (name, fma64, rcp64))
         for pat, what in _ISA_FORBIDDEN:
             n = count(pat)
             if n:

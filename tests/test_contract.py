@@ -86,6 +86,14 @@ SOURCE_MUTANTS = [
     ("vif_device_math.h", "__device__ __forceinline__ float log2_poly",
      "#ifdef __HIP_PLATFORM_AMD__\n#endif\n"
      "__device__ __forceinline__ float log2_poly"),
+    # the written-out fp64 division loses its remainder correction, or
+    # gains a fused step, or a fused step moves outside it
+    ("vif_device_math.h", "  return __builtin_fma(rem, r, q);",
+     "  return q;"),
+    ("vif_device_math.h", "  const double q = a * r;",
+     "  const double q = __builtin_fma(a, r, 0.0);"),
+    ("vif_device_math.h", "  const float q = p * t;",
+     "  const float q = __builtin_fmaf(p, t, 0.0f);"),
 ]
 
 

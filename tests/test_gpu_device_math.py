@@ -162,6 +162,35 @@ def test_ratios_bitwise(dev, orc, nsq):
         assert np.isnan(rd[a == 0]).all() and np.isinf(rd[a > 0]).all()
 
 
+@pytest.mark.parametrize("nsq", [2.0 ** -20, 2.0 ** 20, 2.0 ** -21, 2.0 ** 21])
+def test_ratios_bitwise_whole_range(dev, orc, nsq):
+    """The numerator ratio over every finite fp32 a >= 0 the kernels can
+    form (0 and 2^-149 .. 2^127, log-uniform) and sv from the floor 1e-10 to
+    2^127, at the ends of the power-of-two form's nsq range (2^-20, 2^20:
+    the fp64 division without scaling steps) and just outside it (2^-21,
+    2^21: the general form), against the oracle's fp64 ratios."""
+    import torch
+    from vif_image_fidelity_amd import _lib
+    g = np.random.Generator(np.random.PCG64(34))
+    n = 1 << 20
+    a = np.exp2(g.uniform(-149, 127.9, n)).astype(np.float32)
+    sv = np.exp(g.uniform(np.log(1e-10), np.log(2.0 ** 127), n)).astype(
+        np.float32)
+    a[:64] = 0.0
+    a[64:128] = np.float32(2.0 ** -149)
+    a[128:192] = np.nextafter(np.float32(np.inf), np.float32(0))
+    sv[192:256] = np.float32(1e-10)
+    num = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    den = torch.empty_like(num)
+    da, dsv = _d(a), _d(sv)   # held until the call has finished
+    _check(_lib.load().vif_selftest_ratios(da.data_ptr(), dsv.data_ptr(),
+                                           nsq, n, num.data_ptr(),
+                                           den.data_ptr(), None))
+    rn, rd = orc.ratios(a, sv, nsq=nsq)
+    assert np.array_equal(_h(num).view(np.uint32), rn.view(np.uint32))
+    assert np.array_equal(_h(den).view(np.uint32), rd.view(np.uint32))
+
+
 def _statistic_inputs(g, n):
     """Five filtered values shaped like real data: means in [0, 256),
     variances from 0 to ~2e4 (many near the noise variance 2), covariance

@@ -62,22 +62,57 @@ __device__ __forceinline__ float log2_poly(float x) {
   return static_cast<float>(e) + q;
 }
 
+// The correctly rounded fp64 quotient a / d for operands whose quotient needs
+// no scaling: a == +0 or 2^-700 <= a <= 2^600, and 2^-100 <= d <= 2^200 (so
+// the quotient lies in [2^-900, 2^700] and the exponents of a and d differ
+// by at most 700).  These are the steps of the compiler's IEEE fp64
+// division on gfx950 -- a hardware reciprocal, two Newton-Raphson
+// refinements, the product with a, the remainder and the corrected quotient
+// (six fused multiply-adds, the last of which the expansion issues as
+// v_div_fmas with its scale flag clear) -- without the
+// two operand-scaling steps and the special-case fix-up around them.  In this
+// domain those are identities (the scaling acts only on zero, denormal or
+// extreme-exponent operands and quotients, and the fix-up only on zero,
+// infinite or NaN operands and on overflowing or underflowing quotients; for
+// a == +0 every step gives +0, as the fix-up does), so the result has the
+// same bits.  The fused multiply-adds below are the division's own, exactly
+// as the expansion has them; nowhere else does the library fuse.
+__device__ __forceinline__ double div_in_range(double a, double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  double e = __builtin_fma(-d, r, 1.0);
+  r = __builtin_fma(r, e, r);
+  e = __builtin_fma(-d, r, 1.0);
+  r = __builtin_fma(r, e, r);
+  const double q = a * r;
+  const double rem = __builtin_fma(-d, q, a);
+  return __builtin_fma(rem, r, q);
+}
+
 // fl32(1 + a / (sv + nsq)) with the sum, quotient and sum with one in fp64
 // and a single conversion to fp32 at the end; nsq is the noise variance,
 // kept in binary64 (ADR-1422 "float_vif_sycl computes the CPU's arithmetic
-// ...", Context and Decision).
+// ...", Context and Decision).  kPow2 marks the kernels for a power-of-two
+// nsq in [2^-20, 2^20] (see den_ratio): there a is a finite fp32 value
+// (0 or at least 2^-149, below 2^128) and d = sv + nsq lies in
+// [2^-20, 2^129], inside div_in_range's domain, so the quotient takes the
+// shorter sequence; any other nsq divides with the compiler's expansion.
+template <bool kPow2>
 __device__ __forceinline__ float num_ratio(float a, float sv, double nsq) {
   const double d = static_cast<double>(sv) + nsq;
-  const double q = static_cast<double>(a) / d;
+  double q;
+  if constexpr (kPow2)
+    q = div_in_range(static_cast<double>(a), d);
+  else
+    q = static_cast<double>(a) / d;
   return static_cast<float>(1.0 + q);
 }
 
 // fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.  For a
-// power-of-two nsq (kPow2, sa.inv_nsq = 1 / nsq, not 0) the quotient is the
-// exact product with 1 / nsq.  kPow2 is a compile-time choice: the kernels
-// come in both forms and the host launches the one that matches nsq, so
-// neither carries the other's arithmetic (a run-time branch on it was
-// turned into both computations and a select).
+// power-of-two nsq in [2^-20, 2^20] (kPow2, sa.inv_nsq = 1 / nsq, not 0) the
+// quotient is the exact product with 1 / nsq.  kPow2 is a compile-time
+// choice: the kernels come in both forms and the host launches the one that
+// matches nsq, so neither carries the other's arithmetic (a run-time branch
+// on it was turned into both computations and a select).
 template <bool kPow2>
 __device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
   const double s = static_cast<double>(s1);
@@ -132,7 +167,7 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
   g = g < sa.gain ? g : sa.gain;
   const float gg = g * g;
   const float a = gg * s1;
-  num = log2_poly(num_ratio(a, sv, sa.nsq));
+  num = log2_poly(num_ratio<kPow2>(a, sv, sa.nsq));
   den = log2_poly(den_ratio<kPow2>(s1, sa));
 }
 

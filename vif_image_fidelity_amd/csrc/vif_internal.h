@@ -27,8 +27,9 @@ struct TapArgs {
 // and passed to every scale kernel by value.
 //   nsq      the noise variance (a double, as the branch and both ratios
 //            use it)
-//   inv_nsq  1 / nsq when that is a power of two, so that s * inv_nsq is
-//            the quotient s / nsq exactly; 0 otherwise (divide)
+//   inv_nsq  1 / nsq when that is a power of two in [2^-20, 2^20], so that
+//            s * inv_nsq is the quotient s / nsq exactly; 0 otherwise
+//            (divide).  Non-zero selects the kernels' kPow2 form.
 //   gain     the enhancement gain limit rounded to fp32.  C's MIN(g, limit)
 //            with a double limit selects the same value as the fp32
 //            comparison g < gain: no fp32 value lies strictly between a

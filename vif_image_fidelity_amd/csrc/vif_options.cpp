@@ -43,9 +43,11 @@ StatArgs make_stat_args(double nsq, double gain_limit) {
   a.inv_nsq = 0.0;
   int e = 0;
   // nsq = 2^(e-1) exactly when its frexp fraction is 1/2; the reciprocal
-  // is then exact, and so is the product with any fp32 value for these
-  // exponents (no overflow or underflow in fp64)
-  if (nsq > 0.0 && std::frexp(nsq, &e) == 0.5 && e > -256 && e < 256)
+  // is then exact, and so is the product with any fp32 value (no overflow or
+  // underflow in fp64).  The range 2^-20 .. 2^20 also keeps the numerator
+  // ratio's quotient inside the domain of its shorter division (the kernels
+  // for a power-of-two nsq use it; other values take the general kernels).
+  if (nsq > 0.0 && std::frexp(nsq, &e) == 0.5 && e >= -19 && e <= 21)
     a.inv_nsq = std::ldexp(1.0, 1 - e);
   a.gain = static_cast<float>(gain_limit);
   return a;

@@ -52,7 +52,7 @@ __global__ void ratios_kernel(const float *__restrict__ a,
                               float *__restrict__ den) {
   const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
   if (i < n) {
-    num[i] = vifk::num_ratio(a[i], sv[i], sa.nsq);
+    num[i] = vifk::num_ratio<kPow2>(a[i], sv[i], sa.nsq);
     den[i] = vifk::den_ratio<kPow2>(a[i], sa);
   }
 }
