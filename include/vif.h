@@ -95,11 +95,11 @@ void vif_default_options(vif_options *opt);
  *   bpc    8, 10, 12 or 16 (Research-2130, Sources: 8-bit samples used as
  *          they are, wider samples divided by 4, 16 or 256).
  * Allocates every device buffer the context needs (pyramid planes, the
- * row sums' hand-over words) and pinned host buffers (row sums), on the device current at the
- * call, and computes the taps on the host.  Work goes to the default stream
- * unless vif_set_stream() is called.  Returns NULL on failure; vif_errno()
- * then gives VIF_EINVAL, VIF_ENOMEM or VIF_EHIP.  Geometry is refused here,
- * never in the middle of a frame.
+ * row sums' hand-over words) and pinned host buffers (row sums), on the
+ * device current at the call, and computes the taps on the host.  Work goes
+ * to the default stream unless vif_set_stream() is called.  Returns NULL on
+ * failure; vif_errno() then gives VIF_EINVAL, VIF_ENOMEM or VIF_EHIP.
+ * Geometry is refused here, never in the middle of a frame.
  */
 vif_ctx *vif_create(int w, int h, int bpc);
 
@@ -257,8 +257,8 @@ int vif_scores_from_rows(int w, int h, const vif_options *opt,
  * out).
  * The buffers the kernels need beyond the frames and out (pyramid planes,
  * the row sums' hand-over words, row sums, the eight sums) live in one
- * array of
- * VIF_NOALLOC_SCRATCH bytes of device memory that the library defines: each
+ * array of VIF_NOALLOC_SCRATCH bytes of device memory that the library
+ * defines: each
  * device the call runs on holds it from the call's first use there until
  * the process ends.  A frame whose buffers do not fit is refused with
  * VIF_ETOOBIG before any work is queued (3840x2160 needs about 22 MiB).
@@ -351,8 +351,8 @@ int vif_set_profiling(vif_ctx *ctx, int kinds);
  *         and the ordered row sums: each row's fp32 sum is carried from tile
  *         to tile inside the kernel)
  * A launch here is one kind's work for one submission (all its frames): one
- * kernel launch, or several in a row for a scale with more than 65535 strips
- * of 16 rows, timed as one.
+ * kernel launch, or several in a row for a plane more than 65535 tiles of
+ * 112 columns wide, timed as one.
  * ms and launches hold at least `capacity` entries (either may be NULL).
  * Returns the number of kinds (4) or VIF_EINVAL.
  */

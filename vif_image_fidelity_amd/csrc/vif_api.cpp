@@ -2,27 +2,28 @@
 // read-back per frame and the host sums.
 //
 // Every submission (one frame, or a batch of up to max_batch frames that
-// each kernel processes in one launch, blockIdx.z being the frame) has a slot
-// of a three-slot ring, and every slot its own stream and buffers (pyramid
-// planes, term buffers, and its row sums in pinned host memory, each sized
-// for max_batch frames).  The slot's stream runs the four per-scale kernels
-// (filter, statistic, next scale's planes, and the ordered row sums, each
-// row's fp32 sum carried from tile to tile inside the kernel); the row sums
-// go straight into the host buffer, two floats per row per scale: one
-// read-back per frame with no copy call (ADR-1422 "float_vif_sycl computes
-// the CPU's arithmetic ...", Decision: the row sums come back in one
-// transfer and the host adds them).
+// each kernel processes in one launch, its grid running over the strips of
+// every frame) has a slot of a three-slot ring, and every slot its own
+// stream and buffers (pyramid planes, the row sums' tile-to-tile hand-over
+// words, and its row sums in pinned host memory, each sized for max_batch
+// frames).  The slot's stream runs one kernel per scale; each does the
+// filter, the statistic, the next scale's planes and the ordered row sums,
+// carrying each row's fp32 sum from tile to tile.  The row sums go straight
+// into the host buffer, two floats per row per scale: one read-back per
+// frame with no copy call (ADR-1422 "float_vif_sycl computes the CPU's
+// arithmetic ...", Decision: the row sums come back in one transfer and the
+// host adds them).
 // Frames in host memory are first copied into the slot's own frame buffers
 // on the slot's stream (vif_submit_host).
-// Consecutive frames rotate over the slots, so one frame's small
-// scales and row sums overlap the next frame's scale 0, which fills the
-// GPU.  When one scale-0 kernel covers the GPU twice over, consecutive
-// frames' scale-0 kernels run one after the other (a stream wait on the
-// previous frame's scale-0 event): two of them side by side gain nothing,
-// and each launch's duration then is its own.  A submission is five runtime
-// calls (four launches, one event), plus an event and that stream wait when
-// the scale-0 kernels are ordered (and a launch more per scale for every
-// 65535 tile columns beyond the first: see launch_scale).
+// Consecutive frames rotate over the slots, so one frame's small scales
+// overlap the next frame's scale 0, which fills the GPU.  When one scale-0
+// kernel covers the GPU twice over, consecutive frames' scale-0 kernels run
+// one after the other (a stream wait on the previous frame's scale-0
+// event): two of them side by side gain nothing, and each launch's duration
+// then is its own.  A submission is five runtime calls (four launches, one
+// event), plus an event and that stream wait when the scale-0 kernels are
+// ordered (and a launch more per scale for every 65535 tile columns beyond
+// the first: see launch_scale).
 //
 // The slot streams are blocking streams, so they are ordered after work on
 // the default stream (where a caller typically fills the frames); a caller
@@ -315,7 +316,8 @@ int collect_frame(vif_ctx *ctx, double out[8]) {
     }
   }
   // the own rows of each scale, in scale order
-  const float *rows = sl.rows_host + static_cast<size_t>(z) * 2 * ctx->total_rows;
+  const float *rows =
+      sl.rows_host + static_cast<size_t>(z) * 2 * ctx->total_rows;
   for (int s = 0; s < kScales; ++s)
     std::memcpy(ctx->last_rows + 2 * ctx->own_base[s],
                 rows + 2 * (ctx->row_base[s] + ctx->own0[s]),
@@ -450,7 +452,8 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
     int resident = 0;
     e = vifk::scale0_resident_blocks(bpc, &resident);
     c->order_scale0 =
-        e == hipSuccess && c->geom[0].tiles() >= 2 * static_cast<size_t>(resident);
+        e == hipSuccess &&
+        c->geom[0].tiles() >= 2 * static_cast<size_t>(resident);
   }
   c->total_rows = rows;
   c->own_rows = own;
@@ -485,7 +488,7 @@ vif_create_strip(int w, int h, int bpc, const vif_options *opt,
                         hipHostMallocCoherent);
     if (e == hipSuccess)
       *sl.err_host = 0;
-    // coherent pinned memory: the row-sum kernel's stores reach the host
+    // coherent pinned memory: the scale kernels' row-sum stores reach the host
     // without a copy, visible once the slot's event has completed
     if (e == hipSuccess)
       e = hipHostMalloc(reinterpret_cast<void **>(&sl.rows_host),
