@@ -13,9 +13,10 @@ the next batch's kernels.  `value` is frames/s.  Prints one JSON line.
 
 The line carries, besides the contract fields:
   roofline      the dominant kernel (the scale-0 filter/statistic kernel, one
-                launch per batch): algorithmic fp32 operations per launch /
-                its average duration, timed with HIP events on the slot's
-                stream during the timed region, against the VALU peak;
+                launch per batch): algorithmic operations per launch (fp32
+                and fp64, each IEEE operation once) / its average duration,
+                timed with HIP events on the slot's stream during the timed
+                region, against the VALU peak for plain operations;
                 `traffic` is the kernel's HBM bytes per launch from committed
                 rocprofv3 counters taken at the same batch size, when the
                 kernel source and flags have not changed since, else null.
