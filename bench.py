@@ -85,7 +85,8 @@ OPS_PER_PIXEL_SCALE0 = FILTER_OPS_PER_PIXEL_SCALE0 + STAT_OPS_PER_PIXEL
 # retires more wave instructions than one per quad-cycle per SIMD allows).
 # A plain add or multiply is one operation, so the ceiling is
 # 256 x 4 x 32 x 2.4e9 = 78.6e12 operations/s.
-VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
+VALU_CLOCK_HZ = 2.4e9
+VALU_PEAK_OPS = 256 * 4 * 32 * VALU_CLOCK_HZ
 
 HBM_PEAK_GBS = 8000.0
 
@@ -480,6 +481,39 @@ def copy_calibration(launches):
           file=sys.stderr, flush=True)
 
 
+VALU_WAVES = (4, 5, 6, 7, 8)
+
+
+def valu_rate(iters):
+    """The issue rate of the filter's multiply-and-add pair (a multiply by a
+    uniform tap, a VGPR add) at 4..8 waves per SIMD, from the library's
+    microbenchmark (vif_selftest_valu_rate): 16 rounds of full occupancy,
+    `iters` rounds of 32 VALU instructions per thread.  Prints wave
+    instructions per SIMD per quad-cycle at the nominal 2.4 GHz (the counters
+    SQ_INSTS_VALU and GRBM_GUI_ACTIVE give the rate at the clock the chip
+    actually ran)."""
+    import ctypes
+    import torch
+    from vif_image_fidelity_amd import _lib
+    lib = _lib.load()
+    for w in VALU_WAVES:
+        blocks = 256 * w * 16
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+        ms = ctypes.c_double(0.0)
+        best = None
+        for _ in range(3):
+            rc = lib.vif_selftest_valu_rate(w, iters, blocks, out.data_ptr(),
+                                            ctypes.byref(ms), None)
+            if rc != 0:
+                raise RuntimeError("vif_selftest_valu_rate: %d" % rc)
+            best = ms.value if best is None else min(best, ms.value)
+        insts = blocks * 4.0 * iters * 32
+        quads = best * 1e-3 * VALU_CLOCK_HZ / 4.0
+        print("%d waves/SIMD: %.3f ms, %.3f wave instructions per SIMD per "
+              "quad-cycle at 2.4 GHz" % (w, best, insts / (1024 * quads)),
+              file=sys.stderr, flush=True)
+
+
 def _oracle_frames(args):
     """Worker of the all-cores oracle figure: generates two frames of the
     1/f workload, then scores them in turn for budget_s seconds; returns
@@ -544,7 +578,7 @@ def main():
                     "the 1920x1080 10-bit checkerboard pairs, the 1920x1080 "
                     "16-bit bright pairs, the 576x324 8-bit pairs")
     ap.add_argument("--mode", choices=["full", "frames", "strip", "copy",
-                                       "fssim"],
+                                       "fssim", "valu"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
                     "loop (for profiler runs); strip: the same for one "
@@ -552,7 +586,9 @@ def main():
                     "(rows 272..543, 309 input rows); copy: a plain device "
                     "copy of "
                     "known size (counter calibration); fssim: only the 4K "
-                    "float SSIM loop (for profiler runs)")
+                    "float SSIM loop (for profiler runs); valu: the issue "
+                    "rate of the filter's multiply-and-add pair at 4..8 "
+                    "waves per SIMD")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library scores frames on "
@@ -577,6 +613,10 @@ def main():
         sys.exit(1)
     if args.mode == "copy":
         copy_calibration(args.steps)
+        return
+    if args.mode == "valu":
+        ensure_lib()
+        valu_rate(4096)
         return
     ensure_lib()
     import vif_image_fidelity_amd as V

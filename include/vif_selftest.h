@@ -73,6 +73,21 @@ int vif_selftest_statistic(const float *mu1, const float *mu2,
  * expected).  Host pointers; allocates its own small device buffers. */
 int vif_selftest_carry_wait(int *raised, float *row, void *stream);
 
+/* The VALU issue rate of the scale kernels' filter step at a set occupancy,
+ * the practical ceiling against which their issue rate is read: `blocks`
+ * blocks of 256 threads, each thread running `iters` rounds of 32 VALU
+ * instructions (16 multiplies by a uniform factor, 16 adds, in 8 independent
+ * chains, as the filter's tap multiply and accumulate), with each block
+ * reserving the LDS that lets waves_per_simd (3..8) blocks share a CU, one
+ * wave per SIMD each.  out: DEVICE array of blocks * 256 floats (the
+ * results, kept live).  *ms (HOST) = the kernel's duration from HIP events.
+ * The rate follows as blocks * 4 * iters * 32 wave instructions over the
+ * 1024 SIMDs and the duration (or from the VALU and cycle counters).
+ * VIF_EINVAL for arguments outside those ranges (1 <= iters <= 2^24,
+ * 1 <= blocks <= 2^24). */
+int vif_selftest_valu_rate(int waves_per_simd, int iters, long blocks,
+                           float *out, double *ms, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,24 @@ def test_library_taps_equal_oracle_taps(lib, orc):
         assert a.tobytes() == b.tobytes(), s
 
 
+def test_valu_rate_rejects_bad_arguments(lib):
+    """The issue-rate microbenchmark refuses occupancies, round counts and
+    grid sizes outside its ranges before it touches a device."""
+    import ctypes
+    from vif_image_fidelity_amd import _lib
+    ms = ctypes.c_double(0.0)
+    dummy = ctypes.c_void_p(256)   # never dereferenced: the checks come first
+    for w, it, nb in ((2, 1, 1), (9, 1, 1), (6, 0, 1), (6, 1 << 25, 1),
+                      (6, 1, 0), (6, 1, 1 << 25)):
+        assert lib.vif_selftest_valu_rate(w, it, nb, dummy, ctypes.byref(ms),
+                                          None) == _lib.VIF_EINVAL, (w, it, nb)
+    assert lib.vif_selftest_valu_rate(6, 1, 1, None, ctypes.byref(ms),
+                                      None) == _lib.VIF_EINVAL
+    assert lib.vif_selftest_valu_rate(6, 1, 1, dummy, None,
+                                      None) == _lib.VIF_EINVAL
+    assert ms.value == 0.0
+
+
 def test_taps_bad_scale(lib):
     buf = np.zeros(17, np.float32)
     from vif_image_fidelity_amd import _lib

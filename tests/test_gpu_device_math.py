@@ -255,6 +255,24 @@ def test_selftests_reject_bad_options(dev):
         _lib.VIF_EINVAL
 
 
+def test_valu_rate_microbenchmark_runs(dev):
+    """The issue-rate microbenchmark at 6 and 8 waves per SIMD: it runs,
+    times itself and leaves finite results."""
+    import ctypes
+    import torch
+    from vif_image_fidelity_amd import _lib
+    blocks = 256
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32,
+                     device="cuda:0")
+    for w in (6, 8):
+        ms = ctypes.c_double(0.0)
+        _check(_lib.load().vif_selftest_valu_rate(w, 64, blocks,
+                                                  out.data_ptr(),
+                                                  ctypes.byref(ms), None))
+        assert ms.value > 0.0
+        assert torch.isfinite(out).all()
+
+
 def test_carry_wait_gives_up_and_reports(dev):
     """Scale 0 hands each row's fp32 sum from tile to tile; a tile waits for
     its left neighbour's word with a bounded number of reads.  Forced from

@@ -74,6 +74,34 @@ __global__ void statistic_kernel(const float *__restrict__ mu1,
   }
 }
 
+// The filter's instruction pair at a chosen occupancy: each round, every
+// one of 8 accumulators takes a multiply by a uniform (SGPR) factor and a
+// VGPR add, twice (a += t0 * b, then b += t1 * a): 32 VALU instructions,
+// 8 independent chains.  The dynamic LDS the launch reserves caps the
+// blocks per CU; it is never touched.
+__global__ __launch_bounds__(kBlock) void valu_rate_kernel(
+    float *__restrict__ out, float t0, float t1, int iters) {
+  float a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = static_cast<float>(threadIdx.x + k);
+    b[k] = static_cast<float>(k + 1);
+  }
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      a[k] = a[k] + t0 * b[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      b[k] = b[k] + t1 * a[k];
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    s = s + (a[k] + b[k]);
+  out[static_cast<long>(blockIdx.x) * kBlock + threadIdx.x] = s;
+}
+
 dim3 grid_for(long n) {
   return dim3(static_cast<unsigned>((n + kBlock - 1) / kBlock));
 }
@@ -241,6 +269,45 @@ vif_selftest_carry_wait(int *raised, float *row, void *stream) {
   (void)hipFree(rows);
   (void)hipFree(carry);
   (void)hipFree(err);
+  return vifk::status_from_hip(e);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_valu_rate(int waves_per_simd, int iters, long blocks, float *out,
+                       double *ms, void *stream) {
+  if (waves_per_simd < 3 || waves_per_simd > 8 || iters < 1 ||
+      iters > (1 << 24) || blocks < 1 || blocks > (1L << 24) ||
+      out == nullptr || ms == nullptr)
+    return vifk::set_status(VIF_EINVAL);
+  // 160 KiB of LDS per CU: a block reserving a whole number of KiB under a
+  // 1/w share of 159 KiB lets w blocks (one wave per SIMD each) fit, not
+  // w + 1 (exactly 32 KiB, for w = 5, fits only four times)
+  const size_t lds = static_cast<size_t>(159 / waves_per_simd) * 1024;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess)
+    e = hipEventCreate(&e1);
+  if (e == hipSuccess)
+    e = hipEventRecord(e0, s);
+  if (e == hipSuccess) {
+    valu_rate_kernel<<<dim3(static_cast<unsigned>(blocks)), kBlock, lds, s>>>(
+        out, 1.0e-7f, -1.0e-7f, iters);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess)
+    e = hipEventRecord(e1, s);
+  if (e == hipSuccess)
+    e = hipEventSynchronize(e1);
+  float t = 0.0f;
+  if (e == hipSuccess)
+    e = hipEventElapsedTime(&t, e0, e1);
+  if (e == hipSuccess)
+    *ms = t;
+  if (e0)
+    (void)hipEventDestroy(e0);
+  if (e1)
+    (void)hipEventDestroy(e1);
   return vifk::status_from_hip(e);
 }
 
