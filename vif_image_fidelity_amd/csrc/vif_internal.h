@@ -86,6 +86,7 @@ struct ScaleIO {
   unsigned long long *carry;
   unsigned carry_tag;
   int strips, ntx;
+  int slots; // frames x strips: the grid's x dimension before its padding
   float *rows;
   size_t rows_stride;
   int *err;

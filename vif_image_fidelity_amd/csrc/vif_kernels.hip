@@ -224,18 +224,30 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
 // scale's planes, then the three second moments); the second round's
 // vertical results wait in registers until its write.
 //
-// Tile (tx, strip) of frame z: blockIdx.x = z * strips + strip runs
-// fastest, so consecutive blocks take the same tile column of every strip
-// and frame, and tx = first + blockIdx.y (a plane wider than a grid's y
-// dimension allows is covered by several launches).  Frame z reads
+// Tile (tx, strip) of frame z: blockIdx.x runs fastest over the strips of
+// every frame (in the XCD-aware order below; gridDim.x is padded to a
+// multiple of 8 and the padding blocks exit at once), so consecutive blocks
+// take the same tile column of every strip and frame, and tx = first +
+// blockIdx.y (a plane wider than a grid's y dimension allows is covered by
+// several launches).  Frame z reads
 // io.in_ref[z], io.in_dist[z] and writes at its own offsets of the next
 // scale's planes and the row sums.
 template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
     StatArgs stat, int first) {
-  const int z = static_cast<int>(blockIdx.x) / io.strips;
-  const int strip = static_cast<int>(blockIdx.x) - z * io.strips;
+  // XCD-aware order: block x runs on XCD x % 8 (the dispatcher deals the
+  // blocks of a launch round-robin over the eight XCDs, and gridDim.x is a
+  // multiple of 8), so slot (x % 8) * (gridDim.x / 8) + x / 8 gives each XCD
+  // a run of consecutive strips (which share halo rows in its L2), and the
+  // same strip of the next tile column lands on the same XCD
+  const int per = static_cast<int>(gridDim.x) >> 3;
+  const int sp = static_cast<int>(blockIdx.x & 7) * per +
+                 static_cast<int>(blockIdx.x >> 3);
+  if (sp >= io.slots)
+    return; // padding block
+  const int z = sp / io.strips;
+  const int strip = sp - z * io.strips;
   const int tx = first + static_cast<int>(blockIdx.y);
   const InT *__restrict__ ref = static_cast<const InT *>(io.in_ref[z]);
   const InT *__restrict__ dist = static_cast<const InT *>(io.in_dist[z]);
@@ -550,15 +562,17 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
       io.strips != g.strips || io.ntx != g.ntx ||
       static_cast<long>(n) * g.strips > 0x7fffffffL)
     return hipErrorInvalidValue;
+  ScaleIO iox = io;
+  iox.slots = n * g.strips;
   for (int first = 0; first < g.ntx; first += kMaxGridY) {
-    const dim3 grid(static_cast<unsigned>(n * g.strips),
+    const dim3 grid(static_cast<unsigned>((n * g.strips + 7) & ~7),
                     static_cast<unsigned>(std::min(kMaxGridY, g.ntx - first)),
                     1);
     if (stat.inv_nsq != 0.0)
-      launch_one<true>(scale, bpc, grid, block, stream, io, g, sc, taps,
+      launch_one<true>(scale, bpc, grid, block, stream, iox, g, sc, taps,
                        next_taps, stat, first);
     else
-      launch_one<false>(scale, bpc, grid, block, stream, io, g, sc, taps,
+      launch_one<false>(scale, bpc, grid, block, stream, iox, g, sc, taps,
                         next_taps, stat, first);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -574,13 +588,15 @@ hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
   if (col < 0 || col >= g.ntx || io.carry == nullptr || io.rows == nullptr ||
       io.err == nullptr || io.strips != g.strips || io.ntx != g.ntx)
     return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(g.strips), 1, 1);
+  ScaleIO iox = io;
+  iox.slots = g.strips;
+  const dim3 grid(static_cast<unsigned>((g.strips + 7) & ~7), 1, 1);
   if (stat.inv_nsq != 0.0)
     scale_kernel<8, 4, uint8_t, true><<<grid, dim3(kThreads), 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+        iox, g.w, g.h, 1.0f, taps, next_taps, stat, col);
   else
     scale_kernel<8, 4, uint8_t, false><<<grid, dim3(kThreads), 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+        iox, g.w, g.h, 1.0f, taps, next_taps, stat, col);
   return hipGetLastError();
 }
 
