@@ -229,9 +229,8 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
 // multiple of 8 and the padding blocks exit at once), so consecutive blocks
 // take the same tile column of every strip and frame, and tx = first +
 // blockIdx.y (a plane wider than a grid's y dimension allows is covered by
-// several launches).  Frame z reads
-// io.in_ref[z], io.in_dist[z] and writes at its own offsets of the next
-// scale's planes and the row sums.
+// several launches).  Frame z reads io.in_ref[z], io.in_dist[z] and writes
+// at its own offsets of the next scale's planes and the row sums.
 template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
@@ -560,7 +559,7 @@ hipError_t launch_scale(int scale, int bpc, const ScaleIO &io, int n,
   // crosses launches finds its carries written.
   if (io.carry == nullptr || io.rows == nullptr || io.err == nullptr ||
       io.strips != g.strips || io.ntx != g.ntx ||
-      static_cast<long>(n) * g.strips > 0x7fffffffL)
+      static_cast<long>(n) * g.strips > 0x7ffffff8L) // padded grid x fits
     return hipErrorInvalidValue;
   ScaleIO iox = io;
   iox.slots = n * g.strips;
