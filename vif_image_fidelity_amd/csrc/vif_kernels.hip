@@ -85,6 +85,16 @@ __device__ __forceinline__ void settle(float (&v)[A][B]) {
       asm volatile("" : "+v"(v[a][b]));
 }
 
+// An LDS float index the compiler treats as unknown.  Accesses at constant
+// distances from it then share one address register and carry the
+// distances in their instructions' offset fields.  Otherwise the compiler
+// folds a block-uniform part above the paired read's 8-bit offset range into
+// each address and spends a vector add per pair.  The value is unchanged.
+__device__ __forceinline__ int lds_base(int i) {
+  asm volatile("" : "+v"(i));
+  return i;
+}
+
 // LDS layout of the vertical results (bank = dword address mod 64 for a
 // whole wave, or mod 32 for each half of it; the layouts below avoid
 // conflicts in both readings).
@@ -120,7 +130,7 @@ __device__ __forceinline__ void hpass(const float *__restrict__ sV, int ty,
   constexpr int CWP = vpitch<R>();
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const float *row = sV + (q * kTileH + ty) * CWP + seg * HB;
+    const float *row = sV + lds_base((q * kTileH + ty) * CWP + seg * HB);
     float v[HB + 2 * R];
 #pragma unroll
     for (int j = 0; j < HB + 2 * R; ++j)
@@ -443,6 +453,11 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
     const int hd = h >> 1;
     const int ydg = (y0 >> 1) + yd;
     if (sd < kTileW / 4 && ydg < hd) {
+      const float *drow[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        drow[p] = lds + lds_base(static_cast<int>(sVd - lds) + p * kDecPlane +
+                                 dec_row(yd) + 4 * sd + R - RD);
 #pragma unroll
       for (int o = 0; o < 2; ++o) {
         const int xl = sd * 2 + o;
@@ -450,8 +465,7 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
         if (xdg < wd) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const float *row =
-                sVd + p * kDecPlane + dec_row(yd) + 2 * xl + R - RD;
+            const float *row = drow[p] + 2 * o;
             float a = tap(dtaps, 0, ND) * row[0];
 #pragma unroll
             for (int k = 1; k < ND; ++k)
