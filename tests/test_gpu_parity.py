@@ -453,7 +453,7 @@ def test_contexts_in_two_threads(V, orc):
             assert out.tobytes() == want[key][i].tobytes(), (key, i)
 
 
-def test_graph_replays_match_direct_launches(V, orc):
+def test_timed_and_untimed_launches_interleave(V, orc):
     """Frames submitted with and without kernel timing (the timed ones
     record HIP events around each launch) interleave over changing frames,
     with host synchronisation between rounds: every frame must give the

@@ -134,6 +134,21 @@ __device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
 //   numerator (C's MIN(g, limit), see StatArgs); then the two ratios and
 //   their log2.  With nsq = 0 nothing is special-cased: IEEE arithmetic
 //   throughout, as in the plain definition.
+//
+//   Some of these selects are written as one maximum or minimum instruction
+//   where that gives the same terms:
+//   - the clamps of s1 and s2 at 0, always: xx and yy are >= +0 and never
+//     -0 (sums of products of values >= +0), and so are m11 and m22; their
+//     difference is then never NaN and never -0 (a difference is -0 only
+//     when the left operand is -0), and for such a value max(s, +0) is
+//     exactly s < 0 ? 0 : s;
+//   - the floor of sv at eps and the gain limit, in the kPow2 form only:
+//     there s1 >= nsq >= 2^-20 in this branch, so g = s12 / s1, g * s12 and
+//     sv are finite, never NaN, and max(sv, eps) is the select.  The limit
+//     is >= +0 and never NaN and g >= +0 here, so min(g, gain) is the select
+//     except when g and gain are zeros of opposite sign, where g * g is +0
+//     either way and the terms are the same.  (With nsq = 0, a zero s1 makes
+//     g NaN, and the selects must keep C's handling of it.)
 template <bool kPow2>
 __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
                                             float yy, float xy,
@@ -145,8 +160,8 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
   float s1 = xx - m11;
   float s2 = yy - m22;
   const float s12 = xy - m12;
-  s1 = s1 < 0.0f ? 0.0f : s1;
-  s2 = s2 < 0.0f ? 0.0f : s2;
+  s1 = __builtin_fmaxf(s1, 0.0f);
+  s2 = __builtin_fmaxf(s2, 0.0f);
   if (static_cast<double>(s1) < sa.nsq) {
     num = 1.0f;
     den = 1.0f;
@@ -163,8 +178,13 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
     sv = s2;
     g = 0.0f;
   }
-  sv = sv < kEps ? kEps : sv;
-  g = g < sa.gain ? g : sa.gain;
+  if constexpr (kPow2) {
+    sv = __builtin_fmaxf(sv, kEps);
+    g = __builtin_fminf(g, sa.gain);
+  } else {
+    sv = sv < kEps ? kEps : sv;
+    g = g < sa.gain ? g : sa.gain;
+  }
   const float gg = g * g;
   const float a = gg * s1;
   num = log2_poly(num_ratio<kPow2>(a, sv, sa.nsq));
