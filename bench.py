@@ -481,6 +481,123 @@ def copy_calibration(launches):
           file=sys.stderr, flush=True)
 
 
+# The scale-0 kernel's tile: 16 x 112 output pixels, with a halo of its
+# filter's radius (8) on every side.
+STAGE_TILE_H, STAGE_TILE_W, STAGE_R = 16, 112, 8
+
+
+def _mirror_clamp(i, n):
+    """The kernels' edge rule: reflect about the edge sample once, then
+    clamp into [0, n)."""
+    m = np.abs(i)
+    m = np.where(m > n - 1, 2 * (n - 1) - m, m)
+    return np.clip(m, 0, n - 1)
+
+
+def _stage_rows_cols(w, h):
+    strips = -(-h // STAGE_TILE_H)
+    ntx = -(-w // STAGE_TILE_W)
+    rows = _mirror_clamp(STAGE_TILE_H * np.arange(strips)[:, None] - STAGE_R +
+                         np.arange(STAGE_TILE_H + 2 * STAGE_R)[None, :], h)
+    cols = _mirror_clamp(STAGE_TILE_W * np.arange(ntx)[:, None] - STAGE_R +
+                         np.arange(STAGE_TILE_W + 2 * STAGE_R)[None, :], w)
+    return strips, ntx, rows, cols
+
+
+def stage_tile_sums(pairs, w, h):
+    """What vif_selftest_stage_loads stores for the frame pairs `pairs`
+    (host arrays): for tile column c, frame z and strip r, at
+    [(c * n + z) * strips + r], the sum of the raw samples of the tile's 32
+    mirrored rows x 128 mirrored columns of both planes, mod 2^32."""
+    strips, ntx, rows, cols = _stage_rows_cols(w, h)
+    out = np.zeros((ntx, len(pairs), strips), dtype=np.int64)
+    for z, (ref, dist) in enumerate(pairs):
+        for plane in (ref, dist):
+            rs = plane.astype(np.int64)[rows].sum(axis=1)  # strips x w
+            out[:, z, :] += rs[:, cols].sum(axis=2).T
+    return (out.reshape(-1) & 0xFFFFFFFF).astype(np.uint32)
+
+
+def stage_probe_fetch_bytes(ptr_pairs, w, h, bytes_per_sample):
+    """HBM bytes one launch of the staging probe must fetch when every
+    128-byte line reaches each XCD's L2 once: the launch's blocks go to XCDs
+    round-robin (block x to XCD x % 8; the grid's x dimension is padded to a
+    multiple of 8), block x takes slot (x % 8) * (gridDim.x / 8) + x / 8
+    (frame z = slot / strips, strip slot % strips), and each block reads, in
+    each of its 32 rows and each plane, the samples from its tile's first to
+    its last (mirrored) column.  Returns (bytes summed over the XCDs' distinct
+    lines, bytes of the planes themselves).  ptr_pairs: device addresses of
+    the frames' planes."""
+    n = len(ptr_pairs)
+    strips, ntx, rows, cols = _stage_rows_cols(w, h)
+    slots = n * strips
+    per = ((slots + 7) & ~7) >> 3
+    slot = np.arange(slots)
+    xcd = slot // per
+    z, r = slot // strips, slot % strips
+    lo, hi = cols.min(axis=1), cols.max(axis=1)            # per tile column
+    bps = bytes_per_sample
+    keys = []
+    for p in range(2):
+        base = np.array([pp[p] for pp in ptr_pairs], dtype=np.int64)[z]
+        # [slot, row, column of tiles]
+        row_off = (rows[r].astype(np.int64) * w)[:, :, None]
+        a0 = base[:, None, None] + (row_off + lo[None, None, :]) * bps
+        a1 = base[:, None, None] + (row_off + hi[None, None, :]) * bps + \
+            bps - 1
+        l0, l1 = a0 >> 7, a1 >> 7
+        span = int((l1 - l0).max()) + 1
+        xk = (xcd.astype(np.int64) << 44)[:, None, None]
+        for d in range(span):
+            ln = l0 + d
+            keys.append((xk + ln)[ln <= l1])
+    lines = np.unique(np.concatenate(keys)).size
+    return lines * 128, 2 * n * w * h * bps
+
+
+def stage_probe(frames, w, h, bpc, batch, launches):
+    """Runs the staging probe (vif_selftest_stage_loads) `launches` times on
+    the resident frames, batch frames per launch, alternating between two
+    groups of frames (so one launch's lines are gone from the L2 when the
+    next group is read again); checks the first launch of each group against
+    the host's tile sums and prints the bytes each launch must fetch."""
+    import ctypes
+    import torch
+    from vif_image_fidelity_amd import _lib
+    lib = _lib.load()
+    pairs = _device_pairs(frames)
+    groups = [list(range(g * batch, (g + 1) * batch)) for g in range(2)]
+    strips, ntx = -(-h // STAGE_TILE_H), -(-w // STAGE_TILE_W)
+    out = torch.empty(batch * strips * ntx, dtype=torch.int32,
+                      device="cuda:0")
+    bps = 1 if bpc == 8 else 2
+    expect = []
+    for g in groups:
+        ptrs = [(pairs[i][0].data_ptr(), pairs[i][1].data_ptr()) for i in g]
+        expect.append(stage_probe_fetch_bytes(ptrs, w, h, bps))
+    for k in range(launches):
+        g = groups[k % 2]
+        refs = (ctypes.c_void_p * batch)(*[pairs[i][0].data_ptr() for i in g])
+        dists = (ctypes.c_void_p * batch)(*[pairs[i][1].data_ptr()
+                                            for i in g])
+        rc = lib.vif_selftest_stage_loads(refs, dists, batch, w, h, bpc,
+                                          out.data_ptr(), None)
+        if rc != 0:
+            raise RuntimeError("vif_selftest_stage_loads: %d" % rc)
+        if k < 2:
+            want = stage_tile_sums([(frames[i][0], frames[i][1]) for i in g],
+                                   w, h)
+            got = out.cpu().numpy().view(np.uint32)
+            if not np.array_equal(got, want):
+                raise AssertionError("staging probe read the wrong samples")
+    torch.cuda.synchronize()
+    for i, (fetch, planes) in enumerate(expect):
+        print("staging probe, frames %s: %d launches; each must fetch %d "
+              "bytes (%.1f KiB; the planes alone are %d bytes, x%.4f)"
+              % (groups[i], (launches - i + 1) // 2, fetch, fetch / 1024.0,
+                 planes, fetch / planes), file=sys.stderr, flush=True)
+
+
 VALU_WAVES = (4, 5, 6, 7, 8)
 
 
@@ -578,7 +695,7 @@ def main():
                     "the 1920x1080 10-bit checkerboard pairs, the 1920x1080 "
                     "16-bit bright pairs, the 576x324 8-bit pairs")
     ap.add_argument("--mode", choices=["full", "frames", "strip", "copy",
-                                       "fssim", "valu"],
+                                       "fssim", "valu", "stageprobe"],
                     default="full",
                     help="full: the JSON line; frames: only the timed 4K "
                     "loop (for profiler runs); strip: the same for one "
@@ -588,7 +705,10 @@ def main():
                     "known size (counter calibration); fssim: only the 4K "
                     "float SSIM loop (for profiler runs); valu: the issue "
                     "rate of the filter's multiply-and-add pair at 4..8 "
-                    "waves per SIMD")
+                    "waves per SIMD; stageprobe: the scale-0 kernel's input "
+                    "staging alone on 8 of the 4K frames in two groups of "
+                    "--batch, --steps launches (counter calibration for its "
+                    "access shape)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library scores frames on "
@@ -644,6 +764,9 @@ def main():
           file=sys.stderr, flush=True)
     frames4k = synth.pink_4k_8bit(frames=args.frames)
     w, h, bpc = 3840, 2160, 8
+    if args.mode == "stageprobe":
+        stage_probe(frames4k, w, h, bpc, batch, args.steps)
+        return
     if args.mode == "fssim":
         fb = batch if "--batch" in sys.argv else 1
         dt, _, geom = time_fssim(V, frames4k, w, h, bpc, args.steps * fb,

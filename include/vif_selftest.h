@@ -88,6 +88,25 @@ int vif_selftest_carry_wait(int *raised, float *row, void *stream);
 int vif_selftest_valu_rate(int waves_per_simd, int iters, long blocks,
                            float *out, double *ms, void *stream);
 
+/* The scale-0 kernel's input staging alone, for calibrating HBM traffic
+ * counters against that kernel's own access shape: a launch with the
+ * scale-0 kernel's grid, block order and staging code over the n frame
+ * pairs ref[z], dist[z] (z < n; DEVICE pointers to w x h planes of bpc-bit
+ * samples, row-major, one byte per sample at 8 bits, two otherwise; host
+ * arrays of n pointers), whose blocks each load their tile of 32 rows x 128
+ * columns of both planes (the 16 x 112 output pixels plus the radius-8 halo,
+ * mirrored at the plane's edges, 8 samples per load for tiles inside a plane
+ * whose width is a multiple of 8 and whose planes are aligned to 8 samples)
+ * into LDS and do nothing else.  Block (frame z, strip r, tile column c)
+ * then stores the sum of its tile's raw samples, both planes, at
+ * out[(c * n + z) * ceil(h / 16) + r]: out is a DEVICE array of
+ * n * ceil(h / 16) * ceil(w / 112) unsigned values.  Synchronous.
+ * VIF_EINVAL for n outside 1..VIF_MAX_BATCH, a geometry vif_create refuses,
+ * bpc not 8/10/12/16 or a NULL pointer. */
+int vif_selftest_stage_loads(const void *const *ref, const void *const *dist,
+                             int n, int w, int h, int bpc, unsigned *out,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

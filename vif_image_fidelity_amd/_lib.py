@@ -119,6 +119,8 @@ def load():
                                     vp], ip),
         "vif_selftest_carry_wait": ([ctypes.POINTER(ip), fp, vp], ip),
         "vif_selftest_valu_rate": ([ip, ip, ctypes.c_long, vp, dp, vp], ip),
+        "vif_selftest_stage_loads": ([ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      ip, ip, ip, ip, vp, vp], ip),
         "fssim_create": ([ip, ip, ip], vp),
         "fssim_create_batch": ([ip, ip, ip, ip], vp),
         "fssim_submit_batch": ([vp, ip, ctypes.POINTER(vp),
@@ -160,7 +162,7 @@ def exported_symbols():
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
             "vif_selftest_log2", "vif_selftest_ratios",
             "vif_selftest_statistic", "vif_selftest_carry_wait",
-            "vif_selftest_valu_rate",
+            "vif_selftest_valu_rate", "vif_selftest_stage_loads",
             "fssim_create", "fssim_create_batch", "fssim_submit_batch",
             "fssim_destroy", "fssim_geometry", "fssim_score",
             "fssim_submit", "fssim_collect", "fssim_pending",

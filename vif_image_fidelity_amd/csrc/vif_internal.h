@@ -142,6 +142,14 @@ hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
                                 const StatArgs &stat, int col,
                                 hipStream_t stream);
 
+// Scale 0's input staging alone, for n frames of g (io.in_*, io.vec_in,
+// io.strips, io.ntx as for launch_scale): every block stages its tile into
+// LDS as the scale-0 kernel does and stores the sum of the tile's samples at
+// out[tx * n * strips + frame * strips + strip].
+hipError_t launch_stage_probe(int bpc, const ScaleIO &io, int n,
+                              const ScaleGeom &g, unsigned *out,
+                              hipStream_t stream);
+
 // Blocks of the scale-0 kernel the current device keeps resident at once
 // (blocks per CU times CUs).
 hipError_t scale0_resident_blocks(int bpc, int *blocks);

@@ -220,6 +220,84 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
   }
 }
 
+// The slot of this block in the grid's x dimension, in the XCD-aware order:
+// block x runs on XCD x % 8 (the dispatcher deals the blocks of a launch
+// round-robin over the eight XCDs, and gridDim.x is a multiple of 8), so
+// slot (x % 8) * (gridDim.x / 8) + x / 8 gives each XCD a run of
+// consecutive strips (which share halo rows in its L2), and the same strip
+// of the next tile column lands on the same XCD.  Slots at or past the
+// launch's frames x strips are padding.
+__device__ __forceinline__ int block_slot() {
+  const int per = static_cast<int>(gridDim.x) >> 3;
+  return static_cast<int>(blockIdx.x & 7) * per +
+         static_cast<int>(blockIdx.x >> 3);
+}
+
+// Step 1 of the scale kernels: the input tile [IR][CW] of ref, then of
+// dist, into LDS in the planes' own sample type, for the tile whose first
+// output pixel is (x0, y0).  A tile whose columns all lie inside the plane,
+// in a plane that allows it (vec_in), loads 8 samples per thread and load:
+// 16 threads per row, 16 rows per pass, two passes per plane (x0 - R is a
+// multiple of 8, so every load is aligned).  Other tiles load one sample per
+// thread and row, mirroring each column: waves 0-1 the even rows, waves 2-3
+// the odd ones, so the row (and its mirror) is uniform in a wave.  Either way
+// all of a thread's loads are issued before the first store.
+template <int R, typename InT>
+__device__ __forceinline__ void stage_tile(InT *sIn,
+                                           const InT *__restrict__ ref,
+                                           const InT *__restrict__ dist,
+                                           int vec_in, int x0, int y0, int w,
+                                           int h, int tid) {
+  constexpr int CW = kTileW + 2 * R;
+  constexpr int IR = kTileH + 2 * R;
+  bool vec = false;
+  if constexpr (sizeof(InT) < 4)
+    vec = vec_in != 0 && x0 - R >= 0 && x0 - R + CW <= w;
+  if (vec) {
+    if constexpr (sizeof(InT) < 4) {
+      constexpr int kSpl = 8;               // samples per load
+      constexpr int kTpr = CW / kSpl;       // threads per row
+      constexpr int kRpp = kThreads / kTpr; // rows per pass
+      using Vec =
+          typename std::conditional<sizeof(InT) == 1, uint2, uint4>::type;
+      static_assert(sizeof(Vec) == kSpl * sizeof(InT), "8 samples");
+      static_assert(CW % kSpl == 0 && IR % kRpp == 0, "whole passes");
+      const int q = tid % kTpr;
+      const int r0 = tid / kTpr;
+      Vec a[IR / kRpp], b[IR / kRpp];
+#pragma unroll
+      for (int it = 0; it < IR / kRpp; ++it) {
+        const int j = r0 + kRpp * it;
+        const unsigned gy = static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
+        const unsigned base = gy * static_cast<unsigned>(w) + (x0 - R);
+        a[it] = reinterpret_cast<const Vec *>(ref + base)[q];
+        b[it] = reinterpret_cast<const Vec *>(dist + base)[q];
+      }
+#pragma unroll
+      for (int it = 0; it < IR / kRpp; ++it) {
+        const int j = r0 + kRpp * it;
+        *reinterpret_cast<Vec *>(sIn + j * CW + kSpl * q) = a[it];
+        *reinterpret_cast<Vec *>(sIn + IR * CW + j * CW + kSpl * q) = b[it];
+      }
+    }
+  } else {
+    const int c = tid & 127;
+    const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+    static_assert(IR % 2 == 0, "the two row phases cover the tile");
+    if (c < CW) {
+      const unsigned gx = static_cast<unsigned>(mirror_clamp(x0 - R + c, w));
+#pragma unroll
+      for (int it = 0; it < IR / 2; ++it) {
+        const int j = half + 2 * it;
+        const unsigned gy = static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
+        const unsigned off = gy * static_cast<unsigned>(w) + gx;
+        sIn[j * CW + c] = ref[off];
+        sIn[IR * CW + j * CW + c] = dist[off];
+      }
+    }
+  }
+}
+
 // R: filter radius of this scale (taps 2R+1).  RD: radius of the next
 // scale's low-pass (0 at the last scale: no decimation).
 //
@@ -235,7 +313,7 @@ __device__ __forceinline__ void chain_rows(const ScaleIO &io,
 // vertical results wait in registers until its write.
 //
 // Tile (tx, strip) of frame z: blockIdx.x runs fastest over the strips of
-// every frame (in the XCD-aware order below; gridDim.x is padded to a
+// every frame (in the XCD-aware order of block_slot; gridDim.x is padded to a
 // multiple of 8 and the padding blocks exit at once), so consecutive blocks
 // take the same tile column of every strip and frame, and tx = first +
 // blockIdx.y (a plane wider than a grid's y dimension allows is covered by
@@ -245,14 +323,7 @@ template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
     ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
     StatArgs stat, int first) {
-  // XCD-aware order: block x runs on XCD x % 8 (the dispatcher deals the
-  // blocks of a launch round-robin over the eight XCDs, and gridDim.x is a
-  // multiple of 8), so slot (x % 8) * (gridDim.x / 8) + x / 8 gives each XCD
-  // a run of consecutive strips (which share halo rows in its L2), and the
-  // same strip of the next tile column lands on the same XCD
-  const int per = static_cast<int>(gridDim.x) >> 3;
-  const int sp = static_cast<int>(blockIdx.x & 7) * per +
-                 static_cast<int>(blockIdx.x >> 3);
+  const int sp = block_slot();
   if (sp >= io.slots)
     return; // padding block
   const int z = sp / io.strips;
@@ -290,65 +361,8 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   const int tid = threadIdx.x;
   const int x0 = tx * kTileW;
   const int y0 = strip * kTileH;
-  // 1. input tile [IR][CW] for ref then dist.  A tile whose columns all lie
-  //    inside the plane, in a plane that allows it (io.vec_in), loads 8
-  //    samples per thread and load: 16 threads per row, 16 rows per pass,
-  //    two passes per plane (x0 - R is a multiple of 8, so every load is
-  //    aligned).  Other tiles load one sample per thread and row, mirroring
-  //    each column: waves 0-1 the even rows, waves 2-3 the odd ones, so the
-  //    row (and its mirror) is uniform in a wave.  Either way all of a
-  //    thread's loads are issued before the first store.
-  {
-    bool vec = false;
-    if constexpr (sizeof(InT) < 4)
-      vec = io.vec_in != 0 && x0 - R >= 0 && x0 - R + CW <= w;
-    if (vec) {
-      if constexpr (sizeof(InT) < 4) {
-        constexpr int kSpl = 8;                 // samples per load
-        constexpr int kTpr = CW / kSpl;         // threads per row
-        constexpr int kRpp = kThreads / kTpr;   // rows per pass
-        using Vec = typename std::conditional<sizeof(InT) == 1, uint2,
-                                              uint4>::type;
-        static_assert(sizeof(Vec) == kSpl * sizeof(InT), "8 samples");
-        static_assert(CW % kSpl == 0 && IR % kRpp == 0, "whole passes");
-        const int q = tid % kTpr;
-        const int r0 = tid / kTpr;
-        Vec a[IR / kRpp], b[IR / kRpp];
-#pragma unroll
-        for (int it = 0; it < IR / kRpp; ++it) {
-          const int j = r0 + kRpp * it;
-          const unsigned gy =
-              static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
-          const unsigned base = gy * static_cast<unsigned>(w) + (x0 - R);
-          a[it] = reinterpret_cast<const Vec *>(ref + base)[q];
-          b[it] = reinterpret_cast<const Vec *>(dist + base)[q];
-        }
-#pragma unroll
-        for (int it = 0; it < IR / kRpp; ++it) {
-          const int j = r0 + kRpp * it;
-          *reinterpret_cast<Vec *>(sIn + j * CW + kSpl * q) = a[it];
-          *reinterpret_cast<Vec *>(sIn + IR * CW + j * CW + kSpl * q) = b[it];
-        }
-      }
-    } else {
-      const int c = tid & 127;
-      const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
-      static_assert(IR % 2 == 0, "the two row phases cover the tile");
-      if (c < CW) {
-        const unsigned gx =
-            static_cast<unsigned>(mirror_clamp(x0 - R + c, w));
-#pragma unroll
-        for (int it = 0; it < IR / 2; ++it) {
-          const int j = half + 2 * it;
-          const unsigned gy =
-              static_cast<unsigned>(mirror_clamp(y0 - R + j, h));
-          const unsigned off = gy * static_cast<unsigned>(w) + gx;
-          sIn[j * CW + c] = ref[off];
-          sIn[IR * CW + j * CW + c] = dist[off];
-        }
-      }
-    }
-  }
+  // 1. input tile
+  stage_tile<R, InT>(sIn, ref, dist, io.vec_in, x0, y0, w, h, tid);
   __syncthreads();
 
   // 2. vertical passes: thread (vc, vb) owns column vc, tile rows
@@ -523,6 +537,47 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
                y0 + (tid >> 1), h, tid);
 }
 
+// ------------------------------------------------------------ staging probe
+
+// Scale 0's input staging alone: the blocks of a scale-0 launch, in the same
+// order and with the scale kernel's own staging code, load the same tiles
+// into LDS and do nothing else; each block then adds its tile's samples and
+// stores the sum at out[tx * slots + slot], so no load is dead and the host
+// can check what was read.  Its fetched bytes, against the lines its blocks
+// touch, calibrate the HBM traffic counters for the scale kernel's access
+// shape.
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void stage_probe_kernel(
+    ScaleIO io, int w, int h, int first, unsigned *__restrict__ out) {
+  constexpr int R = 8;
+  constexpr int kElems = 2 * (kTileH + 2 * R) * (kTileW + 2 * R);
+  __shared__ __attribute__((aligned(16))) InT sIn[kElems];
+  __shared__ unsigned red[kThreads / 64];
+  const int sp = block_slot();
+  if (sp >= io.slots)
+    return; // padding block
+  const int z = sp / io.strips;
+  const int strip = sp - z * io.strips;
+  const int tx = first + static_cast<int>(blockIdx.y);
+  const int tid = threadIdx.x;
+  stage_tile<R, InT>(sIn, static_cast<const InT *>(io.in_ref[z]),
+                     static_cast<const InT *>(io.in_dist[z]), io.vec_in,
+                     tx * kTileW, strip * kTileH, w, h, tid);
+  __syncthreads();
+  unsigned sum = 0;
+  for (int i = tid; i < kElems; i += kThreads)
+    sum += sIn[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    sum += __shfl_down(sum, off);
+  if ((tid & 63) == 0)
+    red[tid >> 6] = sum;
+  __syncthreads();
+  if (tid == 0)
+    out[static_cast<size_t>(tx) * io.slots + sp] =
+        red[0] + red[1] + red[2] + red[3];
+}
+
 // ------------------------------------------------------------------ launch
 
 // One launch of the scale kernel of `scale` for the statistic's form kPow2
@@ -611,6 +666,31 @@ hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
     scale_kernel<8, 4, uint8_t, false><<<grid, dim3(kThreads), 0, stream>>>(
         iox, g.w, g.h, 1.0f, taps, next_taps, stat, col);
   return hipGetLastError();
+}
+
+hipError_t launch_stage_probe(int bpc, const ScaleIO &io, int n,
+                              const ScaleGeom &g, unsigned *out,
+                              hipStream_t stream) {
+  if (n < 1 || n > kMaxBatch || out == nullptr || io.strips != g.strips ||
+      io.ntx != g.ntx)
+    return hipErrorInvalidValue;
+  ScaleIO iox = io;
+  iox.slots = n * g.strips;
+  for (int first = 0; first < g.ntx; first += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>((n * g.strips + 7) & ~7),
+                    static_cast<unsigned>(std::min(kMaxGridY, g.ntx - first)),
+                    1);
+    if (bpc == 8)
+      stage_probe_kernel<uint8_t><<<grid, dim3(kThreads), 0, stream>>>(
+          iox, g.w, g.h, first, out);
+    else
+      stage_probe_kernel<uint16_t><<<grid, dim3(kThreads), 0, stream>>>(
+          iox, g.w, g.h, first, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t scale0_resident_blocks(int bpc, int *blocks) {

@@ -311,4 +311,40 @@ vif_selftest_valu_rate(int waves_per_simd, int iters, long blocks, float *out,
   return vifk::status_from_hip(e);
 }
 
+__attribute__((visibility("default"))) int
+vif_selftest_stage_loads(const void *const *ref, const void *const *dist,
+                         int n, int w, int h, int bpc, unsigned *out,
+                         void *stream) {
+  if (ref == nullptr || dist == nullptr || out == nullptr || n < 1 ||
+      n > vifk::kMaxBatch || w < VIF_MIN_SIDE || h < VIF_MIN_SIDE ||
+      static_cast<long>(w) * h > VIF_MAX_PIXELS ||
+      (bpc != 8 && bpc != 10 && bpc != 12 && bpc != 16))
+    return vifk::set_status(VIF_EINVAL);
+  vifk::ScaleGeom g{};
+  g.w = w;
+  g.h = h;
+  g.strips = (h + vifk::kTileH - 1) / vifk::kTileH;
+  g.ntx = (w + vifk::kTileW - 1) / vifk::kTileW;
+  vifk::ScaleIO io{};
+  // 8 samples per load where the scale-0 kernel would take them
+  const uintptr_t align = bpc == 8 ? 8 : 16;
+  bool vec = w % 8 == 0;
+  for (int z = 0; z < n; ++z) {
+    if (ref[z] == nullptr || dist[z] == nullptr)
+      return vifk::set_status(VIF_EINVAL);
+    io.in_ref[z] = ref[z];
+    io.in_dist[z] = dist[z];
+    vec = vec && reinterpret_cast<uintptr_t>(ref[z]) % align == 0 &&
+          reinterpret_cast<uintptr_t>(dist[z]) % align == 0;
+  }
+  io.vec_in = vec ? 1 : 0;
+  io.strips = g.strips;
+  io.ntx = g.ntx;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = vifk::launch_stage_probe(bpc, io, n, g, out, s);
+  if (e != hipSuccess)
+    return vifk::status_from_hip(e);
+  return finish(s);
+}
+
 } // extern "C"
