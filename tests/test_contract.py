@@ -70,8 +70,8 @@ SOURCE_MUTANTS = [
      "acc[0][i] = __builtin_fmaf(t, x, acc[0][i]);"),
     ("vif_device_math.h", "  return static_cast<float>(e) + q;",
      "  return log2f(x);"),
-    ("vif_kernels.hip", "  const int tx = first + static_cast<int>(blockIdx.y);",
-     "  const int tx = first + static_cast<int>(blockIdx.y);\n"
+    ("vif_kernels.hip", "  const int x0 = tx * kTileW;",
+     "  const int x0 = tx * kTileW;\n"
      "  atomicAdd(io.rows, 1.0f);"),
     ("vif_kernels.hip", "  float acc = 0.0f;\n  if (tx > 0)",
      "  float acc = 0.0f;\n  __hip_atomic_fetch_add(io.rows, 1.0f, "
