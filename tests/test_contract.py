@@ -66,8 +66,8 @@ def test_flag_mutants_caught(flags, flag_edit):
 
 
 SOURCE_MUTANTS = [
-    ("vif_kernels.hip", "acc[0][i] = acc[0][i] + t * x;",
-     "acc[0][i] = __builtin_fmaf(t, x, acc[0][i]);"),
+    ("vif_kernels.hip", "a[i] = k == 0 ? t * val : a[i] + t * val;",
+     "a[i] = k == 0 ? t * val : __builtin_fmaf(t, val, a[i]);"),
     ("vif_device_math.h", "  return static_cast<float>(e) + q;",
      "  return log2f(x);"),
     ("vif_kernels.hip", "  const int x0 = tx * kTileW;",

@@ -120,6 +120,69 @@ __device__ __forceinline__ int dec_row(int yd) {
 }
 constexpr int kDecPlane = 1088; // >= dec_row(7) + 128, 0 mod 64
 
+// Input row j (counted from the first input row the outputs read) of one
+// quantity into the vertical accumulators a[i] of OUT consecutive output
+// rows: output i adds tap j - i; its first tap starts the accumulator.
+template <int N, int OUT>
+__device__ __forceinline__ void vacc(float (&a)[OUT], float val, int j, int,
+                                     const TapArgs &taps) {
+#pragma unroll
+  for (int i = 0; i < OUT; ++i) {
+    const int k = j - i;
+    if (k >= 0 && k < N) {
+      const float t = tap(taps, k, N);
+      a[i] = k == 0 ? t * val : a[i] + t * val;
+    }
+  }
+}
+
+template <int A>
+__device__ __forceinline__ void settle1(float (&v)[A]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+    asm volatile("" : "+v"(v[a]));
+}
+
+// The vertical pass of group G over a column of the input tile: so is the
+// group's own plane, sp the other.  Own plane: mean vm and square vs at all
+// kTileH rows, the next scale's low-pass vd at the even rows; cross product
+// x*y: vx at rows G*kTileH/2 .. + kTileH/2 - 1, which read input rows from
+// G*kTileH/2 on.  G is a template argument, so every tap index is a constant.
+template <int R, int RD, typename InT, int G>
+__device__ __forceinline__ void
+vpass(const InT *so, const InT *sp, float sc, const TapArgs &taps,
+      const TapArgs &dtaps, float (&vm)[kTileH], float (&vs)[kTileH],
+      float (&vx)[kTileH / 2], float (&vd)[kTileH / 2]) {
+  constexpr int N = 2 * R + 1;
+  constexpr int ND = 2 * RD + 1;
+  constexpr int CW = kTileW + 2 * R;
+  constexpr int VR = kTileH;
+  constexpr int VC = kTileH / 2;
+#pragma unroll
+  for (int j = 0; j < VR + 2 * R; ++j) {
+    const float p = to_float<InT>(so[j * CW], sc);
+    vacc<N, VR>(vm, p, j, 0, taps);
+    vacc<N, VR>(vs, p * p, j, 0, taps);
+    constexpr int J0 = G * VC;
+    if (j >= J0 && j < J0 + VC + 2 * R) {
+      const float o = to_float<InT>(sp[j * CW], sc);
+      // x * y in that operand order whichever plane is the thread's own
+      vacc<N, VC>(vx, G == 0 ? p * o : o * p, j - J0, 0, taps);
+    }
+    if constexpr (RD > 0) {
+#pragma unroll
+      for (int m = 0; m < VC; ++m) {
+        const int k = j - 2 * m - R + RD;
+        if (k >= 0 && k < ND) {
+          const float t = tap(dtaps, k, ND);
+          vd[m] = k == 0 ? t * p : vd[m] + t * p;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Horizontal pass of NQ quantities stored in LDS as [q][kTileH][vpitch]:
 // thread (ty, seg) computes tile row ty, columns seg*HB .. seg*HB+HB-1.
 template <int R, int NQ, int HB>
@@ -338,7 +401,6 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   constexpr int CW = kTileW + 2 * R; // columns of the vertical pass
   constexpr int IR = kTileH + 2 * R; // input rows
   constexpr int CWP = vpitch<R>();   // conflict-free horizontal reads
-  constexpr int VB = 8;              // rows per thread in the vertical pass
   constexpr int HB = 7;              // outputs per thread, horizontal pass
   constexpr int kQA = 2;             // quantities of the first round
   constexpr int kInFloats =
@@ -354,7 +416,6 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   static_assert(CWP >= CW && CWP % 16 == 8, "vertical-result pitch");
   static_assert(kTileH / 2 == 8 && kTileW / 4 <= 32, "decimation rows");
   static_assert(kTileW == 16 * HB, "16 horizontal segments per row");
-  static_assert(kTileH == 2 * VB, "two row blocks");
   __shared__ __attribute__((aligned(16))) float lds[kLds];
   InT *sIn = reinterpret_cast<InT *>(lds);
 
@@ -365,63 +426,31 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   stage_tile<R, InT>(sIn, ref, dist, io.vec_in, x0, y0, w, h, tid);
   __syncthreads();
 
-  // 2. vertical passes: thread (vc, vb) owns column vc, tile rows
-  //    vb*8 .. vb*8+7; the next scale's low-pass at tile rows vb*8 + 2m.
+  // 2. vertical passes: thread (vc, g) owns column vc and one plane, g = 0
+  //    (waves 0-1) ref, g = 1 (waves 2-3) dist: the plane's mean and square
+  //    at all kTileH rows, the next scale's low-pass of the plane at the even
+  //    rows, and the cross product x*y at rows 8g .. 8g + 7.  Owning every
+  //    row of a column, a thread reads each input row once and shares more of
+  //    the symmetric taps' products between its outputs; the two groups do
+  //    the same work and keep the same registers.
+  constexpr int VR = kTileH;
+  constexpr int VC = kTileH / 2;       // rows of the cross product per group
   const int vc = tid & 127;
-  const int vb = tid >> 7;
+  const int vg = __builtin_amdgcn_readfirstlane(tid >> 7);
   const bool vact = vc < CW;
-  float acc[5][VB];
-  float dacc[2][VB / 2];
+  float vm[VR], vs[VR], vx[VC], vd[VC];
   if (vact) {
-    const InT *sx = sIn + (vb * VB) * CW + vc;
-    const InT *sy = sx + IR * CW;
-#pragma unroll
-    for (int j = 0; j < VB + 2 * R; ++j) {
-      const float x = to_float<InT>(sx[j * CW], in_scale);
-      const float y = to_float<InT>(sy[j * CW], in_scale);
-      const float xx = x * x;
-      const float yy = y * y;
-      const float xy = x * y;
-#pragma unroll
-      for (int i = 0; i < VB; ++i) {
-        const int k = j - i;
-        if (k >= 0 && k < N) {
-          const float t = tap(taps, k, N);
-          if (k == 0) {
-            acc[0][i] = t * x;
-            acc[1][i] = t * y;
-            acc[2][i] = t * xx;
-            acc[3][i] = t * yy;
-            acc[4][i] = t * xy;
-          } else {
-            acc[0][i] = acc[0][i] + t * x;
-            acc[1][i] = acc[1][i] + t * y;
-            acc[2][i] = acc[2][i] + t * xx;
-            acc[3][i] = acc[3][i] + t * yy;
-            acc[4][i] = acc[4][i] + t * xy;
-          }
-        }
-      }
-      if constexpr (RD > 0) {
-#pragma unroll
-        for (int m = 0; m < VB / 2; ++m) {
-          const int k = j - 2 * m - R + RD;
-          if (k >= 0 && k < ND) {
-            const float t = tap(dtaps, k, ND);
-            if (k == 0) {
-              dacc[0][m] = t * x;
-              dacc[1][m] = t * y;
-            } else {
-              dacc[0][m] = dacc[0][m] + t * x;
-              dacc[1][m] = dacc[1][m] + t * y;
-            }
-          }
-        }
-      }
-    }
-    settle(acc);
+    const InT *so = sIn + vg * IR * CW + vc;       // own plane
+    const InT *sp = sIn + (1 - vg) * IR * CW + vc; // the other plane
+    if (vg == 0)
+      vpass<R, RD, InT, 0>(so, sp, in_scale, taps, dtaps, vm, vs, vx, vd);
+    else
+      vpass<R, RD, InT, 1>(so, sp, in_scale, taps, dtaps, vm, vs, vx, vd);
+    settle1(vm);
+    settle1(vs);
+    settle1(vx);
     if constexpr (RD > 0)
-      settle(dacc);
+      settle1(vd);
   }
   __syncthreads(); // the input tile is dead from here on
 
@@ -432,20 +461,16 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   const int seg = (tid & 7) + 8 * (tid >> 7);
   const int ty = ((tid >> 3) & 7) + 8 * ((tid >> 6) & 1);
 
-  // 3. round A: vertical results of x, y and the next scale's vertical
-  //    low-pass to LDS
+  // 3. round A: vertical results of x (group 0) and y (group 1), and each
+  //    plane's vertical low-pass, to LDS
   if (vact) {
 #pragma unroll
-    for (int q = 0; q < kQA; ++q)
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-        sV[(q * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
+    for (int i = 0; i < VR; ++i)
+      sV[(vg * kTileH + i) * CWP + vc] = vm[i];
     if constexpr (RD > 0) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int m = 0; m < VB / 2; ++m)
-          sVd[p * kDecPlane + dec_row(vb * (VB / 2) + m) + vc] = dacc[p][m];
+      for (int m = 0; m < VC; ++m)
+        sVd[vg * kDecPlane + dec_row(m) + vc] = vd[m];
     }
   }
   __syncthreads();
@@ -493,13 +518,15 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   }
   __syncthreads(); // round A's region is free
 
-  // 5. round B: vertical results of x*x, y*y, x*y to LDS
+  // 5. round B: vertical results of x*x (group 0), y*y (group 1) and x*y
+  //    (rows 8g .. 8g + 7) to LDS
   if (vact) {
 #pragma unroll
-    for (int q = kQA; q < 5; ++q)
+    for (int i = 0; i < VR; ++i)
+      sV[(vg * kTileH + i) * CWP + vc] = vs[i];
 #pragma unroll
-      for (int i = 0; i < VB; ++i)
-        sV[((q - kQA) * kTileH + vb * VB + i) * CWP + vc] = acc[q][i];
+    for (int i = 0; i < VC; ++i)
+      sV[(2 * kTileH + vg * VC + i) * CWP + vc] = vx[i];
   }
   __syncthreads();
 
