@@ -179,7 +179,6 @@ vpass(const InT *so, const InT *sp, float sc, const TapArgs &taps,
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
