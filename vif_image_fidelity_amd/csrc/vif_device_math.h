@@ -107,21 +107,30 @@ __device__ __forceinline__ float num_ratio(float a, float sv, double nsq) {
   return static_cast<float>(1.0 + q);
 }
 
-// fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.  For a
-// power-of-two nsq in [2^-20, 2^20] (kPow2, sa.inv_nsq = 1 / nsq, not 0) the
-// quotient is the exact product with 1 / nsq.  kPow2 is a compile-time
-// choice: the kernels come in both forms and the host launches the one that
-// matches nsq, so neither carries the other's arithmetic (a run-time branch
-// on it was turned into both computations and a select).
+// fl32(1 + sigma1_sq / nsq), fp64 quotient and sum, one conversion.  kPow2
+// is a compile-time choice: the kernels come in both forms and the host
+// launches the one that matches nsq, so neither carries the other's
+// arithmetic (a run-time branch on it was turned into both computations and
+// a select).
+//
+// For a power-of-two nsq in [2^-20, 2^20] (kPow2: sa.inv_nsq = 1 / nsq, not
+// 0) the same value comes from two fp32 operations, 1.0f + s1 * (1 / nsq).
+// Let q = s1 * 2^k exactly; fp64 holds it exactly.  When |q| >= 2^-28, 1 + q
+// is exact in fp64 too (q's 24 significant bits and the leading 1 span at
+// most 53 bits; beyond 2^53 the fp64 sum is q rounded, as fp32 rounds it),
+// so the conversion is the one rounding of 1 + q to fp32, which is what
+// 1.0f + q gives: the fp32 product is q itself unless it overflows, and
+// then both paths give an infinity.  When |q| < 2^-28 both give 1.0f: fp32
+// rounds 1 + q to 1 (whether or not a tiny product underflows), and fp64
+// rounds it to within 2^-28 of 1, which converts to 1.  NaN stays NaN.
 template <bool kPow2>
 __device__ __forceinline__ float den_ratio(float s1, const StatArgs &sa) {
-  const double s = static_cast<double>(s1);
-  double q;
-  if constexpr (kPow2)
-    q = s * sa.inv_nsq;
-  else
-    q = s / sa.nsq;
-  return static_cast<float>(1.0 + q);
+  if constexpr (kPow2) {
+    return 1.0f + s1 * sa.inv_nsq_f;
+  } else {
+    const double q = static_cast<double>(s1) / sa.nsq;
+    return static_cast<float>(1.0 + q);
+  }
 }
 
 // Per-pixel statistic from the five filtered values.
@@ -162,7 +171,9 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
   const float s12 = xy - m12;
   s1 = __builtin_fmaxf(s1, 0.0f);
   s2 = __builtin_fmaxf(s2, 0.0f);
-  if (static_cast<double>(s1) < sa.nsq) {
+  // the comparison in fp64; for a power-of-two nsq (kPow2) its fp32 value
+  // is exact, and comparing s1 with it is the same test
+  if (kPow2 ? s1 < sa.nsq_f : static_cast<double>(s1) < sa.nsq) {
     num = 1.0f;
     den = 1.0f;
     return;

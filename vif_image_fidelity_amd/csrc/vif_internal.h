@@ -30,6 +30,9 @@ struct TapArgs {
 //   inv_nsq  1 / nsq when that is a power of two in [2^-20, 2^20], so that
 //            s * inv_nsq is the quotient s / nsq exactly; 0 otherwise
 //            (divide).  Non-zero selects the kernels' kPow2 form.
+//   nsq_f, inv_nsq_f  nsq and inv_nsq as fp32 values when inv_nsq is not
+//            0 (both are then powers of two in [2^-20, 2^20], exact in
+//            fp32); 0 otherwise
 //   gain     the enhancement gain limit rounded to fp32.  C's MIN(g, limit)
 //            with a double limit selects the same value as the fp32
 //            comparison g < gain: no fp32 value lies strictly between a
@@ -39,6 +42,8 @@ struct StatArgs {
   double nsq;
   double inv_nsq;
   float gain;
+  float nsq_f;
+  float inv_nsq_f;
 };
 
 // Option checks and the statistic constants (vif_options.cpp).  Returns

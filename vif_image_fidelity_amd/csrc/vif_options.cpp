@@ -47,8 +47,11 @@ StatArgs make_stat_args(double nsq, double gain_limit) {
   // underflow in fp64).  The range 2^-20 .. 2^20 also keeps the numerator
   // ratio's quotient inside the domain of its shorter division (the kernels
   // for a power-of-two nsq use it; other values take the general kernels).
-  if (nsq > 0.0 && std::frexp(nsq, &e) == 0.5 && e >= -19 && e <= 21)
+  if (nsq > 0.0 && std::frexp(nsq, &e) == 0.5 && e >= -19 && e <= 21) {
     a.inv_nsq = std::ldexp(1.0, 1 - e);
+    a.nsq_f = static_cast<float>(nsq);
+    a.inv_nsq_f = static_cast<float>(a.inv_nsq);
+  }
   a.gain = static_cast<float>(gain_limit);
   return a;
 }
