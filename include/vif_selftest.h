@@ -40,6 +40,14 @@ int vif_selftest_fp64(const float *a, const float *b, double nsq, long n,
 int vif_selftest_div32(const float *a, const float *b, long n, float *q,
                        void *stream);
 
+/* q[i] = a[i] / b[i] in fp32 with the statistic's written-out division for
+ * a power-of-two noise variance, which equals the correctly rounded
+ * division for a[i] == +0 or 2^-100 <= |a[i]| <= 2^17 and
+ * 2^-20 <= b[i] <= 2^17 (its domain; elsewhere the result is unspecified).
+ * Device arrays of n floats; VIF_EINVAL for n < 0 or a NULL array. */
+int vif_selftest_div32_in_range(const float *a, const float *b, long n,
+                                float *q, void *stream);
+
 /* y[i] = the kernels' log2 polynomial of x[i] (x[i] finite, >= 1). */
 int vif_selftest_log2(const float *x, long n, float *y, void *stream);
 

@@ -10,15 +10,18 @@ Context and Consequences).  This module checks three layers:
 
   flags    the library's compiler flags fix contraction off, IEEE division,
            denormals and no fast-math, with packed fp32 disabled;
-  sources  the kernel sources call no fused multiply-add (except the five
-           of the fp64 division written out in div_in_range, checked to be
-           exactly that sequence), no library or hardware log/exp, no atomic
+  sources  the kernel sources call no fused multiply-add (except those of
+           the fp64 and fp32 divisions written out in div_in_range and
+           div_in_range_f32, each checked to be exactly the division's
+           sequence), no library or hardware log/exp, no atomic
            read-modify-write (an atomic add would merge sums in arrival
            order; atomic loads and stores that only hand a value from one
            block to the next are allowed), and include no CUDA or Triton;
   ISA      the compiled gfx950 code of every kernel: each fp32 fused
-           multiply-add belongs to a correctly rounded division expansion
-           (five per v_div_fixup_f32), each fp64 one to an fp64 division
+           multiply-add belongs to a correctly rounded division (one
+           v_rcp_f32 each: five in the compiler's expansion, which ends in
+           v_div_fixup_f32, six in the written-out one), each fp64 one to an
+           fp64 division
            (one v_rcp_f64 each: five fused multiply-adds and a v_div_fmas in
            the compiler's expansion, which ends in v_div_fixup_f64, six in
            the written-out one), and there are no packed-fp32, float mad,
@@ -84,34 +87,53 @@ def _strip_comments(text):
     return re.sub(r"//[^\n]*", "", text)
 
 
-# The one place the sources may fuse: the fp64 division written out step by
-# step (a reciprocal, two Newton-Raphson refinements of two fused
-# multiply-adds each, the product, the remainder and the corrected quotient),
-# the same steps as the compiler's expansion.
-_DIV_HELPER = re.compile(
-    r"double div_in_range\(double a, double d\) \{(?P<body>.*?)\n\}", re.S)
-_DIV_BODY = [
-    "double r = __builtin_amdgcn_rcp(d);",
-    "double e = __builtin_fma(-d, r, 1.0);",
-    "r = __builtin_fma(r, e, r);",
-    "e = __builtin_fma(-d, r, 1.0);",
-    "r = __builtin_fma(r, e, r);",
-    "const double q = a * r;",
-    "const double rem = __builtin_fma(-d, q, a);",
-    "return __builtin_fma(rem, r, q);",
-]
+# The places the sources may fuse: the fp64 and fp32 divisions written out
+# step by step, the same steps as the compiler's expansions.  fp64: a
+# reciprocal, two Newton-Raphson refinements of two fused multiply-adds
+# each, the product, the remainder and the corrected quotient.  fp32: a
+# reciprocal, one refinement, the product, and two rounds of remainder and
+# correction.
+_DIV_HELPERS = (
+    ("div_in_range", re.compile(
+        r"double div_in_range\(double a, double d\) \{(?P<body>.*?)\n\}",
+        re.S), [
+        "double r = __builtin_amdgcn_rcp(d);",
+        "double e = __builtin_fma(-d, r, 1.0);",
+        "r = __builtin_fma(r, e, r);",
+        "e = __builtin_fma(-d, r, 1.0);",
+        "r = __builtin_fma(r, e, r);",
+        "const double q = a * r;",
+        "const double rem = __builtin_fma(-d, q, a);",
+        "return __builtin_fma(rem, r, q);",
+    ]),
+    ("div_in_range_f32", re.compile(
+        r"float div_in_range_f32\(float a, float d\) \{(?P<body>.*?)\n\}",
+        re.S), [
+        "float r = __builtin_amdgcn_rcpf(d);",
+        "const float e = __builtin_fmaf(-d, r, 1.0f);",
+        "r = __builtin_fmaf(e, r, r);",
+        "float q = a * r;",
+        "float rem = __builtin_fmaf(-d, q, a);",
+        "q = __builtin_fmaf(rem, r, q);",
+        "rem = __builtin_fmaf(-d, q, a);",
+        "return __builtin_fmaf(rem, r, q);",
+    ]),
+)
 
 
 def _take_div_helper(name, code, v):
-    """Checks the written-out division, then removes its body from the
-    code the other rules scan."""
-    m = _DIV_HELPER.search(code)
-    if m is None:
-        return code
-    body = [ln.strip() for ln in m.group("body").splitlines() if ln.strip()]
-    if body != _DIV_BODY:
-        v.append("%s: div_in_range is not the fp64 division's steps" % name)
-    return code[:m.start("body")] + code[m.end("body"):]
+    """Checks the written-out divisions, then removes their bodies from
+    the code the other rules scan."""
+    for helper, pattern, steps in _DIV_HELPERS:
+        m = pattern.search(code)
+        if m is None:
+            continue
+        body = [ln.strip() for ln in m.group("body").splitlines()
+                if ln.strip()]
+        if body != steps:
+            v.append("%s: %s is not the division's steps" % (name, helper))
+        code = code[:m.start("body")] + code[m.end("body"):]
+    return code
 
 
 def source_violations(sources):
@@ -194,12 +216,13 @@ def isa_violations(asm):
             return sum(1 for o in ops if re.fullmatch(pat, o))
         fma32 = count(r"v_fmac?_f32(?:_e32|_e64)?")
         fix32 = count(r"v_div_fixup_f32(?:_e64)?")
+        rcp32 = count(r"v_rcp_f32(?:_e32|_e64)?")
         fma64 = count(r"v_fmac?_f64(?:_e32|_e64)?")
         fix64 = count(r"v_div_fixup_f64(?:_e64)?")
         rcp64 = count(r"v_rcp_f64(?:_e32|_e64)?")
-        if fma32 != 5 * fix32:
+        if fix32 > rcp32 or fma32 != 5 * fix32 + 6 * (rcp32 - fix32):
             v.append("%s: %d fp32 fused multiply-adds for %d divisions"
-                     % (name, fma32, fix32))
+                     % (name, fma32, rcp32))
         if fix64 > rcp64 or fma64 != 5 * fix64 + 6 * (rcp64 - fix64):
             v.append("%s: %d fp64 fused multiply-adds for %d divisions"
                      % (name, fma64, rcp64))

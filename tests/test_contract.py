@@ -94,6 +94,13 @@ SOURCE_MUTANTS = [
      "  const double q = __builtin_fma(a, r, 0.0);"),
     ("vif_device_math.h", "  const float q = p * t;",
      "  const float q = __builtin_fmaf(p, t, 0.0f);"),
+    # the same for the written-out fp32 division
+    ("vif_device_math.h", "  return __builtin_fmaf(rem, r, q);",
+     "  return q;"),
+    ("vif_device_math.h", "  float q = a * r;",
+     "  float q = __builtin_fmaf(a, r, 0.0f);"),
+    ("vif_device_math.h", "  const float gs = g * s12;",
+     "  const float gs = __builtin_fmaf(g, s12, 0.0f);"),
 ]
 
 
@@ -131,6 +138,7 @@ def test_isa_catches_planted_instructions():
                  "\tglobal_atomic_add_f32 v1, v2, s[0:1]\n",
                  "\tscratch_store_dword off, v1, off\n",
                  "\tv_fma_f32 v1, v2, v3, v4\n",
+                 "\tv_rcp_f32_e32 v1, v2\n",
                  "\tv_log_f32_e32 v1, v2\n"):
         bad = clean.replace("\ts_endpgm", line + "\ts_endpgm")
         assert contract.isa_violations(bad), line

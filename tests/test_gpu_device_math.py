@@ -6,7 +6,8 @@ Decision, reports a host comparison of the device's fp64 add and divide
 over tens of millions of operand pairs and several noise variances.  Here:
 2^25 pairs with magnitudes from 2^-40 to 2^40, six variances, targeted
 near-ties, each checked on the sum, the quotient and both fp32 roundings of
-one plus the quotient; the fp32 division; the log2 polynomial exhaustively
+one plus the quotient; the fp32 division, and the statistic's written-out
+fp32 division over its domain; the log2 polynomial exhaustively
 (every mantissa of exponents 0..31); the ratios and the whole statistic
 against the oracle.
 """
@@ -106,6 +107,46 @@ def test_fp32_division_bitwise(dev):
     da, db = _d(a), _d(b)  # keep the device copies alive across the call
     _check(_lib.load().vif_selftest_div32(da.data_ptr(), db.data_ptr(),
                                           n, q.data_ptr(), None))
+    assert np.array_equal(_h(q).view(np.uint32), (a / b).view(np.uint32))
+
+
+def test_fp32_division_in_range_bitwise(dev):
+    """The statistic's written-out fp32 division for a power-of-two noise
+    variance (div_in_range_f32) against the host's IEEE division over its
+    whole domain: 2^25 pairs with |a| from 2^-100 to 2^17 (and zeros) and b
+    from 2^-20 to 2^17, 2^20 quotients within an ulp of a midpoint between
+    two fp32 values, and the domain's corners."""
+    import torch
+    from vif_image_fidelity_amd import _lib
+    g = np.random.Generator(np.random.PCG64(37))
+    n = 1 << 25
+    a = (_span_operands(g, n, -100, 17) *
+         np.where(g.random(n) < 0.5, -1, 1)).astype(np.float32)
+    b = _span_operands(g, n, -20, 17)
+    a[:4096] = 0.0
+    # near-ties: a = fl32(b * m) with m the midpoint of two fp32 quotients
+    m = 1 << 20
+    bt = _span_operands(g, m, -20, 17)
+    la = g.uniform(-99, 16, size=m)
+    q0 = np.exp2(la - np.log2(bt.astype(np.float64))).astype(np.float32)
+    mid = (q0.astype(np.float64) +
+           np.nextafter(q0, np.float32(np.inf)).astype(np.float64)) / 2
+    at = (mid * bt.astype(np.float64)).astype(np.float32)
+    a[4096:4096 + m], b[4096:4096 + m] = at, bt
+    corners_a = np.array([2.0 ** -100, -2.0 ** -100, 2.0 ** 17, -2.0 ** 17,
+                          1.0, 3.0, -7.0, 2.0 ** -99 * 3], dtype=np.float32)
+    corners_b = np.array([2.0 ** -20, 2.0 ** 17, 1.0, 3.0, 2.0 ** -20 * 3,
+                          2.0 ** 17 * 0.75], dtype=np.float32)
+    ca, cb = np.meshgrid(corners_a, corners_b)
+    k = ca.size
+    a[-k:], b[-k:] = ca.ravel(), cb.ravel()
+    aa = np.abs(a.astype(np.float64))
+    assert np.all((a == 0) | ((aa >= 2.0 ** -100) & (aa <= 2.0 ** 17)))
+    assert np.all((b >= 2.0 ** -20) & (b <= 2.0 ** 17))
+    q = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    da, db = _d(a), _d(b)
+    _check(_lib.load().vif_selftest_div32_in_range(
+        da.data_ptr(), db.data_ptr(), n, q.data_ptr(), None))
     assert np.array_equal(_h(q).view(np.uint32), (a / b).view(np.uint32))
 
 

@@ -111,6 +111,7 @@ def load():
         "vif_selftest_fp64": ([vp, vp, ctypes.c_double, ctypes.c_long, vp, vp,
                                vp, vp, vp], ip),
         "vif_selftest_div32": ([vp, vp, ctypes.c_long, vp, vp], ip),
+        "vif_selftest_div32_in_range": ([vp, vp, ctypes.c_long, vp, vp], ip),
         "vif_selftest_log2": ([vp, ctypes.c_long, vp, vp], ip),
         "vif_selftest_ratios": ([vp, vp, ctypes.c_double, ctypes.c_long, vp,
                                  vp, vp], ip),
@@ -160,6 +161,7 @@ def exported_symbols():
             "vif_get_sums", "vif_get_row_sums", "vif_taps",
             "vif_set_profiling", "vif_get_kernel_times", "vif_errno",
             "vif_strerror", "vif_selftest_fp64", "vif_selftest_div32",
+            "vif_selftest_div32_in_range",
             "vif_selftest_log2", "vif_selftest_ratios",
             "vif_selftest_statistic", "vif_selftest_carry_wait",
             "vif_selftest_valu_rate", "vif_selftest_stage_loads",

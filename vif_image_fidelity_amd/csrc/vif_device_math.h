@@ -88,6 +88,35 @@ __device__ __forceinline__ double div_in_range(double a, double d) {
   return __builtin_fma(rem, r, q);
 }
 
+// The correctly rounded fp32 quotient a / d for operands that need no
+// scaling: a == +0 or 2^-100 <= |a| <= 2^17, and 2^-20 <= d <= 2^17.  These
+// are the compiler's IEEE fp32 division steps on gfx950 (a hardware
+// reciprocal, one Newton-Raphson refinement, the product with a, and two
+// rounds of remainder and correction, the last of which the expansion issues
+// as v_div_fmas with its scale flag clear) without the two v_div_scale steps
+// and the closing v_div_fixup.  In this domain those are identities:
+// v_div_scale changes an operand only for a zero, denormal or near-overflow
+// one, an exponent gap of 96 or more, a denormal reciprocal or quotient, or
+// a numerator below 2^-103, none of which occurs (|a / d| lies in
+// [2^-117, 2^37]); v_div_fixup changes the result only for zero, infinite or
+// NaN operands and quotients that overflow or underflow, and for a == +0
+// every step gives +0, as the fix-up does.  So the bits are the division's.
+// The statistic's sigma12 / sigma1_sq stays in this domain in the kPow2
+// branch: sigma1_sq >= nsq >= 2^-20 there, every filtered value is below
+// 2^16, and a non-zero sigma12 is at least 2^-100 (a non-zero filtered value
+// of a plane whose samples are multiples of 2^-8 is at least 2^-77 at every
+// scale, and sigma12 is a difference of two such values or zero).
+__device__ __forceinline__ float div_in_range_f32(float a, float d) {
+  float r = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, r, 1.0f);
+  r = __builtin_fmaf(e, r, r);
+  float q = a * r;
+  float rem = __builtin_fmaf(-d, q, a);
+  q = __builtin_fmaf(rem, r, q);
+  rem = __builtin_fmaf(-d, q, a);
+  return __builtin_fmaf(rem, r, q);
+}
+
 // fl32(1 + a / (sv + nsq)) with the sum, quotient and sum with one in fp64
 // and a single conversion to fp32 at the end; nsq is the noise variance,
 // kept in binary64 (ADR-1422 "float_vif_sycl computes the CPU's arithmetic
@@ -178,7 +207,8 @@ __device__ __forceinline__ void pixel_terms(float mu1, float mu2, float xx,
     den = 1.0f;
     return;
   }
-  float g = s12 / s1;
+  // kPow2: s1 >= nsq >= 2^-20 here, inside div_in_range_f32's domain
+  float g = kPow2 ? div_in_range_f32(s12, s1) : s12 / s1;
   const float gs = g * s12;
   float sv = s2 - gs;
   if (s2 < kEps) {

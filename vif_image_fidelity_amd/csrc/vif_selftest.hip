@@ -30,6 +30,14 @@ __global__ void fp64_gate_kernel(const float *__restrict__ a,
   rden[i] = static_cast<float>(1.0 + static_cast<double>(a[i]) / nsq);
 }
 
+__global__ void div32_in_range_kernel(const float *__restrict__ a,
+                                      const float *__restrict__ b, long n,
+                                      float *__restrict__ q) {
+  const long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n)
+    q[i] = vifk::div_in_range_f32(a[i], b[i]);
+}
+
 __global__ void div32_kernel(const float *__restrict__ a,
                              const float *__restrict__ b, long n,
                              float *__restrict__ q) {
@@ -152,6 +160,18 @@ vif_selftest_div32(const float *a, const float *b, long n, float *q,
     return vifk::set_status(VIF_OK);
   hipStream_t s = static_cast<hipStream_t>(stream);
   div32_kernel<<<grid_for(n), kBlock, 0, s>>>(a, b, n, q);
+  return finish(s);
+}
+
+__attribute__((visibility("default"))) int
+vif_selftest_div32_in_range(const float *a, const float *b, long n, float *q,
+                            void *stream) {
+  if (bad_n(n) || (n > 0 && (!a || !b || !q)))
+    return vifk::set_status(VIF_EINVAL);
+  if (n == 0)
+    return vifk::set_status(VIF_OK);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  div32_in_range_kernel<<<grid_for(n), kBlock, 0, s>>>(a, b, n, q);
   return finish(s);
 }
 
