@@ -4,9 +4,10 @@
 //   1. stage the tile's input (+ halo of the filter radius) into LDS in the
 //      plane's sample type, mirroring out-of-plane indices by one
 //      reflection and a clamp (ADR-1444 "float_vif_hip runs the arithmetic
-//      of the CUDA twin ...", Decision); samples are normalised to fp32 where
-//      they are read (Research-2130 "float_ssim decimation on the SYCL
-//      device", Sources: 8-bit as is, 10/12/16-bit divided by 4/16/256);
+//      of the CUDA twin ...", Decision); samples are converted to fp32 where
+//      they are read, and their normalisation (Research-2130 "float_ssim
+//      decimation on the SYCL device", Sources: 8-bit as is, 10/12/16-bit
+//      divided by 4/16/256) rides on the vertical pass's taps (VTaps);
 //   2. the vertical pass of the separable Gaussian for the five quantities
 //      x, y, x*x, y*y, x*y, one thread per column and 8 rows in registers,
 //      and the vertical pass of the next scale's low-pass at even rows;
@@ -40,25 +41,23 @@ constexpr int kThreads = 256;
 
 // Planes hold at most 2^27 samples, so a 32-bit offset addresses them.
 // The input tile stays in LDS in the plane's own sample type (one byte per
-// 8-bit sample); to_float normalises a sample where the vertical pass reads
-// it (Research-2130 "float_ssim decimation on the SYCL device", Sources:
-// 8-bit samples as they are, wider ones divided by 4, 16 or 256).
-template <typename InT>
-__device__ __forceinline__ float to_float(InT v, float scale);
+// 8-bit sample); to_float converts a sample where the vertical pass reads
+// it.  The pages normalise samples to fp32 (Research-2130 "float_ssim
+// decimation on the SYCL device", Sources: 8-bit samples as they are, wider
+// ones divided by 4, 16 or 256).  For 10- to 16-bit samples that division,
+// by a power of two s, is carried by the vertical pass's taps instead (see
+// VTaps): the pass then reads the samples as they are.
+template <typename InT> __device__ __forceinline__ float to_float(InT v);
 
-template <>
-__device__ __forceinline__ float to_float<uint8_t>(uint8_t v, float) {
+template <> __device__ __forceinline__ float to_float<uint8_t>(uint8_t v) {
   return static_cast<float>(v);
 }
 
-template <>
-__device__ __forceinline__ float to_float<uint16_t>(uint16_t v, float scale) {
-  // scale is an exact power of two (1/4, 1/16, 1/256): the product is exact
-  return static_cast<float>(v) * scale;
+template <> __device__ __forceinline__ float to_float<uint16_t>(uint16_t v) {
+  return static_cast<float>(v);
 }
 
-template <>
-__device__ __forceinline__ float to_float<float>(float v, float) {
+template <> __device__ __forceinline__ float to_float<float>(float v) {
   return v;
 }
 
@@ -143,6 +142,22 @@ __device__ __forceinline__ void settle1(float (&v)[A]) {
     asm volatile("" : "+v"(v[a]));
 }
 
+// The vertical pass's taps: m for the planes' means, q for their squares
+// and the cross product, d for the next scale's low-pass.  Normally m and q
+// are the scale's taps t and d the next scale's, dt.  For 10- to 16-bit
+// samples v, normalised as v * s with s = 2^-2, 2^-4 or 2^-8, they are t *
+// s, t * s^2 and dt * s (exact: powers of two times normal fp32 values) and
+// the pass reads v itself, with the same fp32 results: t * (v * s) and
+// (t * s) * v are one real number rounded once; (v * s)^2 rounds to fl(v^2)
+// * s^2, a power-of-two scaling commuting with rounding (the values stay
+// far from underflow and overflow), so t * fl((v * s)^2) and (t * s^2) *
+// fl(v^2) are again one real number, and likewise for x * y and the
+// low-pass; every sum then adds the same values.  That saves the multiply
+// by s for each of the 56 samples a thread reads per tile.
+struct VTaps {
+  TapArgs m, q, d;
+};
+
 // The vertical pass of group G over a column of the input tile: so is the
 // group's own plane, sp the other.  Own plane: mean vm and square vs at all
 // kTileH rows, the next scale's low-pass vd at the even rows; cross product
@@ -150,7 +165,7 @@ __device__ __forceinline__ void settle1(float (&v)[A]) {
 // G*kTileH/2 on.  G is a template argument, so every tap index is a constant.
 template <int R, int RD, typename InT, int G>
 __device__ __forceinline__ void
-vpass(const InT *so, const InT *sp, float sc, const TapArgs &taps,
+vpass(const InT *so, const InT *sp, const TapArgs &tm, const TapArgs &tq,
       const TapArgs &dtaps, float (&vm)[kTileH], float (&vs)[kTileH],
       float (&vx)[kTileH / 2], float (&vd)[kTileH / 2]) {
   constexpr int N = 2 * R + 1;
@@ -160,14 +175,14 @@ vpass(const InT *so, const InT *sp, float sc, const TapArgs &taps,
   constexpr int VC = kTileH / 2;
 #pragma unroll
   for (int j = 0; j < VR + 2 * R; ++j) {
-    const float p = to_float<InT>(so[j * CW], sc);
-    vacc<N, VR>(vm, p, j, 0, taps);
-    vacc<N, VR>(vs, p * p, j, 0, taps);
+    const float p = to_float<InT>(so[j * CW]);
+    vacc<N, VR>(vm, p, j, 0, tm);
+    vacc<N, VR>(vs, p * p, j, 0, tq);
     constexpr int J0 = G * VC;
     if (j >= J0 && j < J0 + VC + 2 * R) {
-      const float o = to_float<InT>(sp[j * CW], sc);
+      const float o = to_float<InT>(sp[j * CW]);
       // x * y in that operand order whichever plane is the thread's own
-      vacc<N, VC>(vx, G == 0 ? p * o : o * p, j - J0, 0, taps);
+      vacc<N, VC>(vx, G == 0 ? p * o : o * p, j - J0, 0, tq);
     }
     if constexpr (RD > 0) {
 #pragma unroll
@@ -383,7 +398,7 @@ __device__ __forceinline__ void stage_tile(InT *sIn,
 // at its own offsets of the next scale's planes and the row sums.
 template <int R, int RD, typename InT, bool kPow2>
 __global__ __launch_bounds__(kThreads) void scale_kernel(
-    ScaleIO io, int w, int h, float in_scale, TapArgs taps, TapArgs dtaps,
+    ScaleIO io, int w, int h, VTaps vt, TapArgs taps, TapArgs dtaps,
     StatArgs stat, int first) {
   const int sp = block_slot();
   if (sp >= io.slots)
@@ -441,10 +456,15 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(
   if (vact) {
     const InT *so = sIn + vg * IR * CW + vc;       // own plane
     const InT *sp = sIn + (1 - vg) * IR * CW + vc; // the other plane
+    // the taps with the samples' normalisation for 10- to 16-bit planes
+    constexpr bool kScaled = std::is_same<InT, uint16_t>::value;
+    const TapArgs &tm = kScaled ? vt.m : taps;
+    const TapArgs &tq = kScaled ? vt.q : taps;
+    const TapArgs &td = kScaled ? vt.d : dtaps;
     if (vg == 0)
-      vpass<R, RD, InT, 0>(so, sp, in_scale, taps, dtaps, vm, vs, vx, vd);
+      vpass<R, RD, InT, 0>(so, sp, tm, tq, td, vm, vs, vx, vd);
     else
-      vpass<R, RD, InT, 1>(so, sp, in_scale, taps, dtaps, vm, vs, vx, vd);
+      vpass<R, RD, InT, 1>(so, sp, tm, tq, td, vm, vs, vx, vd);
     settle1(vm);
     settle1(vs);
     settle1(vx);
@@ -613,26 +633,34 @@ void launch_one(int scale, int bpc, dim3 grid, dim3 block, hipStream_t stream,
                 const ScaleIO &io, const ScaleGeom &g, float sc,
                 const TapArgs &taps, const TapArgs &next_taps,
                 const StatArgs &stat, int first) {
+  VTaps vt{}; // read by the 10- to 16-bit scale-0 kernels only
   switch (scale) {
   case 0:
-    if (bpc == 8)
+    if (bpc == 8) {
       scale_kernel<8, 4, uint8_t, kPow2><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, sc, taps, next_taps, stat, first);
-    else
+          io, g.w, g.h, vt, taps, next_taps, stat, first);
+    } else {
+      // sc is 2^-2, 2^-4 or 2^-8: every product below is exact
+      for (int k = 0; k < kMaxTaps; ++k) {
+        vt.m.t[k] = taps.t[k] * sc;
+        vt.q.t[k] = taps.t[k] * sc * sc;
+        vt.d.t[k] = next_taps.t[k] * sc;
+      }
       scale_kernel<8, 4, uint16_t, kPow2><<<grid, block, 0, stream>>>(
-          io, g.w, g.h, sc, taps, next_taps, stat, first);
+          io, g.w, g.h, vt, taps, next_taps, stat, first);
+    }
     break;
   case 1:
     scale_kernel<4, 2, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
+        io, g.w, g.h, vt, taps, next_taps, stat, first);
     break;
   case 2:
     scale_kernel<2, 1, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
+        io, g.w, g.h, vt, taps, next_taps, stat, first);
     break;
   default:
     scale_kernel<1, 0, float, kPow2><<<grid, block, 0, stream>>>(
-        io, g.w, g.h, 1.0f, taps, next_taps, stat, first);
+        io, g.w, g.h, vt, taps, next_taps, stat, first);
     break;
   }
 }
@@ -687,10 +715,10 @@ hipError_t launch_scale0_column(const ScaleIO &io, const ScaleGeom &g,
   const dim3 grid(static_cast<unsigned>((g.strips + 7) & ~7), 1, 1);
   if (stat.inv_nsq != 0.0)
     scale_kernel<8, 4, uint8_t, true><<<grid, dim3(kThreads), 0, stream>>>(
-        iox, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+        iox, g.w, g.h, VTaps{}, taps, next_taps, stat, col);
   else
     scale_kernel<8, 4, uint8_t, false><<<grid, dim3(kThreads), 0, stream>>>(
-        iox, g.w, g.h, 1.0f, taps, next_taps, stat, col);
+        iox, g.w, g.h, VTaps{}, taps, next_taps, stat, col);
   return hipGetLastError();
 }
 
