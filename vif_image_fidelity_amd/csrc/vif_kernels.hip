@@ -9,8 +9,10 @@
 //      decimation on the SYCL device", Sources: 8-bit as is, 10/12/16-bit
 //      divided by 4/16/256) rides on the vertical pass's taps (VTaps);
 //   2. the vertical pass of the separable Gaussian for the five quantities
-//      x, y, x*x, y*y, x*y, one thread per column and 8 rows in registers,
-//      and the vertical pass of the next scale's low-pass at even rows;
+//      x, y, x*x, y*y, x*y, one thread per column and plane with all 16 of
+//      the tile's rows in registers (its plane's mean and square, half the
+//      rows of the cross product), and the vertical pass of the next
+//      scale's low-pass at even rows;
 //   3. the horizontal pass (7 outputs per thread, in two rounds of
 //      quantities so the block's LDS stays small), the per-pixel statistic
 //      and the two terms, staged in LDS;
